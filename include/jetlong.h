@@ -1,0 +1,128 @@
+/*
+ * jetlong.h - C ABI of the MI355X (gfx950) bifocal RoPE attention library.
+ *
+ * Jet-Long ("Jet-Long: Efficient Long-Context Extension with Dynamic Bifocal
+ * RoPE") extends a RoPE model past its pretraining window without training.
+ * Every (query i, key j) score of causal attention is routed by distance:
+ *   - pairs with i - j < w0 use ordinary RoPE at the absolute positions i, j;
+ *   - farther pairs use RoPE at the aliased positions f(i), f(j),
+ *     f(x) = floor(x / G), G = max(1, ceil(L / w_pretrained)).
+ * (technical summary on gist.science, Methodology item 1, "Dynamic Bifocal
+ * RoPE": local window, remote window, group-size equation and remote map).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE memory owned by the caller.  The library
+ *     never allocates or frees device memory and keeps no pointer after a
+ *     call returns.  Scratch space is the caller's `workspace` (two-call
+ *     protocol: pass workspace == NULL to get the size in *workspace_bytes;
+ *     nothing is launched then).
+ *   - Host pointers (q_to_kv, cu_seqlens) are read during the call only.
+ *   - `hip_stream` is a hipStream_t passed as void* (NULL = default stream).
+ *     Launches are asynchronous on that stream; the caller synchronises.
+ *   - Every argument is validated before anything is launched: a JL_EINVAL
+ *     or JL_EUNSUPPORTED return has no side effect.  A failed launch returns
+ *     JL_EHIP.  jl_last_error() gives a message for the calling thread.
+ *   - Empty work (zero tokens, L == 0) returns JL_OK and launches nothing.
+ *   - Layouts are row-major and contiguous.  RoPE pairs dimension m with
+ *     m + d/2 and uses theta_m = rope_base^(-2m/d) (the rotary layout of the
+ *     Qwen3 models the pages evaluate).  Angles are formed in fp64.
+ *   - softmax_scale <= 0 selects 1/sqrt(head_dim).  LSE outputs are the
+ *     natural log of sum_j exp(softmax_scale * q.k) per (head, row), fp32.
+ *   - q_to_kv: host int32[num_q_heads] giving the kv head of each q head, or
+ *     NULL for h / (num_q_heads / num_kv_heads).
+ */
+#ifndef JETLONG_H
+#define JETLONG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  JL_OK = 0,
+  JL_EINVAL = -1,        /* an argument is out of its documented range */
+  JL_EUNSUPPORTED = -2,  /* valid, but not built (dtype, head_dim, sizes) */
+  JL_ENOSPC = -3,        /* *workspace_bytes is smaller than required */
+  JL_EHIP = -4           /* a HIP launch or runtime call failed */
+} jl_status;
+
+typedef enum { JL_BF16 = 0, JL_FP32 = 1 } jl_dtype;
+
+/* Largest number of packed sequences one jl_bifocal_prefill call accepts. */
+#define JL_MAX_SEQS 64
+
+/*
+ * Group size G = max(1, ceil(L / w_pretrained)) (technical summary,
+ * Methodology item 1, group-size equation).  Host integer function, exact
+ * for all int64 inputs.  Returns G >= 1, or JL_EINVAL (< 0) if L < 0 or
+ * w_pretrained < 1.
+ */
+int64_t jl_group_size(int64_t L, int64_t w_pretrained);
+
+/*
+ * Bifocal causal prefill over packed independent sequences, computed as the
+ * inclusion-exclusion merge of three flash passes combined through their
+ * LogSumExp statistics (technical summary, Methodology item 2, "Inference
+ * efficiency mechanisms": local window with base q/k, full causal with
+ * remote q/k, local window with remote q/k; no mask matrix):
+ *   out = (z1 o1 + z2 o2 - z3 o3) / (z1 + z2 - z3),  z_k = exp(lse_k - M).
+ *
+ *   q          [total_tokens, num_q_heads, head_dim]  raw (pre-RoPE), dtype
+ *   k, v       [total_tokens, num_kv_heads, head_dim] raw (pre-RoPE), dtype
+ *   o          [total_tokens, num_q_heads, head_dim]  dtype (written)
+ *   lse        [num_q_heads, total_tokens] fp32, or NULL
+ *   cu_seqlens host int64[num_seqs + 1], cu_seqlens[0] = 0, non-decreasing,
+ *              cu_seqlens[num_seqs] = total_tokens; NULL means one sequence
+ *              of total_tokens.  Positions restart at 0 in every sequence and
+ *              each sequence uses its own G from its own length.
+ *   num_seqs   1 .. JL_MAX_SEQS
+ *   head_dim   64 or 128 (JL_BF16 needs 128; JL_FP32 accepts both)
+ *   dtype      JL_BF16: bf16 MFMA passes with fp32 accumulation, bf16 o.
+ *              JL_FP32: fp32 vector-ALU passes (exactness reference path).
+ *   w0         >= 0 local window; w_pretrained >= 1; rope_base > 0.
+ *   Sequences longer than 2^31 - 1 tokens are JL_EUNSUPPORTED.
+ */
+int jl_bifocal_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                       const int64_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                       int32_t num_q_heads, int32_t num_kv_heads, const int32_t* q_to_kv,
+                       int32_t head_dim, jl_dtype dtype, int64_t w0, int64_t w_pretrained,
+                       double rope_base, float softmax_scale, void* workspace,
+                       size_t* workspace_bytes, void* hip_stream);
+
+/*
+ * One single-batch generation step against a KV cache of base-RoPE keys
+ * (technical summary, Methodology item 2: the cache holds uncompressed base
+ * keys at their absolute positions; the correction rotation Delta is applied
+ * to the active query and the cached keys on the fly, and the cache is never
+ * rewritten, also when L crosses a G boundary).
+ *
+ *   q        [num_q_heads, head_dim] bf16, already rotated by base RoPE at
+ *            position L - 1 (the query of the newest token)
+ *   k_cache  [L_cap, num_kv_heads, head_dim] bf16; row j holds the key
+ *            rotated at absolute position j; rows 0 .. L-1 are valid (the
+ *            current token's key included).  Read only.
+ *   v_cache  [L_cap, num_kv_heads, head_dim] bf16.  Read only.
+ *   L        number of valid cache rows, 0 .. 2^31 - 1; G = jl_group_size(L).
+ *            Keys with (L - 1) - j < w0 score with the base vectors; the rest
+ *            score with R(f(L-1) - (L-1)) q and R(f(j) - j) k_j.
+ *   o        [num_q_heads, head_dim] bf16 (written)
+ *   lse      [num_q_heads] fp32, or NULL
+ *   head_dim 128; dtype must be JL_BF16.
+ */
+int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_cache, int64_t L,
+                      void* o, float* lse, int32_t num_q_heads, int32_t num_kv_heads,
+                      const int32_t* q_to_kv, int32_t head_dim, jl_dtype dtype, int64_t w0,
+                      int64_t w_pretrained, double rope_base, float softmax_scale,
+                      void* workspace, size_t* workspace_bytes, void* hip_stream);
+
+/* Message describing the last non-JL_OK return on the calling thread. */
+const char* jl_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JETLONG_H */

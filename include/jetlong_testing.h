@@ -1,0 +1,51 @@
+/*
+ * jetlong_testing.h - test-only entry points of libjetlong.so.
+ *
+ * They expose the DEVICE build of the position mapper so that tests can
+ * check it bit for bit against exact integer arithmetic (technical summary
+ * on gist.science, Methodology item 1: group-size equation
+ * G = max(1, ceil(L / w_pretrained)) and remote map f(x) = floor(x / G)).
+ * They are not part of the attention path.  Pointers are device memory owned
+ * by the caller; launches are asynchronous on `hip_stream`.
+ */
+#ifndef JETLONG_TESTING_H
+#define JETLONG_TESTING_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* G_out[i] = G(L[i], w_pretrained) computed on the device, i < n.
+   JL_EINVAL if n < 0, w_pretrained < 1 or a pointer is NULL with n > 0.
+   Negative L[i] produce G_out[i] = -1. */
+int jl_test_group_size_device(const int64_t* L, int64_t n, int64_t w_pretrained, int64_t* G_out,
+                              void* hip_stream);
+
+/* f_out[i] = f(x0 + i) = floor((x0 + i) / G) computed on the device with the
+   same 32-bit routine the kernels use, i < n.  Requires 0 <= x0,
+   x0 + n <= 2^31 - 1, G >= 1. */
+int jl_test_remote_pos_device(int64_t x0, int64_t n, int64_t G, int32_t* f_out, void* hip_stream);
+
+/* cos_out[i], sin_out[i] = cos / sin of the angle pos[i] * theta_m (theta_m =
+   rope_base^(-2m/head_dim)) as the kernels form it (fixed-point revolutions,
+   then fp32 sin/cos), i < n.  Lets tests bound the angle error at long
+   positions. */
+int jl_test_rope_angles_device(const int32_t* pos, int64_t n, int32_t m, int32_t head_dim,
+                               double rope_base, float* cos_out, float* sin_out, void* hip_stream);
+
+/* Instrumentation for benchmarks: while set, every jl_bifocal_prefill and
+   jl_bifocal_decode call made on the calling thread records the hipEvent_t
+   `before` on its stream immediately before launching its attention
+   kernel(s) and `after` immediately after them (the RoPE pre-pass of prefill
+   stays outside).  Pass NULL, NULL to stop.  The events are the caller's;
+   the library never creates or destroys them.  Returns JL_EINVAL if exactly
+   one of the two is NULL. */
+int jl_set_profile_events(void* before, void* after);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JETLONG_TESTING_H */

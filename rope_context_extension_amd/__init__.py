@@ -1,0 +1,207 @@
+"""Jet-Long dynamic bifocal RoPE attention on MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libjetlong.so`` (include/jetlong.h):
+argument marshalling only.  Every step of the attention path runs in the HIP
+kernels of the library; PyTorch provides device memory and the stream.  There
+is no fallback: if the library is missing or a call fails, an exception is
+raised.
+
+    o, lse = prefill(q, k, v, w0=4096, w_pretrained=32768, rope_base=1e6)
+    o, lse = decode(q, k_cache, v_cache, L, w0=4096, w_pretrained=32768, rope_base=1e6)
+    G = group_size(L, w_pretrained)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+__all__ = ["group_size", "prefill", "prefill_workspace_bytes", "decode", "decode_workspace_bytes",
+           "lib", "JetLongError", "LIB_PATH", "BF16", "FP32"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjetlong.so")
+BF16, FP32 = 0, 1
+_STATUS = {0: "JL_OK", -1: "JL_EINVAL", -2: "JL_EUNSUPPORTED", -3: "JL_ENOSPC", -4: "JL_EHIP"}
+
+_lib = None
+
+
+class JetLongError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (built by rope_context_extension_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run python -m rope_context_extension_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        c = ctypes
+        L.jl_group_size.restype = c.c_int64
+        L.jl_group_size.argtypes = [c.c_int64, c.c_int64]
+        L.jl_last_error.restype = c.c_char_p
+        L.jl_last_error.argtypes = []
+        L.jl_bifocal_prefill.restype = c.c_int
+        L.jl_bifocal_prefill.argtypes = [
+            c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,      # q k v o lse
+            c.POINTER(c.c_int64), c.c_int32, c.c_int64,                       # cu_seqlens nseq T
+            c.c_int32, c.c_int32, c.POINTER(c.c_int32),                       # Hq Hkv q_to_kv
+            c.c_int32, c.c_int, c.c_int64, c.c_int64, c.c_double, c.c_float,  # d dtype w0 wpt base scale
+            c.c_void_p, c.POINTER(c.c_size_t), c.c_void_p]                    # ws ws_bytes stream
+        L.jl_bifocal_decode.restype = c.c_int
+        L.jl_bifocal_decode.argtypes = [
+            c.c_void_p, c.c_void_p, c.c_void_p, c.c_int64, c.c_void_p, c.c_void_p,
+            c.c_int32, c.c_int32, c.POINTER(c.c_int32), c.c_int32, c.c_int, c.c_int64, c.c_int64,
+            c.c_double, c.c_float, c.c_void_p, c.POINTER(c.c_size_t), c.c_void_p]
+        L.jl_test_group_size_device.restype = c.c_int
+        L.jl_test_group_size_device.argtypes = [c.c_void_p, c.c_int64, c.c_int64, c.c_void_p, c.c_void_p]
+        L.jl_test_remote_pos_device.restype = c.c_int
+        L.jl_test_remote_pos_device.argtypes = [c.c_int64, c.c_int64, c.c_int64, c.c_void_p, c.c_void_p]
+        L.jl_test_rope_angles_device.restype = c.c_int
+        L.jl_test_rope_angles_device.argtypes = [c.c_void_p, c.c_int64, c.c_int32, c.c_int32, c.c_double,
+                                                 c.c_void_p, c.c_void_p, c.c_void_p]
+        L.jl_set_profile_events.restype = c.c_int
+        L.jl_set_profile_events.argtypes = [c.c_void_p, c.c_void_p]
+        _lib = L
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise JetLongError(rc, lib().jl_last_error().decode())
+
+
+def group_size(L: int, w_pretrained: int) -> int:
+    """G = max(1, ceil(L / w_pretrained)), computed by the library."""
+    g = lib().jl_group_size(int(L), int(w_pretrained))
+    if g < 0:
+        _check(int(g))
+    return int(g)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _i32_array(seq: Optional[Sequence[int]]):
+    if seq is None:
+        return None
+    return (ctypes.c_int32 * len(seq))(*[int(x) for x in seq])
+
+
+def _i64_array(seq: Optional[Sequence[int]]):
+    if seq is None:
+        return None
+    return (ctypes.c_int64 * len(seq))(*[int(x) for x in seq])
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return FP32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _prefill_call(q, k, v, o, lse, cu, nseq, T, Hq, Hkv, kvmap, d, dt, w0, w_pt, base, scale,
+                  ws, ws_bytes, stream):
+    return lib().jl_bifocal_prefill(q, k, v, o, lse, cu, nseq, T, Hq, Hkv, kvmap, d, dt, int(w0),
+                                    int(w_pt), float(base), float(scale), ws, ctypes.byref(ws_bytes),
+                                    stream)
+
+
+def prefill_workspace_bytes(total_tokens: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                            dtype_code: int, *, w_pretrained: int, cu_seqlens=None,
+                            q_to_kv=None) -> int:
+    nseq = 1 if cu_seqlens is None else len(cu_seqlens) - 1
+    n = ctypes.c_size_t(0)
+    _check(_prefill_call(None, None, None, None, None, _i64_array(cu_seqlens), nseq, total_tokens,
+                         num_q_heads, num_kv_heads, _i32_array(q_to_kv), head_dim, dtype_code, 0,
+                         w_pretrained, 10000.0, 0.0, None, n, None))
+    return int(n.value)
+
+
+def prefill(q, k, v, *, w0: int, w_pretrained: int, rope_base: float, cu_seqlens=None,
+            scale: Optional[float] = None, q_to_kv=None, out=None, lse=None, return_lse=True,
+            workspace=None):
+    """Bifocal causal prefill.  q [T, Hq, d], k/v [T, Hkv, d] raw projections
+    (bf16 or fp32, CUDA, contiguous).  Returns (o [T, Hq, d], lse [Hq, T] fp32
+    or None).  cu_seqlens: host list of packed sequence offsets."""
+    import torch
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be GPU tensors")
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dt = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    nseq = 1 if cu_seqlens is None else len(cu_seqlens) - 1
+    cu = _i64_array(cu_seqlens)
+    kvmap = _i32_array(q_to_kv)
+    o = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+    n = ctypes.c_size_t(0)
+    _check(_prefill_call(None, None, None, None, None, cu, nseq, T, Hq, Hkv, kvmap, d, dt, w0,
+                         w_pretrained, rope_base, 0.0, None, n, None))
+    if workspace is None or workspace.numel() < n.value:
+        workspace = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=q.device)
+    n = ctypes.c_size_t(workspace.numel())
+    _check(_prefill_call(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse) if return_lse else None,
+                         cu, nseq, T, Hq, Hkv, kvmap, d, dt, w0, w_pretrained, rope_base,
+                         0.0 if scale is None else scale, _ptr(workspace), n, _stream(q.device)))
+    return o, (lse if return_lse else None)
+
+
+def decode_workspace_bytes(L: int, num_q_heads: int, num_kv_heads: int, head_dim: int = 128,
+                           q_to_kv=None) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().jl_bifocal_decode(None, None, None, int(L), None, None, num_q_heads, num_kv_heads,
+                                   _i32_array(q_to_kv), head_dim, BF16, 0, 1, 10000.0, 0.0, None,
+                                   ctypes.byref(n), None))
+    return int(n.value)
+
+
+def decode(q, k_cache, v_cache, L: int, *, w0: int, w_pretrained: int, rope_base: float,
+           scale: Optional[float] = None, q_to_kv=None, out=None, lse=None, return_lse=True,
+           workspace=None):
+    """One generation step.  q [Hq, d] bf16 (base-rotated at L - 1); caches
+    [L_cap, Hkv, d] bf16 holding base-rotated keys.  Returns (o [Hq, d], lse
+    [Hq] or None)."""
+    import torch
+    Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    if k_cache.shape[0] < L or v_cache.shape[0] < L:
+        raise ValueError("cache shorter than L")
+    q = q.contiguous()
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("caches must be contiguous")
+    o = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((Hq,), dtype=torch.float32, device=q.device)
+    kvmap = _i32_array(q_to_kv)
+    dt = _dtype_code(q)
+    n = ctypes.c_size_t(0)
+    _check(lib().jl_bifocal_decode(None, None, None, int(L), None, None, Hq, Hkv, kvmap, d, dt,
+                                   int(w0), int(w_pretrained), float(rope_base), 0.0, None,
+                                   ctypes.byref(n), None))
+    if workspace is None or workspace.numel() < n.value:
+        workspace = torch.empty(max(int(n.value), 16), dtype=torch.uint8, device=q.device)
+    n = ctypes.c_size_t(workspace.numel())
+    _check(lib().jl_bifocal_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), int(L), _ptr(o),
+                                   _ptr(lse) if return_lse else None, Hq, Hkv, kvmap, d, dt,
+                                   int(w0), int(w_pretrained), float(rope_base),
+                                   0.0 if scale is None else float(scale), _ptr(workspace),
+                                   ctypes.byref(n), _stream(q.device)))
+    return o, (lse if return_lse else None)

@@ -1,0 +1,282 @@
+// jl_api.hip - the C ABI of libjetlong.so: argument validation, workspace
+// protocol and dispatch onto the caller's HIP stream.  See include/jetlong.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/jetlong_testing.h"
+#include "jl_internal.h"
+
+#define JL_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_err[256] = "";
+thread_local hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(JL_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// theta_m / (2 pi) modulo 1 in unsigned 0.64 fixed point, from long double.
+// Only the fractional part matters: p * (n + f) = p * f modulo a whole turn.
+void build_freqs(JlFreqs* fr, int d, double base) {
+  const long double two_pi = 6.283185307179586476925286766559005768L;
+  for (int m = 0; m < d / 2; ++m) {
+    const long double theta = powl((long double)base, -(long double)(2 * m) / (long double)d);
+    long double f = fmodl(theta / two_pi, 1.0L);
+    if (f < 0) f += 1.0L;
+    fr->turn_frac[m] = (uint64_t)ldexpl(f, 64) ;
+  }
+  for (int m = d / 2; m < JL_MAX_HALF; ++m) fr->turn_frac[m] = 0;
+}
+
+int build_head_map(JlHeadMap* hm, int Hq, int Hkv, const int32_t* q_to_kv) {
+  if (Hq < 1 || Hkv < 1) return fail(JL_EINVAL, "num_q_heads and num_kv_heads must be >= 1");
+  if (Hq > JL_MAX_HEADS) return fail(JL_EUNSUPPORTED, "num_q_heads > %d", JL_MAX_HEADS);
+  if (Hkv > Hq) return fail(JL_EINVAL, "num_kv_heads > num_q_heads");
+  if (q_to_kv == nullptr) {
+    if (Hq % Hkv) return fail(JL_EINVAL, "num_q_heads %% num_kv_heads != 0 and no q_to_kv map", 0);
+    for (int h = 0; h < Hq; ++h) hm->kv_of[h] = (uint8_t)(h / (Hq / Hkv));
+  } else {
+    for (int h = 0; h < Hq; ++h) {
+      if (q_to_kv[h] < 0 || q_to_kv[h] >= Hkv) return fail(JL_EINVAL, "q_to_kv[%d] out of range", h);
+      hm->kv_of[h] = (uint8_t)q_to_kv[h];
+    }
+  }
+  for (int h = Hq; h < JL_MAX_HEADS; ++h) hm->kv_of[h] = 0;
+  return JL_OK;
+}
+
+int check_common(int64_t w0, int64_t w_pretrained, double rope_base) {
+  if (w0 < 0) return fail(JL_EINVAL, "w0 must be >= 0");
+  if (w_pretrained < 1) return fail(JL_EINVAL, "w_pretrained must be >= 1");
+  if (!(rope_base > 0.0) || !isfinite(rope_base)) return fail(JL_EINVAL, "rope_base must be finite and > 0");
+  return JL_OK;
+}
+
+struct PrefillPlan {
+  JlSeqs seqs;
+  int32_t max_len;
+  int64_t t_pad;
+  size_t off_qb, off_qr, off_kb, off_kr, off_vt, off_lo, total;
+};
+
+}  // namespace
+
+JL_EXPORT int64_t jl_group_size(int64_t L, int64_t w_pretrained) {
+  if (L < 0 || w_pretrained < 1) return fail(JL_EINVAL, "jl_group_size needs L >= 0 and w_pretrained >= 1");
+  return jl_group_size_i64(L, w_pretrained);
+}
+
+JL_EXPORT const char* jl_last_error(void) { return g_err; }
+
+JL_EXPORT int jl_bifocal_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 const int64_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                                 int32_t num_q_heads, int32_t num_kv_heads, const int32_t* q_to_kv,
+                                 int32_t head_dim, jl_dtype dtype, int64_t w0, int64_t w_pretrained,
+                                 double rope_base, float softmax_scale, void* workspace,
+                                 size_t* workspace_bytes, void* hip_stream) {
+  if (workspace_bytes == nullptr) return fail(JL_EINVAL, "workspace_bytes is NULL");
+  if (total_tokens < 0) return fail(JL_EINVAL, "total_tokens < 0");
+  if (dtype != JL_BF16 && dtype != JL_FP32) return fail(JL_EINVAL, "unknown dtype %d", (int)dtype);
+  int rc = check_common(w0, w_pretrained, rope_base);
+  if (rc) return rc;
+  JlHeadMap hm;
+  rc = build_head_map(&hm, num_q_heads, num_kv_heads, q_to_kv);
+  if (rc) return rc;
+  if (dtype == JL_BF16 && head_dim != 128) return fail(JL_EUNSUPPORTED, "bf16 prefill needs head_dim 128");
+  if (dtype == JL_FP32 && head_dim != 64 && head_dim != 128)
+    return fail(JL_EUNSUPPORTED, "fp32 prefill needs head_dim 64 or 128");
+  if (num_seqs < 1) return fail(JL_EINVAL, "num_seqs must be >= 1");
+  if (num_seqs > JL_MAX_SEQS) return fail(JL_EUNSUPPORTED, "num_seqs > %d", JL_MAX_SEQS);
+  if (cu_seqlens == nullptr && num_seqs != 1) return fail(JL_EINVAL, "cu_seqlens is NULL with num_seqs > 1");
+  if (total_tokens > (int64_t)INT32_MAX - 512) return fail(JL_EUNSUPPORTED, "total_tokens too large");
+
+  PrefillPlan pl;
+  memset(&pl, 0, sizeof(pl));
+  pl.seqs.nseq = num_seqs;
+  for (int b = 0; b < num_seqs; ++b) {
+    int64_t s0 = cu_seqlens ? cu_seqlens[b] : 0;
+    int64_t s1 = cu_seqlens ? cu_seqlens[b + 1] : total_tokens;
+    if (b == 0 && s0 != 0) return fail(JL_EINVAL, "cu_seqlens[0] != 0");
+    if (s1 < s0) return fail(JL_EINVAL, "cu_seqlens decreases at %d", b);
+    pl.seqs.start[b] = (int32_t)s0;
+    pl.seqs.len[b] = (int32_t)(s1 - s0);
+    pl.seqs.G[b] = (int32_t)jl_group_size_i64(s1 - s0, w_pretrained);
+    if (pl.seqs.G[b] > 1) pl.seqs.any_remote = 1;
+    if (pl.seqs.len[b] > pl.max_len) pl.max_len = pl.seqs.len[b];
+  }
+  if (cu_seqlens && cu_seqlens[num_seqs] != total_tokens)
+    return fail(JL_EINVAL, "cu_seqlens[num_seqs] != total_tokens");
+
+  const size_t el = dtype == JL_BF16 ? 2 : 4;
+  pl.t_pad = jl_prefill_t_pad(total_tokens);
+  const size_t nq = (size_t)num_q_heads * pl.t_pad * head_dim * el;
+  const size_t nk = (size_t)num_kv_heads * pl.t_pad * head_dim * el;
+  size_t off = 0;
+  pl.off_qb = off; off += align256(nq);
+  pl.off_qr = off; if (pl.seqs.any_remote) off += align256(nq);
+  pl.off_kb = off; off += align256(nk);
+  pl.off_kr = off; if (pl.seqs.any_remote) off += align256(nk);
+  pl.off_vt = off; if (dtype == JL_BF16) off += align256(nk);
+  // split-operand residuals of the first JL_LO_ROWS positions (bf16 path)
+  const size_t lrows = (size_t)num_seqs * JL_LO_ROWS;
+  const size_t nqlo = (size_t)num_q_heads * lrows * head_dim * el;
+  const size_t nklo = (size_t)num_kv_heads * lrows * head_dim * el;
+  pl.off_lo = off; if (dtype == JL_BF16) off += 2 * align256(nqlo) + 2 * align256(nklo);
+  pl.total = total_tokens == 0 ? 0 : off;
+
+  if (workspace == nullptr) {
+    *workspace_bytes = pl.total;
+    return JL_OK;
+  }
+  if (*workspace_bytes < pl.total)
+    return fail(JL_ENOSPC, "workspace has %zu bytes, %zu needed", *workspace_bytes, pl.total);
+  if (total_tokens == 0) return JL_OK;
+  if (!q || !k || !v || !o) return fail(JL_EINVAL, "q, k, v and o must be device pointers");
+  if (((uintptr_t)workspace & 255) != 0) return fail(JL_EINVAL, "workspace must be 256-byte aligned");
+  if (dtype == JL_BF16 && (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15))
+    return fail(JL_EINVAL, "bf16 tensors must be 16-byte aligned");
+
+  JlFreqs fr;
+  build_freqs(&fr, head_dim, rope_base);
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
+  hipStream_t st = (hipStream_t)hip_stream;
+  char* wsb = (char*)workspace;
+  JlPrefillWs ws;
+  ws.qb = wsb + pl.off_qb;
+  ws.qr = pl.seqs.any_remote ? (void*)(wsb + pl.off_qr) : ws.qb;
+  ws.kb = wsb + pl.off_kb;
+  ws.kr = pl.seqs.any_remote ? (void*)(wsb + pl.off_kr) : ws.kb;
+  ws.vt = dtype == JL_BF16 ? (void*)(wsb + pl.off_vt) : nullptr;
+  ws.qb_lo = ws.qr_lo = ws.kb_lo = ws.kr_lo = nullptr;
+  if (dtype == JL_BF16) {
+    const size_t lrows = (size_t)num_seqs * JL_LO_ROWS;
+    const size_t nqlo = align256((size_t)num_q_heads * lrows * head_dim * el);
+    const size_t nklo = align256((size_t)num_kv_heads * lrows * head_dim * el);
+    ws.qb_lo = wsb + pl.off_lo;
+    ws.qr_lo = wsb + pl.off_lo + nqlo;
+    ws.kb_lo = wsb + pl.off_lo + 2 * nqlo;
+    ws.kr_lo = wsb + pl.off_lo + 2 * nqlo + nklo;
+  }
+  ws.t_pad = pl.t_pad;
+
+  hipError_t e = jl_launch_rope_prepass(q, k, ws, (int)el, total_tokens, num_q_heads, num_kv_heads,
+                                        head_dim, pl.seqs, fr, st);
+  if (e != hipSuccess) return hip_fail(e, "rope pre-pass launch");
+  if (dtype == JL_BF16) {
+    e = jl_launch_transpose_v(v, ws, total_tokens, num_kv_heads, st);
+    if (e != hipSuccess) return hip_fail(e, "v transpose launch");
+    if (g_ev_before) hipEventRecord(g_ev_before, st);
+    e = jl_launch_prefill_bf16(ws, o, lse, total_tokens, num_q_heads, num_kv_heads, hm, pl.seqs, w0,
+                               scale, pl.max_len, st);
+    if (e != hipSuccess) return hip_fail(e, "bf16 prefill launch");
+    if (g_ev_after) hipEventRecord(g_ev_after, st);
+  } else {
+    if (g_ev_before) hipEventRecord(g_ev_before, st);
+    e = jl_launch_prefill_fp32(ws, (const float*)v, (float*)o, lse, total_tokens, num_q_heads,
+                               num_kv_heads, head_dim, hm, pl.seqs, w0, scale, pl.max_len, st);
+    if (e != hipSuccess) return hip_fail(e, "fp32 prefill launch");
+    if (g_ev_after) hipEventRecord(g_ev_after, st);
+  }
+  return JL_OK;
+}
+
+JL_EXPORT int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_cache, int64_t L,
+                                void* o, float* lse, int32_t num_q_heads, int32_t num_kv_heads,
+                                const int32_t* q_to_kv, int32_t head_dim, jl_dtype dtype, int64_t w0,
+                                int64_t w_pretrained, double rope_base, float softmax_scale,
+                                void* workspace, size_t* workspace_bytes, void* hip_stream) {
+  if (workspace_bytes == nullptr) return fail(JL_EINVAL, "workspace_bytes is NULL");
+  if (L < 0) return fail(JL_EINVAL, "L < 0");
+  if (dtype != JL_BF16 && dtype != JL_FP32) return fail(JL_EINVAL, "unknown dtype %d", (int)dtype);
+  int rc = check_common(w0, w_pretrained, rope_base);
+  if (rc) return rc;
+  JlHeadMap hm;
+  rc = build_head_map(&hm, num_q_heads, num_kv_heads, q_to_kv);
+  if (rc) return rc;
+  if (dtype != JL_BF16) return fail(JL_EUNSUPPORTED, "decode is built for bf16 caches only");
+  if (head_dim != 128) return fail(JL_EUNSUPPORTED, "decode needs head_dim 128");
+  if (num_q_heads > 64 || num_kv_heads > 8)
+    return fail(JL_EUNSUPPORTED, "decode supports up to 64 q heads and 8 kv heads");
+  const int NG = num_q_heads / num_kv_heads;
+  if (num_q_heads % num_kv_heads || (NG != 1 && NG != 2 && NG != 4 && NG != 8))
+    return fail(JL_EUNSUPPORTED, "decode needs 1, 2, 4 or 8 q heads per kv head");
+  {
+    int cnt[8] = {0};
+    for (int h = 0; h < num_q_heads; ++h) cnt[hm.kv_of[h]]++;
+    for (int g = 0; g < num_kv_heads; ++g)
+      if (cnt[g] != NG) return fail(JL_EUNSUPPORTED, "decode needs the same number of q heads per kv head");
+  }
+  if (L > (int64_t)INT32_MAX) return fail(JL_EUNSUPPORTED, "L >= 2^31");
+  const size_t need = L == 0 ? 0 : jl_decode_workspace_bytes(L, num_q_heads, head_dim);
+  if (workspace == nullptr) {
+    *workspace_bytes = need;
+    return JL_OK;
+  }
+  if (*workspace_bytes < need) return fail(JL_ENOSPC, "workspace has %zu bytes, %zu needed", *workspace_bytes, need);
+  if (L == 0) return JL_OK;
+  if (!q || !k_cache || !v_cache || !o) return fail(JL_EINVAL, "q, caches and o must be device pointers");
+  if (((uintptr_t)workspace & 15) || (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15))
+    return fail(JL_EINVAL, "q, caches and workspace must be 16-byte aligned");
+
+  JlFreqs fr;
+  build_freqs(&fr, head_dim, rope_base);
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
+  const int32_t G = (int32_t)jl_group_size_i64(L, w_pretrained);
+  if (g_ev_before) hipEventRecord(g_ev_before, (hipStream_t)hip_stream);
+  hipError_t e = jl_launch_decode_bf16(q, k_cache, v_cache, L, o, lse, num_q_heads, num_kv_heads, hm, w0,
+                                       G, scale, fr, workspace, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  if (g_ev_after) hipEventRecord(g_ev_after, (hipStream_t)hip_stream);
+  return JL_OK;
+}
+
+// ------------------------------------------------------------------ test hooks
+
+JL_EXPORT int jl_set_profile_events(void* before, void* after) {
+  if ((before == nullptr) != (after == nullptr)) return fail(JL_EINVAL, "set both events or neither");
+  g_ev_before = (hipEvent_t)before;
+  g_ev_after = (hipEvent_t)after;
+  return JL_OK;
+}
+
+JL_EXPORT int jl_test_group_size_device(const int64_t* L, int64_t n, int64_t w_pretrained, int64_t* G_out,
+                                        void* hip_stream) {
+  if (n < 0 || w_pretrained < 1 || (n > 0 && (!L || !G_out))) return fail(JL_EINVAL, "bad arguments");
+  if (n == 0) return JL_OK;
+  hipError_t e = jl_launch_test_group_size(L, n, w_pretrained, G_out, (hipStream_t)hip_stream);
+  return e == hipSuccess ? JL_OK : hip_fail(e, "test kernel");
+}
+
+JL_EXPORT int jl_test_remote_pos_device(int64_t x0, int64_t n, int64_t G, int32_t* f_out, void* hip_stream) {
+  if (x0 < 0 || n < 0 || G < 1 || G > INT32_MAX || x0 + n > (int64_t)INT32_MAX || (n > 0 && !f_out))
+    return fail(JL_EINVAL, "bad arguments");
+  if (n == 0) return JL_OK;
+  hipError_t e = jl_launch_test_remote_pos(x0, n, (int32_t)G, f_out, (hipStream_t)hip_stream);
+  return e == hipSuccess ? JL_OK : hip_fail(e, "test kernel");
+}
+
+JL_EXPORT int jl_test_rope_angles_device(const int32_t* pos, int64_t n, int32_t m, int32_t head_dim,
+                                         double rope_base, float* cos_out, float* sin_out, void* hip_stream) {
+  if (n < 0 || head_dim < 2 || head_dim > 2 * JL_MAX_HALF || (head_dim & 1) || m < 0 || m >= head_dim / 2 ||
+      !(rope_base > 0.0) || (n > 0 && (!pos || !cos_out || !sin_out)))
+    return fail(JL_EINVAL, "bad arguments");
+  if (n == 0) return JL_OK;
+  JlFreqs fr;
+  build_freqs(&fr, head_dim, rope_base);
+  hipError_t e = jl_launch_test_angles(pos, n, fr.turn_frac[m], cos_out, sin_out, (hipStream_t)hip_stream);
+  return e == hipSuccess ? JL_OK : hip_fail(e, "test kernel");
+}

@@ -1,0 +1,90 @@
+// jl_internal.h - kernel parameter blocks and launcher declarations shared by
+// the C ABI (jl_api.hip) and the kernels.  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/jetlong.h"
+#include "jl_mapper.h"
+
+#define JL_MAX_HEADS 128   // q heads per call
+#define JL_MAX_HALF 64     // head_dim / 2
+
+// Per-sequence schedule of one prefill call (packed varlen batch), built on
+// the host from cu_seqlens and passed by value.
+struct JlSeqs {
+  int32_t nseq;
+  int32_t any_remote;          // 1 if some sequence has G > 1
+  int32_t start[JL_MAX_SEQS];  // first packed token of the sequence
+  int32_t len[JL_MAX_SEQS];    // its length L_b
+  int32_t G[JL_MAX_SEQS];      // its group size G_b
+};
+
+// RoPE frequencies theta_m / (2 pi) in unsigned 0.64 fixed point (see
+// jl_angle_turns in jl_mapper.h).
+struct JlFreqs {
+  uint64_t turn_frac[JL_MAX_HALF];
+};
+
+struct JlHeadMap {
+  uint8_t kv_of[JL_MAX_HEADS];
+};
+
+// Workspace of the prefill path: rotated operands, head-major.
+//   qb, qr   [Hq][T_pad][d]   q rotated at p and at f(p)
+//   kb, kr   [Hkv][T_pad][d]  k rotated at p and at f(p)
+//   vt       [Hkv][d][T_pad]  v transposed (bf16 path only)
+// Rows T .. T_pad-1 are zero.  qr / kr alias qb / kb when no sequence has
+// G > 1.
+//   qb_lo, qr_lo [Hq][nseq * JL_LO_ROWS][d], kb_lo, kr_lo [Hkv][nseq * JL_LO_ROWS][d]
+//            (bf16 path only) the rounding residuals bf16(x - bf16(x)) of the
+//            first JL_LO_ROWS positions of every sequence, row b * JL_LO_ROWS + p
+struct JlPrefillWs {
+  void* qb;
+  void* qr;
+  void* kb;
+  void* kr;
+  void* vt;
+  void* qb_lo;
+  void* qr_lo;
+  void* kb_lo;
+  void* kr_lo;
+  int64_t t_pad;
+};
+
+// Rows whose scores use split (hi + lo) bf16 operands: the first q tile of a
+// sequence, whose rows see at most this many keys.
+#define JL_LO_ROWS 128
+
+int64_t jl_prefill_t_pad(int64_t total_tokens);
+
+// rope pre-pass: writes qb, qr, kb, kr (elem = 2 for bf16, 4 for fp32)
+hipError_t jl_launch_rope_prepass(const void* q, const void* k, const JlPrefillWs& ws, int elem_bytes,
+                                  int64_t total_tokens, int32_t Hq, int32_t Hkv, int32_t d,
+                                  const JlSeqs& seqs, const JlFreqs& fr, hipStream_t st);
+hipError_t jl_launch_transpose_v(const void* v, const JlPrefillWs& ws, int64_t total_tokens,
+                                 int32_t Hkv, hipStream_t st);
+
+hipError_t jl_launch_prefill_fp32(const JlPrefillWs& ws, const float* v, float* o, float* lse,
+                                  int64_t total_tokens, int32_t Hq, int32_t Hkv, int32_t d,
+                                  const JlHeadMap& hm, const JlSeqs& seqs, int64_t w0, float scale,
+                                  int32_t max_len, hipStream_t st);
+
+hipError_t jl_launch_prefill_bf16(const JlPrefillWs& ws, void* o, float* lse, int64_t total_tokens,
+                                  int32_t Hq, int32_t Hkv, const JlHeadMap& hm, const JlSeqs& seqs,
+                                  int64_t w0, float scale, int32_t max_len, hipStream_t st);
+
+// decode
+size_t jl_decode_workspace_bytes(int64_t L, int32_t Hq, int32_t d);
+hipError_t jl_launch_decode_bf16(const void* q, const void* k_cache, const void* v_cache, int64_t L,
+                                 void* o, float* lse, int32_t Hq, int32_t Hkv,
+                                 const JlHeadMap& hm, int64_t w0, int32_t G, float scale,
+                                 const JlFreqs& fr, void* workspace, hipStream_t st);
+
+// test hooks
+hipError_t jl_launch_test_group_size(const int64_t* L, int64_t n, int64_t w, int64_t* G,
+                                     hipStream_t st);
+hipError_t jl_launch_test_remote_pos(int64_t x0, int64_t n, int32_t G, int32_t* f, hipStream_t st);
+hipError_t jl_launch_test_angles(const int32_t* pos, int64_t n, uint64_t turn_frac, float* c,
+                                 float* s, hipStream_t st);

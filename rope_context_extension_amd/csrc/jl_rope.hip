@@ -1,0 +1,185 @@
+// jl_rope.hip - RoPE pre-pass of the prefill path.
+//
+// Rotates every q and k row once, at its absolute position p (base grid) and
+// at its aliased position f(p) = floor(p / G) (remote grid), so the attention
+// kernel never re-rotates a key tile per visit (technical summary on
+// gist.science, Methodology item 1: classical RoPE inside the local window,
+// positions mapped by f beyond it; G per sequence from its length).
+// Also writes V transposed for the bf16 attention kernel, whose PV product
+// reads 8 consecutive keys of one channel per lane.
+#include "jl_internal.h"
+
+int64_t jl_prefill_t_pad(int64_t total_tokens) {
+  // a full 128-row q tile and a 64-key tile may start at any row < T
+  return ((total_tokens + 128 + 63) / 64) * 64;
+}
+
+namespace {
+
+template <typename T>
+__device__ inline float ld_f(const T* p) { return (float)(*p); }
+template <typename T>
+__device__ inline void st_f(T* p, float x) { *p = (T)x; }
+
+// Stores y rounded to T and, when lo != nullptr, the residual y - T(y)
+// rounded to T (used for the first positions of a sequence on the bf16 path).
+template <typename T>
+__device__ inline void st_split(T* hi, T* lo, float y) {
+  const T h = (T)y;
+  *hi = h;
+  if (lo != nullptr) *lo = (T)(y - (float)h);
+}
+
+// One thread per (token, frequency m); it rotates pair (m, m + d/2) of every
+// q and k head of that token with one sin/cos evaluation per grid.
+template <typename T>
+__global__ void __launch_bounds__(256) rope_prepass_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, T* __restrict__ qb, T* __restrict__ qr,
+    T* __restrict__ kb, T* __restrict__ kr, T* __restrict__ qb_lo, T* __restrict__ qr_lo,
+    T* __restrict__ kb_lo, T* __restrict__ kr_lo, int64_t total, int64_t t_pad, int Hq, int Hkv,
+    int d, JlSeqs seqs, JlFreqs fr, int write_remote) {
+  const int half = d >> 1;
+  const int tpb = 256 / half;               // tokens per block
+  const int tl = threadIdx.x / half;
+  const int m = threadIdx.x % half;
+  const int b = blockIdx.y;
+  const int64_t p = (int64_t)blockIdx.x * tpb + tl;
+
+  if (b == seqs.nseq) {                     // zero padding rows T .. t_pad-1
+    const int64_t t = total + p;
+    if (t >= t_pad) return;
+    for (int h = 0; h < Hq; ++h) {
+      T* r0 = qb + ((int64_t)h * t_pad + t) * d;
+      st_f(r0 + m, 0.f); st_f(r0 + m + half, 0.f);
+      if (write_remote) { T* r1 = qr + ((int64_t)h * t_pad + t) * d; st_f(r1 + m, 0.f); st_f(r1 + m + half, 0.f); }
+    }
+    for (int h = 0; h < Hkv; ++h) {
+      T* r0 = kb + ((int64_t)h * t_pad + t) * d;
+      st_f(r0 + m, 0.f); st_f(r0 + m + half, 0.f);
+      if (write_remote) { T* r1 = kr + ((int64_t)h * t_pad + t) * d; st_f(r1 + m, 0.f); st_f(r1 + m + half, 0.f); }
+    }
+    return;
+  }
+  if (p >= seqs.len[b]) {
+    // residual rows past the end of a short sequence are zero
+    if (qb_lo != nullptr && p < JL_LO_ROWS) {
+      const int64_t lrows = (int64_t)seqs.nseq * JL_LO_ROWS;
+      const int64_t lrow = (int64_t)b * JL_LO_ROWS + p;
+      for (int h = 0; h < Hq; ++h) {
+        st_f(qb_lo + ((int64_t)h * lrows + lrow) * d + m, 0.f);
+        st_f(qb_lo + ((int64_t)h * lrows + lrow) * d + m + half, 0.f);
+        st_f(qr_lo + ((int64_t)h * lrows + lrow) * d + m, 0.f);
+        st_f(qr_lo + ((int64_t)h * lrows + lrow) * d + m + half, 0.f);
+      }
+      for (int h = 0; h < Hkv; ++h) {
+        st_f(kb_lo + ((int64_t)h * lrows + lrow) * d + m, 0.f);
+        st_f(kb_lo + ((int64_t)h * lrows + lrow) * d + m + half, 0.f);
+        st_f(kr_lo + ((int64_t)h * lrows + lrow) * d + m, 0.f);
+        st_f(kr_lo + ((int64_t)h * lrows + lrow) * d + m + half, 0.f);
+      }
+    }
+    return;
+  }
+  const int64_t t = seqs.start[b] + p;
+  const int pos = (int)p;
+  float cb, sb, cr = 1.f, sr = 0.f;
+  jl_rope_sincos(pos, fr.turn_frac[m], &sb, &cb);
+  if (write_remote) jl_rope_sincos(jl_remote_pos(pos, seqs.G[b]), fr.turn_frac[m], &sr, &cr);
+
+  const bool lo = qb_lo != nullptr && pos < JL_LO_ROWS;
+  const int64_t lrow = (int64_t)b * JL_LO_ROWS + pos;
+  const int64_t lrows = (int64_t)seqs.nseq * JL_LO_ROWS;
+  for (int h = 0; h < Hq; ++h) {
+    const T* x = q + (t * Hq + h) * d;
+    const float x1 = ld_f(x + m), x2 = ld_f(x + m + half);
+    T* yb = qb + ((int64_t)h * t_pad + t) * d;
+    T* lb = lo ? qb_lo + ((int64_t)h * lrows + lrow) * d : nullptr;
+    st_split(yb + m, lb ? lb + m : nullptr, x1 * cb - x2 * sb);
+    st_split(yb + m + half, lb ? lb + m + half : nullptr, x2 * cb + x1 * sb);
+    if (write_remote) {
+      T* yr = qr + ((int64_t)h * t_pad + t) * d;
+      T* lr = lo ? qr_lo + ((int64_t)h * lrows + lrow) * d : nullptr;
+      st_split(yr + m, lr ? lr + m : nullptr, x1 * cr - x2 * sr);
+      st_split(yr + m + half, lr ? lr + m + half : nullptr, x2 * cr + x1 * sr);
+    }
+  }
+  for (int h = 0; h < Hkv; ++h) {
+    const T* x = k + (t * Hkv + h) * d;
+    const float x1 = ld_f(x + m), x2 = ld_f(x + m + half);
+    T* yb = kb + ((int64_t)h * t_pad + t) * d;
+    T* lb = lo ? kb_lo + ((int64_t)h * lrows + lrow) * d : nullptr;
+    st_split(yb + m, lb ? lb + m : nullptr, x1 * cb - x2 * sb);
+    st_split(yb + m + half, lb ? lb + m + half : nullptr, x2 * cb + x1 * sb);
+    if (write_remote) {
+      T* yr = kr + ((int64_t)h * t_pad + t) * d;
+      T* lr = lo ? kr_lo + ((int64_t)h * lrows + lrow) * d : nullptr;
+      st_split(yr + m, lr ? lr + m : nullptr, x1 * cr - x2 * sr);
+      st_split(yr + m + half, lr ? lr + m + half : nullptr, x2 * cr + x1 * sr);
+    }
+  }
+}
+
+// v [T][Hkv][128] bf16 -> vt [Hkv][128][t_pad], 64 tokens per block through LDS.
+__global__ void __launch_bounds__(256) transpose_v_kernel(const __bf16* __restrict__ v,
+                                                          __bf16* __restrict__ vt, int64_t total,
+                                                          int64_t t_pad, int Hkv) {
+  constexpr int D = 128, TB = 64, P = D + 8;
+  __shared__ __bf16 tile[TB * P];
+  const int h = blockIdx.y;
+  const int64_t t0 = (int64_t)blockIdx.x * TB;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int c = it * 256 + tid;
+    const int tok = c >> 4, col = (c & 15) * 8;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (t0 + tok < total) val = *(const uint4*)(v + ((t0 + tok) * Hkv + h) * D + col);
+    *(uint4*)(tile + tok * P + col) = val;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int c = it * 256 + tid;
+    const int dd = c >> 3, tk = (c & 7) * 8;
+    __bf16 out[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = tile[(tk + e) * P + dd];
+    *(uint4*)(vt + ((int64_t)h * D + dd) * t_pad + t0 + tk) = *(const uint4*)out;
+  }
+}
+
+}  // namespace
+
+hipError_t jl_launch_rope_prepass(const void* q, const void* k, const JlPrefillWs& ws, int elem_bytes,
+                                  int64_t total_tokens, int32_t Hq, int32_t Hkv, int32_t d,
+                                  const JlSeqs& seqs, const JlFreqs& fr, hipStream_t st) {
+  const int half = d / 2;
+  const int tpb = 256 / half;
+  int32_t max_len = 0;
+  for (int b = 0; b < seqs.nseq; ++b) max_len = seqs.len[b] > max_len ? seqs.len[b] : max_len;
+  const int64_t pad_rows = ws.t_pad - total_tokens;
+  int64_t need = (max_len > pad_rows ? max_len : pad_rows);
+  if (ws.qb_lo != nullptr && need < JL_LO_ROWS) need = JL_LO_ROWS;
+  dim3 grid((unsigned)((need + tpb - 1) / tpb), (unsigned)(seqs.nseq + 1));
+  const int wr = seqs.any_remote;
+  if (elem_bytes == 2) {
+    rope_prepass_kernel<__bf16><<<grid, 256, 0, st>>>(
+        (const __bf16*)q, (const __bf16*)k, (__bf16*)ws.qb, (__bf16*)ws.qr, (__bf16*)ws.kb,
+        (__bf16*)ws.kr, (__bf16*)ws.qb_lo, (__bf16*)ws.qr_lo, (__bf16*)ws.kb_lo,
+        (__bf16*)ws.kr_lo, total_tokens, ws.t_pad, Hq, Hkv, d, seqs, fr, wr);
+  } else {
+    rope_prepass_kernel<float><<<grid, 256, 0, st>>>(
+        (const float*)q, (const float*)k, (float*)ws.qb, (float*)ws.qr, (float*)ws.kb,
+        (float*)ws.kr, nullptr, nullptr, nullptr, nullptr, total_tokens, ws.t_pad, Hq, Hkv, d,
+        seqs, fr, wr);
+  }
+  return hipGetLastError();
+}
+
+hipError_t jl_launch_transpose_v(const void* v, const JlPrefillWs& ws, int64_t total_tokens,
+                                 int32_t Hkv, hipStream_t st) {
+  dim3 grid((unsigned)(ws.t_pad / 64), (unsigned)Hkv);
+  transpose_v_kernel<<<grid, 256, 0, st>>>((const __bf16*)v, (__bf16*)ws.vt, total_tokens, ws.t_pad,
+                                           Hkv);
+  return hipGetLastError();
+}

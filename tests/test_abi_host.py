@@ -1,0 +1,134 @@
+"""Host-side tests of the C ABI (no GPU): the library loads, exports every
+declared entry point, computes G exactly, and rejects invalid arguments
+before launching anything."""
+
+import ctypes
+
+import pytest
+
+import oracle
+from jl_testutil import ensure_built, header_symbols
+
+jl = ensure_built()
+L = jl.lib()
+JL_OK, JL_EINVAL, JL_EUNSUPPORTED, JL_ENOSPC = 0, -1, -2, -3
+
+
+def test_exports_every_declared_symbol():
+    names = header_symbols()
+    assert {"jl_group_size", "jl_bifocal_prefill", "jl_bifocal_decode", "jl_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_group_size_matches_oracle():
+    for w in (1, 3, 64, 4096, 32768):
+        for n in list(range(0, 3000)) + [32767, 32768, 32769, 65536, 65537, 131072, 2**40 + 7, 2**62]:
+            assert jl.group_size(n, w) == oracle.group_size(n, w), (n, w)
+
+
+def test_group_size_rejects():
+    assert L.jl_group_size(-1, 5) == JL_EINVAL
+    assert L.jl_group_size(5, 0) == JL_EINVAL
+    assert b"w_pretrained" in L.jl_last_error()
+
+
+def _pf(**kw):
+    a = dict(q=None, k=None, v=None, o=None, lse=None, cu=None, nseq=1, T=256, Hq=4, Hkv=2, kvmap=None,
+             d=128, dt=jl.BF16, w0=16, wpt=64, base=10000.0, scale=0.0, ws=None, nbytes=0)
+    a.update(kw)
+    n = ctypes.c_size_t(a["nbytes"])
+    rc = L.jl_bifocal_prefill(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"], a["nseq"], a["T"],
+                              a["Hq"], a["Hkv"], a["kvmap"], a["d"], a["dt"], a["w0"], a["wpt"],
+                              a["base"], a["scale"], a["ws"], ctypes.byref(n), None)
+    return rc, n.value
+
+
+def test_prefill_size_query():
+    rc, n = _pf()
+    assert rc == JL_OK and n > 0
+    rc1, n1 = _pf(wpt=1000)          # G = 1: no remote copies
+    assert rc1 == JL_OK and n1 < n
+    rc0, n0 = _pf(T=0)
+    assert rc0 == JL_OK and n0 == 0
+    rc2, n2 = _pf(dt=jl.FP32, d=64)
+    assert rc2 == JL_OK and n2 > 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), JL_EINVAL),
+    (dict(Hq=3, Hkv=2), JL_EINVAL),
+    (dict(Hq=0), JL_EINVAL),
+    (dict(Hq=256, Hkv=2), JL_EUNSUPPORTED),
+    (dict(d=96), JL_EUNSUPPORTED),
+    (dict(d=64), JL_EUNSUPPORTED),            # bf16 path is built for d = 128
+    (dict(dt=7), JL_EINVAL),
+    (dict(w0=-1), JL_EINVAL),
+    (dict(wpt=0), JL_EINVAL),
+    (dict(base=0.0), JL_EINVAL),
+    (dict(base=float("nan")), JL_EINVAL),
+    (dict(nseq=0), JL_EINVAL),
+    (dict(nseq=65, cu=(ctypes.c_int64 * 66)(*range(66)), T=65), JL_EUNSUPPORTED),
+    (dict(nseq=2), JL_EINVAL),                # cu_seqlens missing
+    (dict(nseq=2, cu=(ctypes.c_int64 * 3)(0, 300, 256)), JL_EINVAL),
+    (dict(nseq=2, cu=(ctypes.c_int64 * 3)(1, 100, 256)), JL_EINVAL),
+    (dict(nseq=2, cu=(ctypes.c_int64 * 3)(0, 100, 200)), JL_EINVAL),
+    (dict(kvmap=(ctypes.c_int32 * 4)(0, 1, 2, 0)), JL_EINVAL),
+    (dict(T=2**31), JL_EUNSUPPORTED),
+])
+def test_prefill_rejects(kw, code):
+    rc, _ = _pf(**kw)
+    assert rc == code, L.jl_last_error()
+    assert L.jl_last_error()
+
+
+def test_prefill_workspace_too_small_is_enospc():
+    rc, n = _pf()
+    # a non-NULL workspace that is too small is refused before any device access
+    rc2, _ = _pf(ws=0x1000, nbytes=n - 1, q=0x1000, k=0x1000, v=0x1000, o=0x1000)
+    assert rc2 == JL_ENOSPC
+
+
+def test_prefill_null_tensor_is_einval():
+    rc, n = _pf()
+    rc2, _ = _pf(ws=0x1000, nbytes=n)
+    assert rc2 == JL_EINVAL
+
+
+def _dec(**kw):
+    a = dict(L=1000, Hq=32, Hkv=8, kvmap=None, d=128, dt=jl.BF16, w0=16, wpt=64, base=1e6, ws=None, nbytes=0)
+    a.update(kw)
+    n = ctypes.c_size_t(a["nbytes"])
+    rc = L.jl_bifocal_decode(None, None, None, a["L"], None, None, a["Hq"], a["Hkv"], a["kvmap"], a["d"],
+                             a["dt"], a["w0"], a["wpt"], a["base"], 0.0, a["ws"], ctypes.byref(n), None)
+    return rc, n.value
+
+
+def test_decode_size_query():
+    rc, n = _dec()
+    assert rc == JL_OK and n > 0
+    rc, n = _dec(L=0)
+    assert rc == JL_OK and n == 0
+    assert _dec(L=131072)[1] >= _dec(L=1000)[1]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(L=-1), JL_EINVAL),
+    (dict(dt=jl.FP32), JL_EUNSUPPORTED),
+    (dict(d=64), JL_EUNSUPPORTED),
+    (dict(Hq=12, Hkv=4), JL_EUNSUPPORTED),    # 3 q heads per kv head
+    (dict(Hq=32, Hkv=16), JL_EUNSUPPORTED),
+    (dict(Hq=4, Hkv=2, kvmap=(ctypes.c_int32 * 4)(0, 0, 0, 1)), JL_EUNSUPPORTED),
+    (dict(w0=-3), JL_EINVAL),
+    (dict(wpt=0), JL_EINVAL),
+    (dict(L=2**31), JL_EUNSUPPORTED),
+])
+def test_decode_rejects(kw, code):
+    rc, _ = _dec(**kw)
+    assert rc == code, L.jl_last_error()
+
+
+def test_decode_workspace_too_small_is_enospc():
+    _, n = _dec()
+    rc, _ = _dec(ws=0x1000, nbytes=n - 1)
+    assert rc == JL_ENOSPC

@@ -1,0 +1,95 @@
+"""Parity of the HIP bifocal decode step with the fp64 oracle, including the
+steps that cross a G boundary, and a check that the cache is never written
+(technical summary, Methodology item 2: correction rotation Delta applied to
+the query and the cached keys in registers)."""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from jl_testutil import BF16_LSE_RTOL, BF16_O_ATOL, gpu_or_skip, lse_rel_err, max_abs
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _decode_case(jl, torch, L, Hq, Hkv, w0, wpt, base, seed, L_cap=None, q_to_kv=None):
+    cfg = W.DecodeConfig("case", Hq, Hkv, 128, L, w0, wpt, base, seed)
+    q, kc, vc = W.make_decode_inputs(cfg, L_cap=L_cap)
+    _say(f"[decode] L={L} Hq={Hq} Hkv={Hkv} w0={w0} wpt={wpt} cap={kc.shape[0]} seed={seed}")
+    qd, kd, vd = q.cuda(), kc.cuda(), vc.cuda()
+    k_sum = kd.view(torch.int16).sum(dtype=torch.int64).item()
+    o, lse = jl.decode(qd, kd, vd, L, w0=w0, w_pretrained=wpt, rope_base=base, q_to_kv=q_to_kv)
+    torch.cuda.synchronize()
+    assert kd.view(torch.int16).sum(dtype=torch.int64).item() == k_sum      # cache untouched
+    oo, ll = oracle.decode(q.double().numpy(), kc[:L].double().numpy(), vc[:L].double().numpy(), L,
+                           w0=w0, w_pretrained=wpt, rope_base=base, q_to_kv=q_to_kv)
+    og, lg = o.float().cpu().numpy(), lse.cpu().numpy()
+    e_o, e_l = max_abs(og, oo), lse_rel_err(lg, ll)
+    _say(f"[decode] L={L}: max|do|={e_o:.3e} lse rel={e_l:.3e}")
+    assert e_o <= BF16_O_ATOL
+    assert e_l <= BF16_LSE_RTOL
+    return og, lg
+
+
+@pytest.mark.parametrize("L", W.DECODE_LENGTHS)
+def test_qwen3_8b_decode_lengths(L):
+    """32 q / 8 kv heads, d = 128, w0 = 4096, w_pretrained = 32768, at 16K,
+    32K, 32769 (G 1 -> 2), 64K, 65537 (G 2 -> 3) and 128K (G = 4)."""
+    jl, torch = gpu_or_skip()
+    _decode_case(jl, torch, L, 32, 8, 4096, 32768, 1e6, seed=L)
+
+
+@pytest.mark.parametrize("L,Hq,Hkv,w0,wpt", [
+    (1, 4, 2, 4, 8),
+    (63, 4, 2, 10, 16),          # one partial sub-chunk, G = 4
+    (65, 8, 8, 64, 16),          # sub-chunk edge, G = 5
+    (300, 8, 2, 0, 100),         # w0 = 0: every key remote
+    (300, 8, 2, 500, 100),       # w0 >= L: every key local
+    (1000, 16, 2, 100, 2000),    # G = 1
+    (4097, 2, 2, 1, 1024),       # w0 = 1
+    (5000, 32, 8, 333, 1200),    # G = 5, ragged
+])
+def test_small_decode_cases(L, Hq, Hkv, w0, wpt):
+    jl, torch = gpu_or_skip()
+    _decode_case(jl, torch, L, Hq, Hkv, w0, wpt, 1e4, seed=L + 7, L_cap=L + 37)
+
+
+def test_head_map():
+    jl, torch = gpu_or_skip()
+    _decode_case(jl, torch, 700, 4, 2, 50, 256, 1e4, seed=3, q_to_kv=[1, 0, 0, 1])
+
+
+def test_decode_equals_last_prefill_row():
+    """decode(L) on the cache of base-rotated keys equals the last row of the
+    bifocal prefill at L (both from the library)."""
+    jl, torch = gpu_or_skip()
+    L, Hq, Hkv, w0, wpt, base = 1500, 8, 2, 200, 400, 1e6   # G = 4
+    g = torch.Generator("cpu").manual_seed(11)
+    q = torch.randn((L, Hq, 128), generator=g).bfloat16()
+    k = torch.randn((L, Hkv, 128), generator=g).bfloat16()
+    v = torch.randn((L, Hkv, 128), generator=g).bfloat16()
+    o_p, lse_p = jl.prefill(q.cuda(), k.cuda(), v.cuda(), w0=w0, w_pretrained=wpt, rope_base=base)
+    # cache and query rotated at absolute positions (fp64 on the host, rounded to bf16)
+    th = oracle.rope_theta(128, base)
+    kc = torch.from_numpy(oracle.rope(k.double().numpy(), np.arange(L), th)).bfloat16()
+    qb = torch.from_numpy(oracle.rope(q[L - 1:L].double().numpy(), np.array([L - 1]), th)[0]).bfloat16()
+    o_d, lse_d = jl.decode(qb.cuda(), kc.cuda(), v.cuda(), L, w0=w0, w_pretrained=wpt, rope_base=base)
+    torch.cuda.synchronize()
+    assert max_abs(o_d.float().cpu().numpy(), o_p[L - 1].float().cpu().numpy()) <= 2 * BF16_O_ATOL
+    assert lse_rel_err(lse_d.cpu().numpy(), lse_p[:, L - 1].cpu().numpy()) <= 2 * BF16_LSE_RTOL
+
+
+def test_empty_cache_is_noop():
+    jl, torch = gpu_or_skip()
+    q = torch.zeros((4, 128), dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros((8, 2, 128), dtype=torch.bfloat16, device="cuda")
+    o, lse = jl.decode(q, kc, kc, 0, w0=4, w_pretrained=8, rope_base=1e4)
+    torch.cuda.synchronize()
+    assert o.shape == (4, 128)

@@ -1,0 +1,195 @@
+"""Parity of the HIP bifocal prefill with the fp64 oracle.
+
+fp32 path: o max-abs <= 1e-5.  bf16 path: o max-abs <= 2e-2 and LSE relative
+error <= 1e-3.  Small cases compare every row; the Qwen3-shaped sizes
+compare sampled rows (first rows, both sides of the window edge, group phase
+rows, the last row and seeded random rows) for all heads."""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from jl_testutil import (BF16_LSE_RTOL, BF16_O_ATOL, FP32_LSE_ATOL, FP32_O_ATOL, gpu_or_skip,
+                         lse_rel_err, max_abs)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _run(jl, torch, q, k, v, **kw):
+    o, lse = jl.prefill(q.cuda(), k.cuda(), v.cuda(), **kw)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def _inputs(torch, T, Hq, Hkv, d, dtype, seed):
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = torch.randn((T, Hq, d), generator=g)
+    k = torch.randn((T, Hkv, d), generator=g)
+    v = torch.randn((T, Hkv, d), generator=g)
+    if dtype == "bf16":
+        q, k, v = q.bfloat16(), k.bfloat16(), v.bfloat16()
+    return q, k, v
+
+
+def _np(t):
+    return t.double().numpy()
+
+
+def _check_full(jl, torch, L, Hq, Hkv, d, dtype, w0, wpt, base, seed, q_to_kv=None, cu=None):
+    _say(f"[prefill] L={L} Hq={Hq} Hkv={Hkv} d={d} {dtype} w0={w0} wpt={wpt} cu={cu} seed={seed}")
+    T = L if cu is None else cu[-1]
+    q, k, v = _inputs(torch, T, Hq, Hkv, d, dtype, seed)
+    o, lse = _run(jl, torch, q, k, v, w0=w0, w_pretrained=wpt, rope_base=base, q_to_kv=q_to_kv,
+                  cu_seqlens=cu)
+    cus = [0, T] if cu is None else cu
+    for b in range(len(cus) - 1):
+        s0, s1 = cus[b], cus[b + 1]
+        if s1 == s0:
+            continue
+        oo, ll = oracle.prefill(_np(q[s0:s1]), _np(k[s0:s1]), _np(v[s0:s1]), w0=w0, w_pretrained=wpt,
+                                rope_base=base, q_to_kv=q_to_kv)
+        if dtype == "fp32":
+            assert max_abs(o[s0:s1], oo) <= FP32_O_ATOL, (b, max_abs(o[s0:s1], oo))
+            assert max_abs(lse[:, s0:s1], ll) <= FP32_LSE_ATOL
+        else:
+            assert max_abs(o[s0:s1], oo) <= BF16_O_ATOL, (b, max_abs(o[s0:s1], oo))
+            assert lse_rel_err(lse[:, s0:s1], ll) <= BF16_LSE_RTOL
+
+
+def test_tiny_fp32_config():
+    """1 q / 1 kv head, d = 64, L = 256, w_pretrained = 64 (G = 4), w0 = 16,
+    base 1e4: every row against the oracle."""
+    jl, torch = gpu_or_skip()
+    cfg = W.TINY
+    q, k, v = W.make_prefill_inputs(cfg)
+    _say("[prefill] tiny fp32 config")
+    o, lse = _run(jl, torch, q, k, v, w0=cfg.w0, w_pretrained=cfg.w_pretrained, rope_base=cfg.rope_base)
+    oo, ll = oracle.prefill(_np(q), _np(k), _np(v), w0=cfg.w0, w_pretrained=cfg.w_pretrained,
+                            rope_base=cfg.rope_base)
+    assert max_abs(o, oo) <= FP32_O_ATOL
+    assert max_abs(lse, ll) <= FP32_LSE_ATOL
+
+
+@pytest.mark.parametrize("L,Hq,Hkv,d,w0,wpt", [
+    (300, 4, 2, 128, 37, 80),      # G = 4, ragged
+    (517, 2, 1, 64, 100, 200),     # G = 3
+    (200, 2, 2, 64, 0, 60),        # w0 = 0: all remote
+    (200, 2, 2, 64, 250, 60),      # w0 >= L: all local
+    (180, 2, 1, 128, 30, 400),     # G = 1
+    (1, 2, 1, 64, 4, 8),           # single token
+])
+def test_fp32_cases(L, Hq, Hkv, d, w0, wpt):
+    jl, torch = gpu_or_skip()
+    _check_full(jl, torch, L, Hq, Hkv, d, "fp32", w0, wpt, 10000.0, seed=L)
+
+
+def test_fp32_varlen_and_head_map():
+    jl, torch = gpu_or_skip()
+    _check_full(jl, torch, None, 3, 2, 64, "fp32", 20, 50, 10000.0, seed=5, q_to_kv=[1, 0, 1],
+                cu=[0, 130, 131, 131, 300])
+
+
+@pytest.mark.parametrize("L,Hq,Hkv,w0,wpt", [
+    (1000, 4, 2, 200, 300),        # G = 4, several q tiles, ragged tail
+    (777, 2, 1, 64, 200),          # G = 4, w0 = one key tile
+    (1500, 2, 2, 1, 700),          # G = 3, w0 = 1 (only the diagonal is local)
+    (640, 4, 1, 0, 160),           # w0 = 0
+    (600, 2, 1, 700, 100),         # w0 >= L
+    (900, 4, 2, 100, 5000),        # G = 1
+    (129, 2, 1, 33, 40),           # tile edges
+    (64, 2, 1, 10, 16),
+    (2, 2, 1, 1, 1),
+])
+def test_bf16_full_rows(L, Hq, Hkv, w0, wpt):
+    jl, torch = gpu_or_skip()
+    _check_full(jl, torch, L, Hq, Hkv, 128, "bf16", w0, wpt, 1e6, seed=L + 1)
+
+
+def test_bf16_varlen_small():
+    jl, torch = gpu_or_skip()
+    _check_full(jl, torch, None, 4, 2, 128, "bf16", 96, 200, 1e6, seed=9,
+                cu=[0, 700, 701, 701, 1330, 1600])
+
+
+def test_bf16_empty_is_noop():
+    jl, torch = gpu_or_skip()
+    q = torch.empty((0, 2, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty((0, 1, 128), dtype=torch.bfloat16, device="cuda")
+    o, lse = jl.prefill(q, k, k, w0=4, w_pretrained=8, rope_base=1e4)
+    torch.cuda.synchronize()
+    assert o.shape == (0, 2, 128) and lse.shape == (2, 0)
+
+
+def _check_sampled(jl, torch, cfg, n_random, seqs_to_check=None):
+    q, k, v = W.make_prefill_inputs(cfg)
+    cu = W.cu_seqlens_of(cfg.seqlens)
+    _say(f"[prefill] {cfg.name} T={cfg.total_tokens} w0={cfg.w0}")
+    o, lse = jl.prefill(q.cuda(), k.cuda(), v.cuda(), w0=cfg.w0, w_pretrained=cfg.w_pretrained,
+                        rope_base=cfg.rope_base, cu_seqlens=cu if len(cfg.seqlens) > 1 else None)
+    torch.cuda.synchronize()
+    worst_o, worst_l = 0.0, 0.0
+    for b in (range(len(cfg.seqlens)) if seqs_to_check is None else seqs_to_check):
+        s0, L = cu[b], cfg.seqlens[b]
+        G = oracle.group_size(L, cfg.w_pretrained)
+        rows = W.sample_rows(L, cfg.w0, G, n_random, seed=100 + b)
+        oo, ll = _oracle_rows(q, k, v, s0, L, cfg, rows)
+        idx = [s0 + r for r in rows]
+        og = o[idx].float().cpu().numpy()
+        lg = lse[:, idx].cpu().numpy()
+        worst_o = max(worst_o, max_abs(og, oo))
+        worst_l = max(worst_l, lse_rel_err(lg, ll))
+    _say(f"[prefill] {cfg.name}: max|do|={worst_o:.3e} lse rel={worst_l:.3e}")
+    assert worst_o <= BF16_O_ATOL
+    assert worst_l <= BF16_LSE_RTOL
+
+
+def _oracle_rows(q, k, v, s0, L, cfg, rows):
+    # The sequence's G comes from its full length L, so the oracle gets arrays
+    # of length L.  It reads q only at the sampled rows: the q array is a
+    # lazily zero-filled buffer with just those rows written.
+    qn = np.zeros((L,) + tuple(q.shape[1:]), dtype=np.float64)
+    r = torch_index(rows)
+    qn[rows] = q[s0 + r].double().numpy()
+    kmax = max(rows) + 1
+    kn = np.zeros((L,) + tuple(k.shape[1:]), dtype=np.float64)
+    vn = np.zeros_like(kn)
+    kn[:kmax] = _np(k[s0:s0 + kmax])
+    vn[:kmax] = _np(v[s0:s0 + kmax])
+    return oracle.prefill(qn, kn, vn, w0=cfg.w0, w_pretrained=cfg.w_pretrained,
+                          rope_base=cfg.rope_base, rows=rows)
+
+
+def torch_index(rows):
+    import torch
+    return torch.tensor(rows, dtype=torch.long)
+
+
+def test_qwen3_1p7b_32k_g1():
+    """16 q / 8 kv heads, L = 32768 = w_pretrained: G = 1, plain causal RoPE."""
+    jl, torch = gpu_or_skip()
+    _check_sampled(jl, torch, W.QWEN3_1P7B_32K, n_random=24)
+
+
+def test_qwen3_1p7b_64k_g2():
+    jl, torch = gpu_or_skip()
+    _check_sampled(jl, torch, W.QWEN3_1P7B_64K, n_random=16)
+
+
+def test_qwen3_8b_128k_g4():
+    jl, torch = gpu_or_skip()
+    _check_sampled(jl, torch, W.QWEN3_8B_128K, n_random=8)
+
+
+def test_qwen3_4b_varlen():
+    jl, torch = gpu_or_skip()
+    cfg = W.varlen_4b(1024)
+    # check the shortest and the longest sequence
+    lens = list(cfg.seqlens)
+    _check_sampled(jl, torch, cfg, n_random=4, seqs_to_check=[lens.index(min(lens)), lens.index(max(lens))])
