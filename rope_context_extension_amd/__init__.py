@@ -39,6 +39,10 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is not built; run python -m rope_context_extension_amd.build")
+        # torch ships its own HIP runtime under the same SONAME as the system
+        # one; loading torch first makes the library bind to the runtime that
+        # owns torch's device memory and streams.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         c = ctypes
         L.jl_group_size.restype = c.c_int64

@@ -117,6 +117,8 @@ JL_EXPORT int jl_bifocal_prefill(const void* q, const void* k, const void* v, vo
     pl.seqs.G[b] = (int32_t)jl_group_size_i64(s1 - s0, w_pretrained);
     if (pl.seqs.G[b] > 1) pl.seqs.any_remote = 1;
     if (pl.seqs.len[b] > pl.max_len) pl.max_len = pl.seqs.len[b];
+    pl.seqs.vstart[b] = pl.seqs.vt_cols;
+    pl.seqs.vt_cols += (pl.seqs.len[b] + 63) / 64 * 64;
   }
   if (cu_seqlens && cu_seqlens[num_seqs] != total_tokens)
     return fail(JL_EINVAL, "cu_seqlens[num_seqs] != total_tokens");
@@ -130,7 +132,8 @@ JL_EXPORT int jl_bifocal_prefill(const void* q, const void* k, const void* v, vo
   pl.off_qr = off; if (pl.seqs.any_remote) off += align256(nq);
   pl.off_kb = off; off += align256(nk);
   pl.off_kr = off; if (pl.seqs.any_remote) off += align256(nk);
-  pl.off_vt = off; if (dtype == JL_BF16) off += align256(nk);
+  pl.off_vt = off;
+  if (dtype == JL_BF16) off += align256((size_t)num_kv_heads * head_dim * pl.seqs.vt_cols * el);
   // split-operand residuals of the first JL_LO_ROWS positions (bf16 path)
   const size_t lrows = (size_t)num_seqs * JL_LO_ROWS;
   const size_t nqlo = (size_t)num_q_heads * lrows * head_dim * el;
@@ -170,6 +173,10 @@ JL_EXPORT int jl_bifocal_prefill(const void* q, const void* k, const void* v, vo
     ws.qr_lo = wsb + pl.off_lo + nqlo;
     ws.kb_lo = wsb + pl.off_lo + 2 * nqlo;
     ws.kr_lo = wsb + pl.off_lo + 2 * nqlo + nklo;
+    if (!pl.seqs.any_remote) {   // remote grid == base grid: share the residuals too
+      ws.qr_lo = ws.qb_lo;
+      ws.kr_lo = ws.kb_lo;
+    }
   }
   ws.t_pad = pl.t_pad;
 
@@ -177,19 +184,19 @@ JL_EXPORT int jl_bifocal_prefill(const void* q, const void* k, const void* v, vo
                                         head_dim, pl.seqs, fr, st);
   if (e != hipSuccess) return hip_fail(e, "rope pre-pass launch");
   if (dtype == JL_BF16) {
-    e = jl_launch_transpose_v(v, ws, total_tokens, num_kv_heads, st);
+    e = jl_launch_transpose_v(v, ws, pl.seqs, num_kv_heads, st);
     if (e != hipSuccess) return hip_fail(e, "v transpose launch");
-    if (g_ev_before) hipEventRecord(g_ev_before, st);
+    if (g_ev_before) (void)hipEventRecord(g_ev_before, st);
     e = jl_launch_prefill_bf16(ws, o, lse, total_tokens, num_q_heads, num_kv_heads, hm, pl.seqs, w0,
                                scale, pl.max_len, st);
     if (e != hipSuccess) return hip_fail(e, "bf16 prefill launch");
-    if (g_ev_after) hipEventRecord(g_ev_after, st);
+    if (g_ev_after) (void)hipEventRecord(g_ev_after, st);
   } else {
-    if (g_ev_before) hipEventRecord(g_ev_before, st);
+    if (g_ev_before) (void)hipEventRecord(g_ev_before, st);
     e = jl_launch_prefill_fp32(ws, (const float*)v, (float*)o, lse, total_tokens, num_q_heads,
                                num_kv_heads, head_dim, hm, pl.seqs, w0, scale, pl.max_len, st);
     if (e != hipSuccess) return hip_fail(e, "fp32 prefill launch");
-    if (g_ev_after) hipEventRecord(g_ev_after, st);
+    if (g_ev_after) (void)hipEventRecord(g_ev_after, st);
   }
   return JL_OK;
 }
@@ -236,11 +243,11 @@ JL_EXPORT int jl_bifocal_decode(const void* q, const void* k_cache, const void* 
   build_freqs(&fr, head_dim, rope_base);
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
   const int32_t G = (int32_t)jl_group_size_i64(L, w_pretrained);
-  if (g_ev_before) hipEventRecord(g_ev_before, (hipStream_t)hip_stream);
+  if (g_ev_before) (void)hipEventRecord(g_ev_before, (hipStream_t)hip_stream);
   hipError_t e = jl_launch_decode_bf16(q, k_cache, v_cache, L, o, lse, num_q_heads, num_kv_heads, hm, w0,
                                        G, scale, fr, workspace, (hipStream_t)hip_stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
-  if (g_ev_after) hipEventRecord(g_ev_after, (hipStream_t)hip_stream);
+  if (g_ev_after) (void)hipEventRecord(g_ev_after, (hipStream_t)hip_stream);
   return JL_OK;
 }
 

@@ -254,12 +254,18 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
   }
 }
 
-// Merge of the split-K partials: one workgroup per head slot.
-__global__ void __launch_bounds__(128) decode_reduce_kernel(const float* __restrict__ part, int nwg,
+// Merge of the split-K partials through their LogSumExp statistics.
+// Workgroup (slot, quarter): 32 channels of one head slot; its 256 threads
+// split the partial records 8 ways and the 32 channels 32 ways.
+__global__ void __launch_bounds__(256) decode_reduce_kernel(const float* __restrict__ part, int nwg,
                                                             int Hq, int NG, JlHeadMap hm,
                                                             __bf16* __restrict__ o,
                                                             float* __restrict__ lse) {
-  const int slot = blockIdx.x, d = threadIdx.x;
+  __shared__ float red_m[256];
+  __shared__ float red_l[8], red_a[8][32];
+  const int slot = blockIdx.x, quarter = blockIdx.y, tid = threadIdx.x;
+  const int c = tid & 31, grp = tid >> 5;
+  const int d = quarter * 32 + c;
   // head of this slot (same ordering rule as the split kernel)
   const int kvh = slot / NG, n = slot % NG;
   int cnt = 0, head = 0;
@@ -269,16 +275,34 @@ __global__ void __launch_bounds__(128) decode_reduce_kernel(const float* __restr
       ++cnt;
     }
   float M = -INFINITY;
-  for (int w = 0; w < nwg; ++w) M = fmaxf(M, part[((int64_t)w * Hq + slot) * PS]);
+  for (int w = tid; w < nwg; w += 256) M = fmaxf(M, part[((int64_t)w * Hq + slot) * PS]);
+  red_m[tid] = M;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red_m[tid] = fmaxf(red_m[tid], red_m[tid + s]);
+    __syncthreads();
+  }
+  M = red_m[0];
   float l = 0.f, acc = 0.f;
-  for (int w = 0; w < nwg; ++w) {
+  for (int w = grp; w < nwg; w += 8) {
     const float* r = part + ((int64_t)w * Hq + slot) * PS;
     const float e = __builtin_amdgcn_exp2f(r[0] - M);
     l += e * r[1];
     acc += e * r[4 + d];
   }
-  o[head * D + d] = (__bf16)(acc / l);
-  if (lse != nullptr && d == 0) lse[head] = (M + __log2f(l)) * LN2;
+  red_a[grp][c] = acc;
+  if (c == 0) red_l[grp] = l;
+  __syncthreads();
+  if (grp == 0) {
+    float A = 0.f, Lt = 0.f;
+#pragma unroll
+    for (int g2 = 0; g2 < 8; ++g2) {
+      A += red_a[g2][c];
+      Lt += red_l[g2];
+    }
+    o[head * D + d] = (__bf16)(A / Lt);
+    if (lse != nullptr && quarter == 0 && c == 0) lse[head] = (M + __log2f(Lt)) * LN2;
+  }
 }
 
 }  // namespace
@@ -322,6 +346,6 @@ hipError_t jl_launch_decode_bf16(const void* q, const void* k_cache, const void*
 #undef JL_DEC
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  decode_reduce_kernel<<<Hq, 128, 0, st>>>(part, nwg, Hq, NG, hm, (__bf16*)o, lse);
+  decode_reduce_kernel<<<dim3(Hq, 4), 256, 0, st>>>(part, nwg, Hq, NG, hm, (__bf16*)o, lse);
   return hipGetLastError();
 }

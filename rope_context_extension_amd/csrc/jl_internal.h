@@ -19,6 +19,19 @@ struct JlSeqs {
   int32_t start[JL_MAX_SEQS];  // first packed token of the sequence
   int32_t len[JL_MAX_SEQS];    // its length L_b
   int32_t G[JL_MAX_SEQS];      // its group size G_b
+  int32_t vstart[JL_MAX_SEQS]; // first V^T column of the sequence (multiple of 64)
+  int32_t vt_cols;             // V^T row length: sum of lengths rounded up to 64
+};
+
+// Work order of the bf16 prefill kernel (q tiles >= 1 of every sequence):
+// sequences sorted by tile count c[] (descending), perm[] maps back.
+struct JlSched {
+  int32_t nlev;
+  int32_t total_units;
+  int32_t xcd_heads;           // Hq / 8 when Hq % 8 == 0, else 0
+  int32_t c[JL_MAX_SEQS];
+  int32_t perm[JL_MAX_SEQS];
+  uint8_t head_order[JL_MAX_HEADS];   // q heads grouped by kv head
 };
 
 // RoPE frequencies theta_m / (2 pi) in unsigned 0.64 fixed point (see
@@ -34,7 +47,9 @@ struct JlHeadMap {
 // Workspace of the prefill path: rotated operands, head-major.
 //   qb, qr   [Hq][T_pad][d]   q rotated at p and at f(p)
 //   kb, kr   [Hkv][T_pad][d]  k rotated at p and at f(p)
-//   vt       [Hkv][d][T_pad]  v transposed (bf16 path only)
+//   vt       [Hkv][d][vt_cols] v transposed (bf16 path only); sequence b
+//            starts at column vstart[b], a multiple of 64, and its columns
+//            past L_b up to the next multiple of 64 are zero
 // Rows T .. T_pad-1 are zero.  qr / kr alias qb / kb when no sequence has
 // G > 1.
 //   qb_lo, qr_lo [Hq][nseq * JL_LO_ROWS][d], kb_lo, kr_lo [Hkv][nseq * JL_LO_ROWS][d]
@@ -63,7 +78,7 @@ int64_t jl_prefill_t_pad(int64_t total_tokens);
 hipError_t jl_launch_rope_prepass(const void* q, const void* k, const JlPrefillWs& ws, int elem_bytes,
                                   int64_t total_tokens, int32_t Hq, int32_t Hkv, int32_t d,
                                   const JlSeqs& seqs, const JlFreqs& fr, hipStream_t st);
-hipError_t jl_launch_transpose_v(const void* v, const JlPrefillWs& ws, int64_t total_tokens,
+hipError_t jl_launch_transpose_v(const void* v, const JlPrefillWs& ws, const JlSeqs& seqs,
                                  int32_t Hkv, hipStream_t st);
 
 hipError_t jl_launch_prefill_fp32(const JlPrefillWs& ws, const float* v, float* o, float* lse,

@@ -119,21 +119,25 @@ __global__ void __launch_bounds__(256) rope_prepass_kernel(
   }
 }
 
-// v [T][Hkv][128] bf16 -> vt [Hkv][128][t_pad], 64 tokens per block through LDS.
+// v [T][Hkv][128] bf16 -> vt [Hkv][128][vt_cols], 64 tokens of one sequence
+// per block through LDS; columns past the sequence end are zero.
 __global__ void __launch_bounds__(256) transpose_v_kernel(const __bf16* __restrict__ v,
-                                                          __bf16* __restrict__ vt, int64_t total,
-                                                          int64_t t_pad, int Hkv) {
+                                                          __bf16* __restrict__ vt, int64_t vt_cols,
+                                                          int Hkv, JlSeqs seqs) {
   constexpr int D = 128, TB = 64, P = D + 8;
   __shared__ __bf16 tile[TB * P];
-  const int h = blockIdx.y;
-  const int64_t t0 = (int64_t)blockIdx.x * TB;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int p0 = blockIdx.x * TB;
+  const int L = seqs.len[b];
+  if (p0 >= L) return;
+  const int64_t s0 = seqs.start[b];
   const int tid = threadIdx.x;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int c = it * 256 + tid;
     const int tok = c >> 4, col = (c & 15) * 8;
     uint4 val = make_uint4(0, 0, 0, 0);
-    if (t0 + tok < total) val = *(const uint4*)(v + ((t0 + tok) * Hkv + h) * D + col);
+    if (p0 + tok < L) val = *(const uint4*)(v + ((s0 + p0 + tok) * Hkv + h) * D + col);
     *(uint4*)(tile + tok * P + col) = val;
   }
   __syncthreads();
@@ -144,7 +148,7 @@ __global__ void __launch_bounds__(256) transpose_v_kernel(const __bf16* __restri
     __bf16 out[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) out[e] = tile[(tk + e) * P + dd];
-    *(uint4*)(vt + ((int64_t)h * D + dd) * t_pad + t0 + tk) = *(const uint4*)out;
+    *(uint4*)(vt + ((int64_t)h * D + dd) * vt_cols + seqs.vstart[b] + p0 + tk) = *(const uint4*)out;
   }
 }
 
@@ -176,10 +180,12 @@ hipError_t jl_launch_rope_prepass(const void* q, const void* k, const JlPrefillW
   return hipGetLastError();
 }
 
-hipError_t jl_launch_transpose_v(const void* v, const JlPrefillWs& ws, int64_t total_tokens,
+hipError_t jl_launch_transpose_v(const void* v, const JlPrefillWs& ws, const JlSeqs& seqs,
                                  int32_t Hkv, hipStream_t st) {
-  dim3 grid((unsigned)(ws.t_pad / 64), (unsigned)Hkv);
-  transpose_v_kernel<<<grid, 256, 0, st>>>((const __bf16*)v, (__bf16*)ws.vt, total_tokens, ws.t_pad,
-                                           Hkv);
+  int32_t max_len = 0;
+  for (int b = 0; b < seqs.nseq; ++b) max_len = seqs.len[b] > max_len ? seqs.len[b] : max_len;
+  if (max_len == 0) return hipSuccess;
+  dim3 grid((unsigned)((max_len + 63) / 64), (unsigned)Hkv, (unsigned)seqs.nseq);
+  transpose_v_kernel<<<grid, 256, 0, st>>>((const __bf16*)v, (__bf16*)ws.vt, seqs.vt_cols, Hkv, seqs);
   return hipGetLastError();
 }
