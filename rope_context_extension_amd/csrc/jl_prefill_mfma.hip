@@ -55,8 +55,10 @@ constexpr int KP = 272;                 // LDS pitch of a K row (256 B + 16 B pa
 constexpr int VP = 144;                 // LDS pitch of a V^T row (128 B + 16 B pad)
 constexpr int KT_BYTES = BK * KP;       // 17408
 constexpr int VT_BYTES = D * VP;        // 18432
-constexpr int KT_INSTR = KT_BYTES / 1024;          // 17 KiB pieces
-constexpr int VT_INSTR = VT_BYTES / 1024;          // 18 KiB pieces
+constexpr int KT_PIECES = KT_BYTES / 1024;         // 17 KiB pieces of K
+constexpr int PIECES = (KT_BYTES + VT_BYTES) / 1024; // 35 KiB pieces per tile
+constexpr int PIECES_PER_WAVE = (PIECES + 3) / 4;   // 9
+constexpr int NBUF = 3;                             // tile buffers in LDS
 constexpr int BUF_BYTES = KT_BYTES + VT_BYTES;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -76,26 +78,30 @@ __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 // [n KiB, n KiB + 1 KiB) and each lane fetches the global chunk that belongs
 // at its LDS offset.  Lanes that land in a pad re-fetch the row's first
 // chunk (the pad is never read).
+//
+// Every wave issues exactly PIECES_PER_WAVE instructions per tile (a wave
+// that runs out of pieces repeats the last one, rewriting identical bytes), so
+// "all but the newest tile landed" is the same vmcnt value in every wave.
 __device__ inline void issue_tile(char* buf, const char* kg, const char* vg, int64_t vrow_bytes,
                                   int wave, int lane) {
 #pragma unroll
-  for (int n = wave; n < KT_INSTR; n += 4) {
-    const int off = n * 1024 + lane * 16;
-    const int r = off / KP, cb = off - r * KP;
-    const int c = cb < 256 ? cb : 0;
-    __builtin_amdgcn_global_load_lds(kg + r * 256 + c, (lds_void*)(buf + n * 1024), 16, 0, 0);
-  }
-#pragma unroll
-  for (int n = wave; n < VT_INSTR; n += 4) {
-    const int off = n * 1024 + lane * 16;
-    const int r = off / VP, cb = off - r * VP;
-    const int c = cb < 128 ? cb : 0;
-    __builtin_amdgcn_global_load_lds(vg + r * vrow_bytes + c,
-                                     (lds_void*)(buf + KT_BYTES + n * 1024), 16, 0, 0);
+  for (int i = 0; i < PIECES_PER_WAVE; ++i) {
+    const int n = min(wave + 4 * i, PIECES - 1);
+    if (n < KT_PIECES) {
+      const int off = n * 1024 + lane * 16;
+      const int r = off / KP, cb = off - r * KP;
+      const int c = cb < 256 ? cb : 0;
+      __builtin_amdgcn_global_load_lds(kg + r * 256 + c, (lds_void*)(buf + n * 1024), 16, 0, 0);
+    } else {
+      const int off = (n - KT_PIECES) * 1024 + lane * 16;
+      const int r = off / VP, cb = off - r * VP;
+      const int c = cb < 128 ? cb : 0;
+      __builtin_amdgcn_global_load_lds(vg + r * vrow_bytes + c, (lds_void*)(buf + n * 1024), 16, 0, 0);
+    }
   }
 }
 
-__device__ inline void wait_tiles() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ inline void wait_all_tiles() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ inline int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
@@ -152,45 +158,60 @@ __device__ inline void pv_tile(const char* vt, const f32x16* p, int lane, f32x16
 __device__ inline int key_of(int sb, int i, int g) { return sb * 32 + 16 * (i >> 3) + 8 * g + (i & 7); }
 
 struct PassState {
-  float m;      // running max (log2 units), identical in lanes l and l ^ 32
-  float l;      // this lane's partial sum
+  float m;      // stabiliser (log2 units), identical in lanes l and l ^ 32
+  float l;      // this lane's partial sum of exp2(s - m)
 };
 
-// One online-softmax step over the tile held in s (raw scores).  `masked`
-// selects the index masks: KIND 0 keeps dist >= 0, KIND 1 keeps 0 <= dist < w0.
+// The stabiliser m of a row is raised only when the row's score maximum
+// exceeds it by more than RESCALE_LOG2 (log2 units), so most tiles skip the
+// rescale of the accumulators.  Any m works in exact arithmetic (the merge
+// uses lse = m + log2 l); the bound keeps every p = exp2(s - m) <= 2^8.
+constexpr float RESCALE_LOG2 = 8.f;
+
+// Index masks of a tile: KIND 0 keeps dist >= 0 (causal), KIND 1 keeps
+// 0 <= dist < w0 (window).  Masked scores become -inf.
 template <int KIND>
-__device__ inline float softmax_tile(f32x16* s, PassState& st, bool masked, int myrow, int j0,
-                                     int w0, float sl2, int g) {
-  float mx = -INFINITY;
+__device__ inline void mask_tile(f32x16* s, int myrow, int j0, int w0, int g) {
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float x = s[sb][i] * sl2;
-      if (masked) {
-        const int dist = myrow - (j0 + key_of(sb, i, g));
-        const bool keep = KIND == 0 ? dist >= 0 : (dist >= 0 && dist < w0);
-        x = keep ? x : -INFINITY;
-      }
-      s[sb][i] = x;
-      mx = fmaxf(mx, x);
+      const int dist = myrow - (j0 + key_of(sb, i, g));
+      const bool keep = KIND == 0 ? dist >= 0 : (dist >= 0 && dist < w0);
+      s[sb][i] = keep ? s[sb][i] : -INFINITY;
     }
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  const float mn = fmaxf(st.m, mx);
-  const float base = mn == -INFINITY ? 0.f : mn;
-  const float alpha = __builtin_amdgcn_exp2f(st.m - base);
+}
+
+// Online softmax on raw scores s (masked entries -inf): p = exp2(s sl2 - m)
+// written back into s, the row sum accumulated in st.l, and the accumulators
+// rescaled when the stabiliser moves.
+__device__ inline void softmax_tile(f32x16* s, PassState& st, f32x16* o, float sl2) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sb][i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;        // sl2 > 0
+  const bool raise = mx > st.m + RESCALE_LOG2;          // false for an all-masked row
+  if (__any(raise)) {
+    const float mn = raise ? mx : st.m;
+    const float a = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m - mn);
+    st.l *= a;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[db] *= a;
+    st.m = mn;
+  }
+  const float nb = st.m == -INFINITY ? 0.f : -st.m;
   float sum = 0.f;
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float p = __builtin_amdgcn_exp2f(s[sb][i] - base);
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][i], sl2, nb));
       s[sb][i] = p;
       sum += p;
     }
-  st.l = st.l * alpha + sum;
-  st.m = mn;
-  return alpha;
+  st.l += sum;
 }
 
 __device__ inline void load_q(bf16x8* qf, const __bf16* rowp, int g) {
@@ -205,50 +226,100 @@ struct TileSrc {
   const __bf16* klo;   // residual K rows (PRECISE), row p of the sequence
 };
 
-// Per-tile work of a pass for this wave; returns without work when the wave
-// sees no key of the tile (causal) or no key inside the window.
-template <int KIND, bool PRECISE>
-__device__ inline void pass_tile(const char* buf, const TileSrc& src, int j0, const bf16x8* qf,
-                                 const bf16x8* ql, PassState& st, f32x16* o, int iw, int myrow,
-                                 int w0, float sl2, int lane) {
-  if (j0 > iw + 31) return;                                      // all keys after every row
-  if (KIND == 1 && j0 + BK - 1 < iw - w0 + 1) return;            // all keys outside the window
-  const int g = lane >> 5;
-  bool masked = j0 + BK - 1 > iw;                                // some pair has dist < 0
-  if (KIND == 1) masked = masked || (j0 < iw + 31 - w0 + 1);     // some pair has dist >= w0
-  f32x16 s[2];
-  score_tile<PRECISE>(buf, qf, ql, PRECISE ? src.klo + (int64_t)j0 * D : nullptr, lane, s);
-  const float a = softmax_tile<KIND>(s, st, masked, myrow, j0, w0, sl2, g);
-#pragma unroll
-  for (int db = 0; db < 4; ++db) o[db] *= a;
-  pv_tile(buf + KT_BYTES, s, lane, o);
+struct WaveRows {
+  int iw;      // first row of the wave
+  int myrow;   // this lane's row
+  int w0;
+};
+
+// Does this wave have any (causal / window) pair in the key tile at j0?
+template <int KIND>
+__device__ inline bool wave_has_work(int j0, const WaveRows& wr) {
+  if (j0 > wr.iw + 31) return false;
+  if (KIND == 1 && j0 + BK - 1 < wr.iw - wr.w0 + 1) return false;
+  return true;
 }
 
-// A full pass over key tiles [t0, t1) with the double-buffered pipeline.
-// Two iterations per loop trip so that each buffer's LDS reads and the DMA
-// into the other buffer refer to distinct LDS objects.
-template <int KIND, bool PRECISE>
-__device__ inline void run_pass(char* buf0, char* buf1, const TileSrc& src, int t0, int t1,
-                                const bf16x8* qf, const bf16x8* ql, PassState& st, f32x16* o,
-                                int iw, int myrow, int w0, float sl2, int wave, int lane) {
-  __syncthreads();                      // every wave is done with both buffers
+template <int KIND>
+__device__ inline bool wave_needs_mask(int j0, const WaveRows& wr) {
+  bool m = j0 + BK - 1 > wr.iw;                              // some pair has dist < 0
+  if (KIND == 1) m = m || (j0 < wr.iw + 31 - wr.w0 + 1);     // some pair has dist >= w0
+  return m;
+}
+
+// A full flash pass over key tiles [t0, t1).
+// PIPE = false: two LDS buffers; iteration t waits for tile t, issues the DMA
+// of tile t+1 into the other buffer and multiplies tile t.  Latency between
+// MFMA and vector ALU work is hidden by the second wave on each SIMD.
+// PIPE = true (one wave per SIMD): three buffers, and within the wave the
+// MFMAs of S(t+1) = K_{t+1} Q^T are issued before the softmax of tile t, so
+// the vector ALU work overlaps them; iteration t waits for tile t+1, DMAs
+// tile t+2 into the buffer tile t-1 used, then S(t+1), softmax(t), PV(t).
+template <int KIND, bool PRECISE, bool PIPE>
+__device__ inline void run_pass(char* smem, const TileSrc& src, int t0, int t1, const bf16x8* qf,
+                                const bf16x8* ql, PassState& st, f32x16* o, const WaveRows& wr,
+                                float sl2, int wave, int lane) {
+  constexpr int NB = PIPE ? 3 : 2;
+  const int g = lane >> 5;
+  __syncthreads();                      // every wave is done with all buffers
   if (t0 >= t1) return;
-  issue_tile(buf0, src.k + (int64_t)t0 * BK * 256, src.v + (int64_t)t0 * BK * 2, src.vrow_bytes,
-             wave, lane);
-  for (int t = t0; t < t1; t += 2) {
-    wait_tiles();
-    __syncthreads();                    // tile t in buf0; buf1 free
-    if (t + 1 < t1)
-      issue_tile(buf1, src.k + (int64_t)(t + 1) * BK * 256, src.v + (int64_t)(t + 1) * BK * 2,
-                 src.vrow_bytes, wave, lane);
-    pass_tile<KIND, PRECISE>(buf0, src, t * BK, qf, ql, st, o, iw, myrow, w0, sl2, lane);
-    if (t + 1 >= t1) break;
-    wait_tiles();
-    __syncthreads();                    // tile t+1 in buf1; buf0 free
-    if (t + 2 < t1)
-      issue_tile(buf0, src.k + (int64_t)(t + 2) * BK * 256, src.v + (int64_t)(t + 2) * BK * 2,
-                 src.vrow_bytes, wave, lane);
-    pass_tile<KIND, PRECISE>(buf1, src, (t + 1) * BK, qf, ql, st, o, iw, myrow, w0, sl2, lane);
+  auto bufp = [&](int t) { return smem + ((t - t0) % NB) * BUF_BYTES; };
+  auto issue = [&](int t) {
+    issue_tile(bufp(t), src.k + (int64_t)t * BK * 256, src.v + (int64_t)t * BK * 2, src.vrow_bytes,
+               wave, lane);
+  };
+  auto scores = [&](int t, f32x16* s) {
+    score_tile<PRECISE>(bufp(t), qf, ql, PRECISE ? src.klo + (int64_t)t * BK * D : nullptr, lane, s);
+  };
+  auto finish = [&](int t, f32x16* s) {
+    const int j0 = t * BK;
+    if (wave_needs_mask<KIND>(j0, wr)) mask_tile<KIND>(s, wr.myrow, j0, wr.w0, g);
+    softmax_tile(s, st, o, sl2);
+    pv_tile(bufp(t) + KT_BYTES, s, lane, o);
+  };
+  issue(t0);
+  if constexpr (!PIPE) {
+    for (int t = t0; t < t1; ++t) {
+      wait_all_tiles();                 // tile t landed
+      __syncthreads();                  // ... for every wave; tile t-1's buffer is free
+      if (t + 1 < t1) issue(t + 1);
+      if (wave_has_work<KIND>(t * BK, wr)) {
+        f32x16 s[2];
+        scores(t, s);
+        finish(t, s);
+      }
+    }
+  } else {
+    if (t0 + 1 < t1) {
+      issue(t0 + 1);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PIECES_PER_WAVE) : "memory");   // tile t0 landed
+    } else {
+      wait_all_tiles();
+    }
+    __syncthreads();
+    f32x16 sa[2], sb[2];
+    bool wa = wave_has_work<KIND>(t0 * BK, wr), wb = false;
+    if (wa) scores(t0, sa);
+    // two iterations per trip so the two score sets never need a copy
+    for (int t = t0; t < t1; t += 2) {
+      if (t + 1 < t1) {
+        wait_all_tiles();
+        __syncthreads();
+        if (t + 2 < t1) issue(t + 2);
+        wb = wave_has_work<KIND>((t + 1) * BK, wr);
+        if (wb) scores(t + 1, sb);
+      }
+      if (wa) finish(t, sa);
+      if (t + 1 >= t1) break;
+      if (t + 2 < t1) {
+        wait_all_tiles();
+        __syncthreads();
+        if (t + 3 < t1) issue(t + 3);
+        wa = wave_has_work<KIND>((t + 2) * BK, wr);
+        if (wa) scores(t + 2, sa);
+      }
+      if (wb) finish(t + 1, sb);
+    }
   }
 }
 
@@ -267,148 +338,231 @@ __device__ inline void unit_to_tile(const JlSched& sc, int u, int* seq, int* qt)
   *seq = sc.perm[off % (k + 1)];
 }
 
-// PRECISE = true: the first q tile (rows 0 .. 127) of every sequence, with
-// split-operand scores.  PRECISE = false: every other q tile.
-template <bool PRECISE>
-__global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(
-    const __bf16* __restrict__ qb, const __bf16* __restrict__ qr, const __bf16* __restrict__ kb,
-    const __bf16* __restrict__ kr, const __bf16* __restrict__ vt, const __bf16* __restrict__ qb_lo,
-    const __bf16* __restrict__ qr_lo, const __bf16* __restrict__ kb_lo,
-    const __bf16* __restrict__ kr_lo, __bf16* __restrict__ out, float* __restrict__ lse,
-    int64_t total, int64_t t_pad, int Hq, JlHeadMap hm, JlSeqs seqs, JlSched sc, int64_t w0_64,
-    float sl2) {
-  __shared__ __align__(1024) char buf0[BUF_BYTES];
-  __shared__ __align__(1024) char buf1[BUF_BYTES];
-  int h, b, qt;
-  {
-    const int n = blockIdx.x;
-    if (PRECISE) {
-      b = n / Hq;
-      h = sc.head_order[n % Hq];
-      qt = 0;
-    } else if (sc.xcd_heads > 0) {
-      const int s = n & 7, slot = n >> 3;
-      const int u = slot / sc.xcd_heads;
-      h = sc.head_order[s * sc.xcd_heads + slot % sc.xcd_heads];
-      if (u >= sc.total_units) return;
-      unit_to_tile(sc, u, &b, &qt);
-    } else {
-      const int u = n / Hq;
-      h = sc.head_order[n % Hq];
-      unit_to_tile(sc, u, &b, &qt);
-    }
+// Work item of a block: head h, sequence b, q tile qt (rows qt*128 ..).
+// FIRST: q tile 0 of every sequence (split-operand scores).  Otherwise q
+// tiles >= 1 in the heavy-first, XCD-grouped order of JlSched.
+template <bool FIRST>
+__device__ inline bool block_item(const JlSched& sc, int Hq, int* h, int* b, int* qt) {
+  const int n = blockIdx.x;
+  if (FIRST) {
+    *b = n / Hq;
+    *h = sc.head_order[n % Hq];
+    *qt = 0;
+    return true;
   }
-  const int L = seqs.len[b];
-  const int i0 = qt * BQ;
-  if (i0 >= L) return;
+  int u;
+  if (sc.xcd_heads > 0) {
+    const int s = n & 7, slot = n >> 3;
+    u = slot / sc.xcd_heads;
+    *h = sc.head_order[s * sc.xcd_heads + slot % sc.xcd_heads];
+  } else {
+    u = n / Hq;
+    *h = sc.head_order[n % Hq];
+  }
+  if (u >= sc.total_units) return false;
+  unit_to_tile(sc, u, b, qt);
+  return true;
+}
+
+struct PrefillArgs {
+  const __bf16* qb;
+  const __bf16* qr;
+  const __bf16* kb;
+  const __bf16* kr;
+  const __bf16* vt;
+  const __bf16* qb_lo;
+  const __bf16* qr_lo;
+  const __bf16* kb_lo;
+  const __bf16* kr_lo;
+  __bf16* out;        // [T][Hq][128] bf16
+  float* lse;         // [Hq][T] or nullptr
+  float* o2;          // [Hq][T][128] fp32: pass 2 output for the band kernel
+  float* lse2;        // [Hq][T]: pass 2 LogSumExp (log2 units)
+  int64_t total;
+  int64_t t_pad;
+  int64_t w0;
+  int Hq;
+  float sl2;          // softmax scale * log2(e)
+};
+
+struct BlockCtx {
+  int h, b, kvh, L, i0, w0, wave, lane, g;
+  int64_t s0;
+  bool only1, only2;
+  int tiles_end, tw0;
+  WaveRows wr;
+  TileSrc base_src, rem_src;
+  int64_t lrows, lo_base;
+};
+
+__device__ inline bool make_ctx(const PrefillArgs& A, const JlHeadMap& hm, const JlSeqs& seqs,
+                                int h, int b, int qt, BlockCtx* c) {
+  c->h = h;
+  c->b = b;
+  c->L = seqs.len[b];
+  c->i0 = qt * BQ;
+  if (c->i0 >= c->L) return false;
   const int tid = threadIdx.x;
   // wave index in a scalar register: the LDS destination of global_load_lds
   // (M0) must be wave-uniform
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, g = lane >> 5;
-  const int kvh = hm.kv_of[h];
-  const int64_t s0 = seqs.start[b];
-  const int G = seqs.G[b];
-  const int w0 = w0_64 > (int64_t)L ? L : (int)w0_64;
-  const bool only1 = w0 >= L;               // every pair local: pass 1 alone
-  const bool only2 = G == 1 && !only1;       // remote grid == base grid: pass 2 alone
-  const int iw = i0 + wave * 32;             // first row of this wave
-  const int myrow = iw + (lane & 31);
-  const int tiles_end = min((i0 + BQ + BK - 1) / BK, (L + BK - 1) / BK);
-  const int tw0 = (i0 - w0 + 1) > 0 ? (i0 - w0 + 1) / BK : 0;   // first window tile
-
-  const int64_t lrows = (int64_t)seqs.nseq * JL_LO_ROWS;
-  const int64_t lo_base = (int64_t)b * JL_LO_ROWS;
+  c->wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  c->lane = tid & 63;
+  c->g = c->lane >> 5;
+  c->kvh = hm.kv_of[h];
+  c->s0 = seqs.start[b];
+  c->w0 = A.w0 > (int64_t)c->L ? c->L : (int)A.w0;
+  c->only1 = c->w0 >= c->L;                       // every pair local: pass 1 alone
+  c->only2 = seqs.G[b] == 1 && !c->only1;          // remote grid == base grid: pass 2 alone
+  const int iw = c->i0 + c->wave * 32;
+  c->wr = WaveRows{iw, iw + (c->lane & 31), c->w0};
+  c->tiles_end = min((c->i0 + BQ + BK - 1) / BK, (c->L + BK - 1) / BK);
+  c->tw0 = (c->i0 - c->w0 + 1) > 0 ? (c->i0 - c->w0 + 1) / BK : 0;   // first window tile
+  c->lrows = (int64_t)seqs.nseq * JL_LO_ROWS;
+  c->lo_base = (int64_t)b * JL_LO_ROWS;
   const int64_t vcols = seqs.vt_cols;
-  TileSrc base_src{(const char*)(kb + ((int64_t)kvh * t_pad + s0) * D),
-                   (const char*)(vt + (int64_t)kvh * D * vcols + seqs.vstart[b]), vcols * 2,
-                   kb_lo + ((int64_t)kvh * lrows + lo_base) * D};
-  TileSrc rem_src{(const char*)(kr + ((int64_t)kvh * t_pad + s0) * D), base_src.v, vcols * 2,
-                  kr_lo + ((int64_t)kvh * lrows + lo_base) * D};
+  const char* vbase = (const char*)(A.vt + (int64_t)c->kvh * D * vcols + seqs.vstart[b]);
+  c->base_src = TileSrc{(const char*)(A.kb + ((int64_t)c->kvh * A.t_pad + c->s0) * D), vbase, vcols * 2,
+                        A.kb_lo + ((int64_t)c->kvh * c->lrows + c->lo_base) * D};
+  c->rem_src = TileSrc{(const char*)(A.kr + ((int64_t)c->kvh * A.t_pad + c->s0) * D), vbase, vcols * 2,
+                       A.kr_lo + ((int64_t)c->kvh * c->lrows + c->lo_base) * D};
+  return true;
+}
 
-  bf16x8 qf[8];
-  bf16x8 ql[PRECISE ? 8 : 1];
-  f32x16 acc[4], keep[4];
-  PassState st2{-INFINITY, 0.f}, st1{-INFINITY, 0.f}, st3{-INFINITY, 0.f};
-  float out_scale, lse_ref, lse_den;   // final: o = keep * out_scale
+template <bool PRECISE>
+__device__ inline void load_q_pair(bf16x8* qf, bf16x8* ql, const __bf16* q, const __bf16* q_lo,
+                                   const PrefillArgs& A, const BlockCtx& c) {
+  load_q(qf, q + ((int64_t)c.h * A.t_pad + c.s0 + c.wr.myrow) * D, c.g);
+  if constexpr (PRECISE) load_q(ql, q_lo + ((int64_t)c.h * c.lrows + c.lo_base + c.wr.myrow) * D, c.g);
+}
 
-  if (only1) {
-    // ---- pass 1 alone ----
-    load_q(qf, qb + ((int64_t)h * t_pad + s0 + myrow) * D, g);
-    if constexpr (PRECISE) load_q(ql, qb_lo + ((int64_t)h * lrows + lo_base + myrow) * D, g);
+// o (unnormalised, lane holds channels db*32 + 8*(i/4) + 4*g + i%4 of its row)
+// * scale -> bf16 output row.
+__device__ inline void store_out(const PrefillArgs& A, const BlockCtx& c, const f32x16* o, float scale) {
+  __bf16* orow = A.out + ((c.s0 + c.wr.myrow) * A.Hq + c.h) * D;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) keep[db] = f32x16{};
-    run_pass<1, PRECISE>(buf0, buf1, base_src, 0, tiles_end, qf, ql, st1, keep, iw, myrow, w0, sl2,
-                         wave, lane);
-    const float l1 = st1.l + __shfl_xor(st1.l, 32, 64);
-    out_scale = 1.f / l1;
-    lse_ref = st1.m;
-    lse_den = l1;
-  } else {
-    // ---- pass 2: remote q/k, causal ----
-    load_q(qf, qr + ((int64_t)h * t_pad + s0 + myrow) * D, g);
-    if constexpr (PRECISE) load_q(ql, qr_lo + ((int64_t)h * lrows + lo_base + myrow) * D, g);
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int db = 0; db < 4; ++db) keep[db] = f32x16{};
-    run_pass<0, PRECISE>(buf0, buf1, rem_src, 0, tiles_end, qf, ql, st2, keep, iw, myrow, w0, sl2,
-                         wave, lane);
-    const float l2 = st2.l + __shfl_xor(st2.l, 32, 64);
-    if (only2) {
-      out_scale = 1.f / l2;
-      lse_ref = st2.m;
-      lse_den = l2;
-    } else {
-      // ---- pass 1: base q/k, window ----
-      load_q(qf, qb + ((int64_t)h * t_pad + s0 + myrow) * D, g);
-      if constexpr (PRECISE) load_q(ql, qb_lo + ((int64_t)h * lrows + lo_base + myrow) * D, g);
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4 w;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) acc[db] = f32x16{};
-      run_pass<1, PRECISE>(buf0, buf1, base_src, tw0, tiles_end, qf, ql, st1, acc, iw, myrow, w0,
-                           sl2, wave, lane);
-      const float l1 = st1.l + __shfl_xor(st1.l, 32, 64);
-      // fold: M = max(lse_1, lse_2); keep = z1 o1 + z2 o2 (unnormalised: e_k A_k)
-      const float lam1 = l1 > 0.f ? st1.m + __log2f(l1) : -INFINITY;
-      const float lam2 = st2.m + __log2f(l2);
-      const float M = fmaxf(lam1, lam2);
-      const float e1 = l1 > 0.f ? __builtin_amdgcn_exp2f(st1.m - M) : 0.f;
-      const float e2 = __builtin_amdgcn_exp2f(st2.m - M);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) keep[db] = e1 * acc[db] + e2 * keep[db];
-      const float D1 = e1 * l1, D2 = e2 * l2;
-      // ---- pass 3: remote q/k, window ----
-      load_q(qf, qr + ((int64_t)h * t_pad + s0 + myrow) * D, g);
-      if constexpr (PRECISE) load_q(ql, qr_lo + ((int64_t)h * lrows + lo_base + myrow) * D, g);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) acc[db] = f32x16{};
-      run_pass<1, PRECISE>(buf0, buf1, rem_src, tw0, tiles_end, qf, ql, st3, acc, iw, myrow, w0,
-                           sl2, wave, lane);
-      const float l3 = st3.l + __shfl_xor(st3.l, 32, 64);
-      const float e3 = l3 > 0.f ? __builtin_amdgcn_exp2f(st3.m - M) : 0.f;
-      const float D3 = e3 * l3;
-      // far-pair mass z2 - z3; it is exactly 0 for rows without remote pairs
-      // (passes 2 and 3 then run identical arithmetic) and never negative
-      const float Z = D1 + fmaxf(D2 - D3, 0.f);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) keep[db] -= e3 * acc[db];
-      out_scale = 1.f / Z;
-      lse_ref = M;
-      lse_den = Z;
+      for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[db][4 * q4 + e] * scale);
+      *(bf16x4*)(orow + db * 32 + 8 * q4 + 4 * c.g) = w;
     }
-  }
+}
 
-  if (myrow < L) {
-    __bf16* orow = out + ((s0 + myrow) * Hq + h) * D;
+// ---- kernel 1: pass 2 (remote q/k, full causal) -------------------------
+// For G = 1 sequences this is the whole result.  Otherwise it leaves the
+// pass-2 output o2 (normalised, fp32) and lse_2 for the band kernel.
+template <bool FIRST>
+__global__ void __launch_bounds__(NT, 2) prefill_pass2_kernel(PrefillArgs A, JlHeadMap hm, JlSeqs seqs,
+                                                              JlSched sc) {
+  __shared__ __align__(1024) char smem[2 * BUF_BYTES];
+  int h, b, qt;
+  if (!block_item<FIRST>(sc, A.Hq, &h, &b, &qt)) return;
+  BlockCtx c;
+  if (!make_ctx(A, hm, seqs, h, b, qt, &c)) return;
+  if (c.only1) return;                                   // pass 1 alone: band kernel
+  bf16x8 qf[8];
+  bf16x8 ql[FIRST ? 8 : 1];
+  load_q_pair<FIRST>(qf, ql, A.qr, A.qr_lo, A, c);
+  f32x16 o[4];
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        bf16x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(keep[db][4 * q4 + e] * out_scale);
-        *(bf16x4*)(orow + db * 32 + 8 * q4 + 4 * g) = w;
-      }
-    if (lse != nullptr && g == 0) lse[(int64_t)h * total + s0 + myrow] = (lse_ref + __log2f(lse_den)) * LN2;
+  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+  PassState st{-INFINITY, 0.f};
+  run_pass<0, FIRST, false>(smem, c.rem_src, 0, c.tiles_end, qf, ql, st, o, c.wr, A.sl2, c.wave, c.lane);
+  const float l = st.l + __shfl_xor(st.l, 32, 64);
+  if (c.wr.myrow >= c.L) return;
+  const float lam = st.m + __log2f(l);                 // lse_2 in log2 units
+  if (c.only2) {
+    store_out(A, c, o, 1.f / l);
+    if (A.lse != nullptr && c.g == 0) A.lse[(int64_t)c.h * A.total + c.s0 + c.wr.myrow] = lam * LN2;
+    return;
   }
+  float* orow = A.o2 + ((int64_t)c.h * A.total + c.s0 + c.wr.myrow) * D;
+  const float inv = 1.f / l;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      *(float4*)(orow + db * 32 + 8 * q4 + 4 * c.g) =
+          make_float4(o[db][4 * q4] * inv, o[db][4 * q4 + 1] * inv, o[db][4 * q4 + 2] * inv,
+                      o[db][4 * q4 + 3] * inv);
+  if (c.g == 0) A.lse2[(int64_t)c.h * A.total + c.s0 + c.wr.myrow] = lam;
+}
+
+// ---- kernel 2: passes 1 and 3 over the window tiles, and the I-E merge ----
+template <bool FIRST>
+__global__ void __launch_bounds__(NT, 1) prefill_band_kernel(PrefillArgs A, JlHeadMap hm, JlSeqs seqs,
+                                                             JlSched sc) {
+  __shared__ __align__(1024) char smem[3 * BUF_BYTES];
+  int h, b, qt;
+  if (!block_item<FIRST>(sc, A.Hq, &h, &b, &qt)) return;
+  BlockCtx c;
+  if (!make_ctx(A, hm, seqs, h, b, qt, &c)) return;
+  if (c.only2) return;                                   // pass 2 alone: done
+  bf16x8 qf[8];
+  bf16x8 ql[FIRST ? 8 : 1];
+  f32x16 o1[4], o3[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o1[db] = f32x16{};
+  PassState st1{-INFINITY, 0.f};
+  // ---- pass 1: base q/k, window ----
+  load_q_pair<FIRST>(qf, ql, A.qb, A.qb_lo, A, c);
+  run_pass<1, FIRST, true>(smem, c.base_src, c.only1 ? 0 : c.tw0, c.tiles_end, qf, ql, st1, o1, c.wr,
+                           A.sl2, c.wave, c.lane);
+  const float l1 = st1.l + __shfl_xor(st1.l, 32, 64);
+  if (c.only1) {
+    if (c.wr.myrow >= c.L) return;
+    store_out(A, c, o1, 1.f / l1);
+    if (A.lse != nullptr && c.g == 0)
+      A.lse[(int64_t)c.h * A.total + c.s0 + c.wr.myrow] = (st1.m + __log2f(l1)) * LN2;
+    return;
+  }
+  // ---- pass 3: remote q/k, window ----
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o3[db] = f32x16{};
+  PassState st3{-INFINITY, 0.f};
+  load_q_pair<FIRST>(qf, ql, A.qr, A.qr_lo, A, c);
+  run_pass<1, FIRST, true>(smem, c.rem_src, c.tw0, c.tiles_end, qf, ql, st3, o3, c.wr, A.sl2, c.wave,
+                           c.lane);
+  const float l3 = st3.l + __shfl_xor(st3.l, 32, 64);
+  if (c.wr.myrow >= c.L) return;
+  // ---- merge: lse_k = m_k + log2 l_k, M = max(lse_1, lse_2), z_k = 2^(lse_k - M) ----
+  const int64_t ridx = (int64_t)c.h * A.total + c.s0 + c.wr.myrow;
+  const float lam2 = A.lse2[ridx];
+  const float lam1 = l1 > 0.f ? st1.m + __log2f(l1) : -INFINITY;
+  const float lam3 = l3 > 0.f ? st3.m + __log2f(l3) : -INFINITY;
+  const float M = fmaxf(lam1, lam2);
+  const float z1 = __builtin_amdgcn_exp2f(lam1 - M);
+  const float z2 = __builtin_amdgcn_exp2f(lam2 - M);
+  const float z3 = __builtin_amdgcn_exp2f(lam3 - M);
+  // o_k = A_k / l_k, so z_k o_k = 2^(m_k - M) A_k for passes 1 and 3
+  const float c1 = l1 > 0.f ? __builtin_amdgcn_exp2f(st1.m - M) : 0.f;
+  const float c3 = l3 > 0.f ? __builtin_amdgcn_exp2f(st3.m - M) : 0.f;
+  // the remote-only mass z2 - z3 is exactly 0 for rows without remote pairs
+  // (passes 2 and 3 then see identical scores) and never counted negative
+  const float far = z2 - z3;
+  const float Z = z1 + fmaxf(far, 0.f);
+  const float inv = 1.f / Z;
+  const float* o2row = A.o2 + ridx * D;
+  __bf16* orow = A.out + ((c.s0 + c.wr.myrow) * A.Hq + c.h) * D;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = db * 32 + 8 * q4 + 4 * c.g;
+      const float4 v2 = *(const float4*)(o2row + d0);
+      const float o2v[4] = {v2.x, v2.y, v2.z, v2.w};
+      bf16x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * q4 + e;
+        const float far_num = far > 0.f ? z2 * o2v[e] - c3 * o3[db][i] : 0.f;
+        w[e] = (__bf16)((c1 * o1[db][i] + far_num) * inv);
+      }
+      *(bf16x4*)(orow + d0) = w;
+    }
+  if (A.lse != nullptr && c.g == 0) A.lse[ridx] = (M + __log2f(Z)) * LN2;
 }
 
 }  // namespace
@@ -452,21 +606,41 @@ hipError_t jl_launch_prefill_bf16(const JlPrefillWs& ws, void* o, float* lse, in
   (void)max_len;
   JlSched sc;
   jl_build_sched(seqs, hm, Hq, &sc);
-  const float sl2 = scale * LOG2E;
-  if (sc.total_units > 0) {
-    const unsigned nblk = (unsigned)sc.total_units * (unsigned)Hq;   // multiple of 8 when xcd_heads
-    prefill_bf16_kernel<false><<<nblk, NT, 0, st>>>(
-        (const __bf16*)ws.qb, (const __bf16*)ws.qr, (const __bf16*)ws.kb, (const __bf16*)ws.kr,
-        (const __bf16*)ws.vt, (const __bf16*)ws.qb_lo, (const __bf16*)ws.qr_lo,
-        (const __bf16*)ws.kb_lo, (const __bf16*)ws.kr_lo, (__bf16*)o, lse, total_tokens, ws.t_pad,
-        Hq, hm, seqs, sc, w0, sl2);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  PrefillArgs A;
+  A.qb = (const __bf16*)ws.qb;
+  A.qr = (const __bf16*)ws.qr;
+  A.kb = (const __bf16*)ws.kb;
+  A.kr = (const __bf16*)ws.kr;
+  A.vt = (const __bf16*)ws.vt;
+  A.qb_lo = (const __bf16*)ws.qb_lo;
+  A.qr_lo = (const __bf16*)ws.qr_lo;
+  A.kb_lo = (const __bf16*)ws.kb_lo;
+  A.kr_lo = (const __bf16*)ws.kr_lo;
+  A.out = (__bf16*)o;
+  A.lse = lse;
+  A.o2 = (float*)ws.o2;
+  A.lse2 = (float*)ws.lse2;
+  A.total = total_tokens;
+  A.t_pad = ws.t_pad;
+  A.w0 = w0;
+  A.Hq = Hq;
+  A.sl2 = scale * LOG2E;
+  bool any_band = false, any_p2 = false;
+  for (int b = 0; b < seqs.nseq; ++b) {
+    const bool only1 = w0 >= (int64_t)seqs.len[b];
+    const bool only2 = seqs.G[b] == 1 && !only1;
+    any_band |= !only2 && seqs.len[b] > 0;
+    any_p2 |= !only1 && seqs.len[b] > 0;
   }
-  prefill_bf16_kernel<true><<<(unsigned)(seqs.nseq * Hq), NT, 0, st>>>(
-      (const __bf16*)ws.qb, (const __bf16*)ws.qr, (const __bf16*)ws.kb, (const __bf16*)ws.kr,
-      (const __bf16*)ws.vt, (const __bf16*)ws.qb_lo, (const __bf16*)ws.qr_lo,
-      (const __bf16*)ws.kb_lo, (const __bf16*)ws.kr_lo, (__bf16*)o, lse, total_tokens, ws.t_pad, Hq,
-      hm, seqs, sc, w0, sl2);
+  const unsigned nblk = (unsigned)sc.total_units * (unsigned)Hq;   // multiple of 8 when xcd_heads
+  const unsigned nfirst = (unsigned)(seqs.nseq * Hq);
+  if (any_p2) {
+    if (nblk) prefill_pass2_kernel<false><<<nblk, NT, 0, st>>>(A, hm, seqs, sc);
+    prefill_pass2_kernel<true><<<nfirst, NT, 0, st>>>(A, hm, seqs, sc);
+  }
+  if (any_band) {
+    if (nblk) prefill_band_kernel<false><<<nblk, NT, 0, st>>>(A, hm, seqs, sc);
+    prefill_band_kernel<true><<<nfirst, NT, 0, st>>>(A, hm, seqs, sc);
+  }
   return hipGetLastError();
 }
