@@ -70,7 +70,7 @@ struct PrefillPlan {
   JlSeqs seqs;
   int32_t max_len;
   int64_t t_pad;
-  size_t off_qb, off_qr, off_kb, off_kr, off_vt, off_lo, off_o2, off_lse2, total;
+  size_t off_qb, off_qr, off_kb, off_kr, off_vt, off_lo, off_o, off_lse, total;
 };
 
 }  // namespace
@@ -139,10 +139,12 @@ JL_EXPORT int jl_bifocal_prefill(const void* q, const void* k, const void* v, vo
   const size_t nqlo = (size_t)num_q_heads * lrows * head_dim * el;
   const size_t nklo = (size_t)num_kv_heads * lrows * head_dim * el;
   pl.off_lo = off; if (dtype == JL_BF16) off += 2 * align256(nqlo) + 2 * align256(nklo);
-  // pass-2 output handed from the causal kernel to the window (band) kernel
-  const bool band = dtype == JL_BF16 && pl.seqs.any_remote;
-  pl.off_o2 = off; if (band) off += align256((size_t)num_q_heads * total_tokens * head_dim * 4);
-  pl.off_lse2 = off; if (band) off += align256((size_t)num_q_heads * total_tokens * 4);
+  // passes 1 and 2 hand (o_k, lse_k) to the pass-3 launch that merges them
+  const bool merge = dtype == JL_BF16 && pl.seqs.any_remote;
+  const size_t no = align256((size_t)num_q_heads * total_tokens * head_dim * 4);
+  const size_t nl = align256((size_t)num_q_heads * total_tokens * 4);
+  pl.off_o = off; if (merge) off += 2 * no;
+  pl.off_lse = off; if (merge) off += 2 * nl;
   pl.total = total_tokens == 0 ? 0 : off;
 
   if (workspace == nullptr) {
@@ -169,8 +171,14 @@ JL_EXPORT int jl_bifocal_prefill(const void* q, const void* k, const void* v, vo
   ws.kr = pl.seqs.any_remote ? (void*)(wsb + pl.off_kr) : ws.kb;
   ws.vt = dtype == JL_BF16 ? (void*)(wsb + pl.off_vt) : nullptr;
   ws.qb_lo = ws.qr_lo = ws.kb_lo = ws.kr_lo = nullptr;
-  ws.o2 = wsb + pl.off_o2;
-  ws.lse2 = wsb + pl.off_lse2;
+  {
+    const size_t no = align256((size_t)num_q_heads * total_tokens * head_dim * 4);
+    const size_t nl = align256((size_t)num_q_heads * total_tokens * 4);
+    ws.o1 = wsb + pl.off_o;
+    ws.o2 = wsb + pl.off_o + no;
+    ws.lse1 = wsb + pl.off_lse;
+    ws.lse2 = wsb + pl.off_lse + nl;
+  }
   if (dtype == JL_BF16) {
     const size_t lrows = (size_t)num_seqs * JL_LO_ROWS;
     const size_t nqlo = align256((size_t)num_q_heads * lrows * head_dim * el);

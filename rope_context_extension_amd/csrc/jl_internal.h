@@ -65,7 +65,9 @@ struct JlPrefillWs {
   void* qr_lo;
   void* kb_lo;
   void* kr_lo;
-  void* o2;      // [Hq][T][d] fp32: normalised pass-2 output (bf16 path, some G > 1)
+  void* o1;      // [Hq][T][d] fp32: normalised pass-1 output (bf16 path, some G > 1)
+  void* o2;      // [Hq][T][d] fp32: normalised pass-2 output
+  void* lse1;    // [Hq][T] fp32: pass-1 LogSumExp, log2 units
   void* lse2;    // [Hq][T] fp32: pass-2 LogSumExp, log2 units
   int64_t t_pad;
 };

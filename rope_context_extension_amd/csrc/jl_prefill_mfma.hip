@@ -376,7 +376,9 @@ struct PrefillArgs {
   const __bf16* kr_lo;
   __bf16* out;        // [T][Hq][128] bf16
   float* lse;         // [Hq][T] or nullptr
-  float* o2;          // [Hq][T][128] fp32: pass 2 output for the band kernel
+  float* o1;          // [Hq][T][128] fp32: normalised pass 1 output
+  float* o2;          // [Hq][T][128] fp32: normalised pass 2 output
+  float* lse1;        // [Hq][T]: pass 1 LogSumExp (log2 units)
   float* lse2;        // [Hq][T]: pass 2 LogSumExp (log2 units)
   int64_t total;
   int64_t t_pad;
@@ -450,119 +452,96 @@ __device__ inline void store_out(const PrefillArgs& A, const BlockCtx& c, const 
     }
 }
 
-// ---- kernel 1: pass 2 (remote q/k, full causal) -------------------------
-// For G = 1 sequences this is the whole result.  Otherwise it leaves the
-// pass-2 output o2 (normalised, fp32) and lse_2 for the band kernel.
-template <bool FIRST>
-__global__ void __launch_bounds__(NT, 2) prefill_pass2_kernel(PrefillArgs A, JlHeadMap hm, JlSeqs seqs,
-                                                              JlSched sc) {
+// ---- one flash pass per launch --------------------------------------------
+// ROLE 0: pass 2 (remote q/k, causal, all key tiles).  For G = 1 sequences it
+//         is the whole result; otherwise it leaves (o2, lse_2) in workspace.
+// ROLE 1: pass 1 (base q/k, window tiles).  For w0 >= L it is the whole
+//         result; otherwise it leaves (o1, lse_1) in workspace.
+// ROLE 2: pass 3 (remote q/k, window tiles), then the inclusion-exclusion
+//         merge of the three (o_k, lse_k) into the output.
+// o_k are stored normalised in fp32 and lse_k in log2 units.
+template <int ROLE, bool FIRST>
+__global__ void __launch_bounds__(NT, 2) prefill_pass_kernel(PrefillArgs A, JlHeadMap hm, JlSeqs seqs,
+                                                             JlSched sc) {
+  constexpr int KIND = ROLE == 0 ? 0 : 1;
   __shared__ __align__(1024) char smem[2 * BUF_BYTES];
   int h, b, qt;
   if (!block_item<FIRST>(sc, A.Hq, &h, &b, &qt)) return;
   BlockCtx c;
   if (!make_ctx(A, hm, seqs, h, b, qt, &c)) return;
-  if (c.only1) return;                                   // pass 1 alone: band kernel
+  if (ROLE == 0 && c.only1) return;
+  if (ROLE == 1 && c.only2) return;
+  if (ROLE == 2 && (c.only1 || c.only2)) return;
   bf16x8 qf[8];
   bf16x8 ql[FIRST ? 8 : 1];
-  load_q_pair<FIRST>(qf, ql, A.qr, A.qr_lo, A, c);
+  if (ROLE == 1) load_q_pair<FIRST>(qf, ql, A.qb, A.qb_lo, A, c);
+  else load_q_pair<FIRST>(qf, ql, A.qr, A.qr_lo, A, c);
   f32x16 o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16{};
   PassState st{-INFINITY, 0.f};
-  run_pass<0, FIRST, false>(smem, c.rem_src, 0, c.tiles_end, qf, ql, st, o, c.wr, A.sl2, c.wave, c.lane);
+  const int t0 = ROLE == 0 || c.only1 ? 0 : c.tw0;
+  run_pass<KIND, FIRST, false>(smem, ROLE == 1 ? c.base_src : c.rem_src, t0, c.tiles_end, qf, ql, st, o,
+                               c.wr, A.sl2, c.wave, c.lane);
   const float l = st.l + __shfl_xor(st.l, 32, 64);
   if (c.wr.myrow >= c.L) return;
-  const float lam = st.m + __log2f(l);                 // lse_2 in log2 units
-  if (c.only2) {
-    store_out(A, c, o, 1.f / l);
-    if (A.lse != nullptr && c.g == 0) A.lse[(int64_t)c.h * A.total + c.s0 + c.wr.myrow] = lam * LN2;
-    return;
-  }
-  float* orow = A.o2 + ((int64_t)c.h * A.total + c.s0 + c.wr.myrow) * D;
-  const float inv = 1.f / l;
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-      *(float4*)(orow + db * 32 + 8 * q4 + 4 * c.g) =
-          make_float4(o[db][4 * q4] * inv, o[db][4 * q4 + 1] * inv, o[db][4 * q4 + 2] * inv,
-                      o[db][4 * q4 + 3] * inv);
-  if (c.g == 0) A.lse2[(int64_t)c.h * A.total + c.s0 + c.wr.myrow] = lam;
-}
-
-// ---- kernel 2: passes 1 and 3 over the window tiles, and the I-E merge ----
-template <bool FIRST>
-__global__ void __launch_bounds__(NT, 1) prefill_band_kernel(PrefillArgs A, JlHeadMap hm, JlSeqs seqs,
-                                                             JlSched sc) {
-  __shared__ __align__(1024) char smem[3 * BUF_BYTES];
-  int h, b, qt;
-  if (!block_item<FIRST>(sc, A.Hq, &h, &b, &qt)) return;
-  BlockCtx c;
-  if (!make_ctx(A, hm, seqs, h, b, qt, &c)) return;
-  if (c.only2) return;                                   // pass 2 alone: done
-  bf16x8 qf[8];
-  bf16x8 ql[FIRST ? 8 : 1];
-  f32x16 o1[4], o3[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) o1[db] = f32x16{};
-  PassState st1{-INFINITY, 0.f};
-  // ---- pass 1: base q/k, window ----
-  load_q_pair<FIRST>(qf, ql, A.qb, A.qb_lo, A, c);
-  run_pass<1, FIRST, true>(smem, c.base_src, c.only1 ? 0 : c.tw0, c.tiles_end, qf, ql, st1, o1, c.wr,
-                           A.sl2, c.wave, c.lane);
-  const float l1 = st1.l + __shfl_xor(st1.l, 32, 64);
-  if (c.only1) {
-    if (c.wr.myrow >= c.L) return;
-    store_out(A, c, o1, 1.f / l1);
-    if (A.lse != nullptr && c.g == 0)
-      A.lse[(int64_t)c.h * A.total + c.s0 + c.wr.myrow] = (st1.m + __log2f(l1)) * LN2;
-    return;
-  }
-  // ---- pass 3: remote q/k, window ----
-#pragma unroll
-  for (int db = 0; db < 4; ++db) o3[db] = f32x16{};
-  PassState st3{-INFINITY, 0.f};
-  load_q_pair<FIRST>(qf, ql, A.qr, A.qr_lo, A, c);
-  run_pass<1, FIRST, true>(smem, c.rem_src, c.tw0, c.tiles_end, qf, ql, st3, o3, c.wr, A.sl2, c.wave,
-                           c.lane);
-  const float l3 = st3.l + __shfl_xor(st3.l, 32, 64);
-  if (c.wr.myrow >= c.L) return;
-  // ---- merge: lse_k = m_k + log2 l_k, M = max(lse_1, lse_2), z_k = 2^(lse_k - M) ----
   const int64_t ridx = (int64_t)c.h * A.total + c.s0 + c.wr.myrow;
-  const float lam2 = A.lse2[ridx];
-  const float lam1 = l1 > 0.f ? st1.m + __log2f(l1) : -INFINITY;
-  const float lam3 = l3 > 0.f ? st3.m + __log2f(l3) : -INFINITY;
-  const float M = fmaxf(lam1, lam2);
-  const float z1 = __builtin_amdgcn_exp2f(lam1 - M);
-  const float z2 = __builtin_amdgcn_exp2f(lam2 - M);
-  const float z3 = __builtin_amdgcn_exp2f(lam3 - M);
-  // o_k = A_k / l_k, so z_k o_k = 2^(m_k - M) A_k for passes 1 and 3
-  const float c1 = l1 > 0.f ? __builtin_amdgcn_exp2f(st1.m - M) : 0.f;
-  const float c3 = l3 > 0.f ? __builtin_amdgcn_exp2f(st3.m - M) : 0.f;
-  // the remote-only mass z2 - z3 is exactly 0 for rows without remote pairs
-  // (passes 2 and 3 then see identical scores) and never counted negative
-  const float far = z2 - z3;
-  const float Z = z1 + fmaxf(far, 0.f);
-  const float inv = 1.f / Z;
-  const float* o2row = A.o2 + ridx * D;
-  __bf16* orow = A.out + ((c.s0 + c.wr.myrow) * A.Hq + c.h) * D;
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int d0 = db * 32 + 8 * q4 + 4 * c.g;
-      const float4 v2 = *(const float4*)(o2row + d0);
-      const float o2v[4] = {v2.x, v2.y, v2.z, v2.w};
-      bf16x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * q4 + e;
-        const float far_num = far > 0.f ? z2 * o2v[e] - c3 * o3[db][i] : 0.f;
-        w[e] = (__bf16)((c1 * o1[db][i] + far_num) * inv);
-      }
-      *(bf16x4*)(orow + d0) = w;
+  if constexpr (ROLE != 2) {
+    // lse_k in log2 units; an empty pass (w0 = 0 leaves pass 1 without keys)
+    // has lse = -inf and weight 0 in the merge
+    const float lam = l > 0.f ? st.m + __log2f(l) : -INFINITY;
+    if ((ROLE == 0 && c.only2) || (ROLE == 1 && c.only1)) {
+      store_out(A, c, o, 1.f / l);
+      if (A.lse != nullptr && c.g == 0) A.lse[ridx] = lam * LN2;
+      return;
     }
-  if (A.lse != nullptr && c.g == 0) A.lse[ridx] = (M + __log2f(Z)) * LN2;
+    float* orow = (ROLE == 0 ? A.o2 : A.o1) + ridx * D;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *(float4*)(orow + db * 32 + 8 * q4 + 4 * c.g) =
+            make_float4(o[db][4 * q4] * inv, o[db][4 * q4 + 1] * inv, o[db][4 * q4 + 2] * inv,
+                        o[db][4 * q4 + 3] * inv);
+    if (c.g == 0) (ROLE == 0 ? A.lse2 : A.lse1)[ridx] = lam;
+  } else {
+    // ---- merge: M = max(lse_1, lse_2), z_k = 2^(lse_k - M) ----
+    const float lam1 = A.lse1[ridx];
+    const float lam2 = A.lse2[ridx];
+    const float lam3 = l > 0.f ? st.m + __log2f(l) : -INFINITY;
+    const float M = fmaxf(lam1, lam2);
+    const float z1 = __builtin_amdgcn_exp2f(lam1 - M);
+    const float z2 = __builtin_amdgcn_exp2f(lam2 - M);
+    const float z3 = __builtin_amdgcn_exp2f(lam3 - M);
+    const float c3 = l > 0.f ? __builtin_amdgcn_exp2f(st.m - M) : 0.f;   // z3 o3 = c3 * A3
+    // the remote-only mass z2 - z3 is exactly 0 for rows without remote pairs
+    // (passes 2 and 3 then see identical scores) and never counted negative
+    const float far = z2 - z3;
+    const float Z = z1 + fmaxf(far, 0.f);
+    const float inv = 1.f / Z;
+    const float* o1row = A.o1 + ridx * D;
+    const float* o2row = A.o2 + ridx * D;
+    __bf16* orow = A.out + ((c.s0 + c.wr.myrow) * A.Hq + c.h) * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = db * 32 + 8 * q4 + 4 * c.g;
+        const float4 v1 = *(const float4*)(o1row + d0);
+        const float4 v2 = *(const float4*)(o2row + d0);
+        const float o1v[4] = {v1.x, v1.y, v1.z, v1.w};
+        const float o2v[4] = {v2.x, v2.y, v2.z, v2.w};
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float far_num = far > 0.f ? z2 * o2v[e] - c3 * o[db][4 * q4 + e] : 0.f;
+          w[e] = (__bf16)((z1 * o1v[e] + far_num) * inv);
+        }
+        *(bf16x4*)(orow + d0) = w;
+      }
+    if (A.lse != nullptr && c.g == 0) A.lse[ridx] = (M + __log2f(Z)) * LN2;
+  }
 }
 
 }  // namespace
@@ -618,29 +597,34 @@ hipError_t jl_launch_prefill_bf16(const JlPrefillWs& ws, void* o, float* lse, in
   A.kr_lo = (const __bf16*)ws.kr_lo;
   A.out = (__bf16*)o;
   A.lse = lse;
+  A.o1 = (float*)ws.o1;
   A.o2 = (float*)ws.o2;
+  A.lse1 = (float*)ws.lse1;
   A.lse2 = (float*)ws.lse2;
   A.total = total_tokens;
   A.t_pad = ws.t_pad;
   A.w0 = w0;
   A.Hq = Hq;
   A.sl2 = scale * LOG2E;
-  bool any_band = false, any_p2 = false;
+  bool any_p1 = false, any_p2 = false, any_p3 = false;
   for (int b = 0; b < seqs.nseq; ++b) {
+    if (seqs.len[b] == 0) continue;
     const bool only1 = w0 >= (int64_t)seqs.len[b];
     const bool only2 = seqs.G[b] == 1 && !only1;
-    any_band |= !only2 && seqs.len[b] > 0;
-    any_p2 |= !only1 && seqs.len[b] > 0;
+    any_p1 |= !only2;
+    any_p2 |= !only1;
+    any_p3 |= !only1 && !only2;
   }
   const unsigned nblk = (unsigned)sc.total_units * (unsigned)Hq;   // multiple of 8 when xcd_heads
   const unsigned nfirst = (unsigned)(seqs.nseq * Hq);
-  if (any_p2) {
-    if (nblk) prefill_pass2_kernel<false><<<nblk, NT, 0, st>>>(A, hm, seqs, sc);
-    prefill_pass2_kernel<true><<<nfirst, NT, 0, st>>>(A, hm, seqs, sc);
-  }
-  if (any_band) {
-    if (nblk) prefill_band_kernel<false><<<nblk, NT, 0, st>>>(A, hm, seqs, sc);
-    prefill_band_kernel<true><<<nfirst, NT, 0, st>>>(A, hm, seqs, sc);
-  }
+#define JL_PASS(ROLE)                                                                   \
+  do {                                                                                  \
+    if (nblk) prefill_pass_kernel<ROLE, false><<<nblk, NT, 0, st>>>(A, hm, seqs, sc);   \
+    prefill_pass_kernel<ROLE, true><<<nfirst, NT, 0, st>>>(A, hm, seqs, sc);            \
+  } while (0)
+  if (any_p2) JL_PASS(0);
+  if (any_p1) JL_PASS(1);
+  if (any_p3) JL_PASS(2);
+#undef JL_PASS
   return hipGetLastError();
 }
