@@ -47,9 +47,10 @@ struct JlHeadMap {
 // Workspace of the prefill path: rotated operands, head-major.
 //   qb, qr   [Hq][T_pad][d]   q rotated at p and at f(p)
 //   kb, kr   [Hkv][T_pad][d]  k rotated at p and at f(p)
-//   vt       [Hkv][d][vt_cols] v transposed (bf16 path only); sequence b
-//            starts at column vstart[b], a multiple of 64, and its columns
-//            past L_b up to the next multiple of 64 are zero
+//   vt       [Hkv][vt_cols / 64][d][64] v transposed in 64-key tiles (bf16
+//            path only); sequence b starts at key column vstart[b], a
+//            multiple of 64, and its columns past L_b up to the next multiple
+//            of 64 are zero
 // Rows T .. T_pad-1 are zero.  qr / kr alias qb / kb when no sequence has
 // G > 1.
 //   qb_lo, qr_lo [Hq][nseq * JL_LO_ROWS][d], kb_lo, kr_lo [Hkv][nseq * JL_LO_ROWS][d]

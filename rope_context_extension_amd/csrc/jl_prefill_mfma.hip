@@ -55,10 +55,10 @@ constexpr int KP = 272;                 // LDS pitch of a K row (256 B + 16 B pa
 constexpr int VP = 144;                 // LDS pitch of a V^T row (128 B + 16 B pad)
 constexpr int KT_BYTES = BK * KP;       // 17408
 constexpr int VT_BYTES = D * VP;        // 18432
-constexpr int KT_PIECES = KT_BYTES / 1024;         // 17 KiB pieces of K
-constexpr int PIECES = (KT_BYTES + VT_BYTES) / 1024; // 35 KiB pieces per tile
-constexpr int PIECES_PER_WAVE = (PIECES + 3) / 4;   // 9
-constexpr int NBUF = 3;                             // tile buffers in LDS
+constexpr int KT_PIECES = KT_BYTES / 1024;          // 17 KiB pieces of a K tile
+constexpr int VT_PIECES = VT_BYTES / 1024;          // 18 KiB pieces of a V^T tile
+constexpr int K_PER_WAVE = (KT_PIECES + 3) / 4;     // 5
+constexpr int V_PER_WAVE = (VT_PIECES + 3) / 4;     // 5
 constexpr int BUF_BYTES = KT_BYTES + VT_BYTES;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -77,27 +77,48 @@ __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 // contiguous KiB per wave instruction, so piece n of a tile covers LDS bytes
 // [n KiB, n KiB + 1 KiB) and each lane fetches the global chunk that belongs
 // at its LDS offset.  Lanes that land in a pad re-fetch the row's first
-// chunk (the pad is never read).
-//
-// Every wave issues exactly PIECES_PER_WAVE instructions per tile (a wave
-// that runs out of pieces repeats the last one, rewriting identical bytes), so
-// "all but the newest tile landed" is the same vmcnt value in every wave.
-__device__ inline void issue_tile(char* buf, const char* kg, const char* vg, int64_t vrow_bytes,
-                                  int wave, int lane) {
+// chunk (the pad is never read).  Every wave issues the same number of
+// pieces per tile (a wave that runs out repeats its last piece, rewriting
+// identical bytes), so waits are the same in every wave.  The per-lane source
+// offsets depend only on (wave, lane) and are computed once.
+struct DmaPlan {
+  uint32_t koff[K_PER_WAVE];   // byte offset of this lane's source chunk in a K tile
+  uint32_t voff[V_PER_WAVE];   // ... in a V^T tile
+};
+
+__device__ inline DmaPlan make_dma_plan(int wave, int lane) {
+  DmaPlan p;
 #pragma unroll
-  for (int i = 0; i < PIECES_PER_WAVE; ++i) {
-    const int n = min(wave + 4 * i, PIECES - 1);
-    if (n < KT_PIECES) {
-      const int off = n * 1024 + lane * 16;
-      const int r = off / KP, cb = off - r * KP;
-      const int c = cb < 256 ? cb : 0;
-      __builtin_amdgcn_global_load_lds(kg + r * 256 + c, (lds_void*)(buf + n * 1024), 16, 0, 0);
-    } else {
-      const int off = (n - KT_PIECES) * 1024 + lane * 16;
-      const int r = off / VP, cb = off - r * VP;
-      const int c = cb < 128 ? cb : 0;
-      __builtin_amdgcn_global_load_lds(vg + r * vrow_bytes + c, (lds_void*)(buf + n * 1024), 16, 0, 0);
-    }
+  for (int i = 0; i < K_PER_WAVE; ++i) {
+    const int n = min(wave + 4 * i, KT_PIECES - 1);
+    const int off = n * 1024 + lane * 16;
+    const int r = off / KP, cb = off - r * KP;
+    p.koff[i] = (uint32_t)(r * 256 + (cb < 256 ? cb : 0));
+  }
+#pragma unroll
+  for (int i = 0; i < V_PER_WAVE; ++i) {
+    const int n = min(wave + 4 * i, VT_PIECES - 1);
+    const int off = n * 1024 + lane * 16;
+    const int r = off / VP, cb = off - r * VP;
+    p.voff[i] = (uint32_t)(r * 128 + (cb < 128 ? cb : 0));
+  }
+  return p;
+}
+
+// kg / vg: the tile's first byte in global memory (K rows / V^T block)
+__device__ inline void issue_k(char* kbuf, const char* kg, const DmaPlan& p, int wave) {
+#pragma unroll
+  for (int i = 0; i < K_PER_WAVE; ++i) {
+    const int n = min(wave + 4 * i, KT_PIECES - 1);
+    __builtin_amdgcn_global_load_lds(kg + p.koff[i], (lds_void*)(kbuf + n * 1024), 16, 0, 0);
+  }
+}
+
+__device__ inline void issue_v(char* vbuf, const char* vg, const DmaPlan& p, int wave) {
+#pragma unroll
+  for (int i = 0; i < V_PER_WAVE; ++i) {
+    const int n = min(wave + 4 * i, VT_PIECES - 1);
+    __builtin_amdgcn_global_load_lds(vg + p.voff[i], (lds_void*)(vbuf + n * 1024), 16, 0, 0);
   }
 }
 
@@ -182,10 +203,10 @@ __device__ inline void mask_tile(f32x16* s, int myrow, int j0, int w0, int g) {
     }
 }
 
-// Online softmax on raw scores s (masked entries -inf): p = exp2(s sl2 - m)
-// written back into s, the row sum accumulated in st.l, and the accumulators
-// rescaled when the stabiliser moves.
-__device__ inline void softmax_tile(f32x16* s, PassState& st, f32x16* o, float sl2) {
+// Online softmax on raw scores s (masked entries -inf), first half: the row
+// maximum and the lazy rescale of the accumulators when the stabiliser moves.
+// Returns -m (the exp2 bias) for the second half.
+__device__ inline float softmax_max(const f32x16* s, PassState& st, f32x16* o, float sl2) {
   float mx = -INFINITY;
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb)
@@ -201,7 +222,11 @@ __device__ inline void softmax_tile(f32x16* s, PassState& st, f32x16* o, float s
     for (int db = 0; db < 4; ++db) o[db] *= a;
     st.m = mn;
   }
-  const float nb = st.m == -INFINITY ? 0.f : -st.m;
+  return st.m == -INFINITY ? 0.f : -st.m;
+}
+
+// Second half: p = exp2(s sl2 - m) written back into s, row sum into st.l.
+__device__ inline void softmax_exp(f32x16* s, PassState& st, float sl2, float nb) {
   float sum = 0.f;
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb)
@@ -221,8 +246,7 @@ __device__ inline void load_q(bf16x8* qf, const __bf16* rowp, int g) {
 
 struct TileSrc {
   const char* k;       // K rows of (kv head, sequence), row-major 256 B rows
-  const char* v;       // V^T rows of (kv head, sequence start), 128 channels
-  int64_t vrow_bytes;  // bytes between V^T rows
+  const char* v;       // V^T tiles of (kv head, sequence), 16 KiB [128][64] blocks
   const __bf16* klo;   // residual K rows (PRECISE), row p of the sequence
 };
 
@@ -247,79 +271,70 @@ __device__ inline bool wave_needs_mask(int j0, const WaveRows& wr) {
   return m;
 }
 
-// A full flash pass over key tiles [t0, t1).
-// PIPE = false: two LDS buffers; iteration t waits for tile t, issues the DMA
-// of tile t+1 into the other buffer and multiplies tile t.  Latency between
-// MFMA and vector ALU work is hidden by the second wave on each SIMD.
-// PIPE = true (one wave per SIMD): three buffers, and within the wave the
-// MFMAs of S(t+1) = K_{t+1} Q^T are issued before the softmax of tile t, so
-// the vector ALU work overlaps them; iteration t waits for tile t+1, DMAs
-// tile t+2 into the buffer tile t-1 used, then S(t+1), softmax(t), PV(t).
-template <int KIND, bool PRECISE, bool PIPE>
+// A full flash pass over key tiles [t0, t1), software-pipelined within each
+// wave: the MFMAs of S(t+1) = K_{t+1} Q^T are issued before the softmax of
+// tile t, so that vector-ALU work overlaps them.  K and V^T tiles have two
+// LDS buffers each; K runs two tiles ahead, V one.  Iteration t:
+//   wait for K(t+1), V(t); barrier (every wave is done with S(t)'s K buffer
+//   and PV(t-1)'s V buffer); DMA K(t+2) and V(t+1) into those buffers;
+//   S(t+1); softmax(t); PV(t).
+template <int KIND, bool PRECISE>
 __device__ inline void run_pass(char* smem, const TileSrc& src, int t0, int t1, const bf16x8* qf,
                                 const bf16x8* ql, PassState& st, f32x16* o, const WaveRows& wr,
                                 float sl2, int wave, int lane) {
-  constexpr int NB = PIPE ? 3 : 2;
   const int g = lane >> 5;
   __syncthreads();                      // every wave is done with all buffers
   if (t0 >= t1) return;
-  auto bufp = [&](int t) { return smem + ((t - t0) % NB) * BUF_BYTES; };
-  auto issue = [&](int t) {
-    issue_tile(bufp(t), src.k + (int64_t)t * BK * 256, src.v + (int64_t)t * BK * 2, src.vrow_bytes,
-               wave, lane);
-  };
+  const DmaPlan plan = make_dma_plan(wave, lane);
+  char* const kb0 = smem;
+  char* const kb1 = smem + KT_BYTES;
+  char* const vb0 = smem + 2 * KT_BYTES;
+  char* const vb1 = smem + 2 * KT_BYTES + VT_BYTES;
+  auto kbuf = [&](int t) { return ((t - t0) & 1) ? kb1 : kb0; };
+  auto vbuf = [&](int t) { return ((t - t0) & 1) ? vb1 : vb0; };
+  auto issue_kt = [&](int t) { issue_k(kbuf(t), src.k + (int64_t)t * BK * 256, plan, wave); };
+  auto issue_vt = [&](int t) { issue_v(vbuf(t), src.v + (int64_t)t * (D * BK * 2), plan, wave); };
   auto scores = [&](int t, f32x16* s) {
-    score_tile<PRECISE>(bufp(t), qf, ql, PRECISE ? src.klo + (int64_t)t * BK * D : nullptr, lane, s);
+    score_tile<PRECISE>(kbuf(t), qf, ql, PRECISE ? src.klo + (int64_t)t * BK * D : nullptr, lane, s);
   };
   auto finish = [&](int t, f32x16* s) {
     const int j0 = t * BK;
     if (wave_needs_mask<KIND>(j0, wr)) mask_tile<KIND>(s, wr.myrow, j0, wr.w0, g);
-    softmax_tile(s, st, o, sl2);
-    pv_tile(bufp(t) + KT_BYTES, s, lane, o);
+    const float nb = softmax_max(s, st, o, sl2);
+    softmax_exp(s, st, sl2, nb);
+    pv_tile(vbuf(t), s, lane, o);
   };
-  issue(t0);
-  if constexpr (!PIPE) {
-    for (int t = t0; t < t1; ++t) {
-      wait_all_tiles();                 // tile t landed
-      __syncthreads();                  // ... for every wave; tile t-1's buffer is free
-      if (t + 1 < t1) issue(t + 1);
-      if (wave_has_work<KIND>(t * BK, wr)) {
-        f32x16 s[2];
-        scores(t, s);
-        finish(t, s);
-      }
-    }
-  } else {
-    if (t0 + 1 < t1) {
-      issue(t0 + 1);
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PIECES_PER_WAVE) : "memory");   // tile t0 landed
-    } else {
-      wait_all_tiles();
-    }
+  issue_kt(t0);
+  if (t0 + 1 < t1) issue_kt(t0 + 1);
+  issue_vt(t0);
+  wait_all_tiles();
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  bool wa = wave_has_work<KIND>(t0 * BK, wr), wb = false;
+  if (wa) scores(t0, sa);
+  // two iterations per trip so the two score sets never need a copy
+  for (int t = t0; t < t1; t += 2) {
+    // ---- iteration t: S(t) in sa ----
+    wait_all_tiles();                   // K(t+1) and V(t) landed
     __syncthreads();
-    f32x16 sa[2], sb[2];
-    bool wa = wave_has_work<KIND>(t0 * BK, wr), wb = false;
-    if (wa) scores(t0, sa);
-    // two iterations per trip so the two score sets never need a copy
-    for (int t = t0; t < t1; t += 2) {
-      if (t + 1 < t1) {
-        wait_all_tiles();
-        __syncthreads();
-        if (t + 2 < t1) issue(t + 2);
-        wb = wave_has_work<KIND>((t + 1) * BK, wr);
-        if (wb) scores(t + 1, sb);
-      }
-      if (wa) finish(t, sa);
-      if (t + 1 >= t1) break;
-      if (t + 2 < t1) {
-        wait_all_tiles();
-        __syncthreads();
-        if (t + 3 < t1) issue(t + 3);
-        wa = wave_has_work<KIND>((t + 2) * BK, wr);
-        if (wa) scores(t + 2, sa);
-      }
-      if (wb) finish(t + 1, sb);
+    if (t + 2 < t1) issue_kt(t + 2);
+    if (t + 1 < t1) {
+      issue_vt(t + 1);
+      wb = wave_has_work<KIND>((t + 1) * BK, wr);
+      if (wb) scores(t + 1, sb);
     }
+    if (wa) finish(t, sa);
+    if (t + 1 >= t1) break;
+    // ---- iteration t+1: S(t+1) in sb ----
+    wait_all_tiles();
+    __syncthreads();
+    if (t + 3 < t1) issue_kt(t + 3);
+    if (t + 2 < t1) {
+      issue_vt(t + 2);
+      wa = wave_has_work<KIND>((t + 2) * BK, wr);
+      if (wa) scores(t + 2, sa);
+    }
+    if (wb) finish(t + 1, sb);
   }
 }
 
@@ -421,11 +436,11 @@ __device__ inline bool make_ctx(const PrefillArgs& A, const JlHeadMap& hm, const
   c->tw0 = (c->i0 - c->w0 + 1) > 0 ? (c->i0 - c->w0 + 1) / BK : 0;   // first window tile
   c->lrows = (int64_t)seqs.nseq * JL_LO_ROWS;
   c->lo_base = (int64_t)b * JL_LO_ROWS;
-  const int64_t vcols = seqs.vt_cols;
-  const char* vbase = (const char*)(A.vt + (int64_t)c->kvh * D * vcols + seqs.vstart[b]);
-  c->base_src = TileSrc{(const char*)(A.kb + ((int64_t)c->kvh * A.t_pad + c->s0) * D), vbase, vcols * 2,
+  const int64_t vtiles = seqs.vt_cols / 64;
+  const char* vbase = (const char*)(A.vt + ((int64_t)c->kvh * vtiles + seqs.vstart[b] / 64) * (D * 64));
+  c->base_src = TileSrc{(const char*)(A.kb + ((int64_t)c->kvh * A.t_pad + c->s0) * D), vbase,
                         A.kb_lo + ((int64_t)c->kvh * c->lrows + c->lo_base) * D};
-  c->rem_src = TileSrc{(const char*)(A.kr + ((int64_t)c->kvh * A.t_pad + c->s0) * D), vbase, vcols * 2,
+  c->rem_src = TileSrc{(const char*)(A.kr + ((int64_t)c->kvh * A.t_pad + c->s0) * D), vbase,
                        A.kr_lo + ((int64_t)c->kvh * c->lrows + c->lo_base) * D};
   return true;
 }
@@ -464,7 +479,7 @@ template <int ROLE, bool FIRST>
 __global__ void __launch_bounds__(NT, 2) prefill_pass_kernel(PrefillArgs A, JlHeadMap hm, JlSeqs seqs,
                                                              JlSched sc) {
   constexpr int KIND = ROLE == 0 ? 0 : 1;
-  __shared__ __align__(1024) char smem[2 * BUF_BYTES];
+  __shared__ __align__(1024) char smem[2 * KT_BYTES + 2 * VT_BYTES];
   int h, b, qt;
   if (!block_item<FIRST>(sc, A.Hq, &h, &b, &qt)) return;
   BlockCtx c;
@@ -481,8 +496,8 @@ __global__ void __launch_bounds__(NT, 2) prefill_pass_kernel(PrefillArgs A, JlHe
   for (int db = 0; db < 4; ++db) o[db] = f32x16{};
   PassState st{-INFINITY, 0.f};
   const int t0 = ROLE == 0 || c.only1 ? 0 : c.tw0;
-  run_pass<KIND, FIRST, false>(smem, ROLE == 1 ? c.base_src : c.rem_src, t0, c.tiles_end, qf, ql, st, o,
-                               c.wr, A.sl2, c.wave, c.lane);
+  run_pass<KIND, FIRST>(smem, ROLE == 1 ? c.base_src : c.rem_src, t0, c.tiles_end, qf, ql, st, o, c.wr,
+                        A.sl2, c.wave, c.lane);
   const float l = st.l + __shfl_xor(st.l, 32, 64);
   if (c.wr.myrow >= c.L) return;
   const int64_t ridx = (int64_t)c.h * A.total + c.s0 + c.wr.myrow;

@@ -119,8 +119,9 @@ __global__ void __launch_bounds__(256) rope_prepass_kernel(
   }
 }
 
-// v [T][Hkv][128] bf16 -> vt [Hkv][128][vt_cols], 64 tokens of one sequence
-// per block through LDS; columns past the sequence end are zero.
+// v [T][Hkv][128] bf16 -> vt [Hkv][vt_cols / 64][128][64] (V^T in 64-key
+// tiles), 64 tokens of one sequence per block through LDS; keys past the
+// sequence end are zero.
 __global__ void __launch_bounds__(256) transpose_v_kernel(const __bf16* __restrict__ v,
                                                           __bf16* __restrict__ vt, int64_t vt_cols,
                                                           int Hkv, JlSeqs seqs) {
@@ -148,7 +149,9 @@ __global__ void __launch_bounds__(256) transpose_v_kernel(const __bf16* __restri
     __bf16 out[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) out[e] = tile[(tk + e) * P + dd];
-    *(uint4*)(vt + ((int64_t)h * D + dd) * vt_cols + seqs.vstart[b] + p0 + tk) = *(const uint4*)out;
+    // tile-major: 64-key tile n of kv head h is a contiguous [128][64] block
+    const int64_t tile = (seqs.vstart[b] + p0) / 64;
+    *(uint4*)(vt + (((int64_t)h * (vt_cols / 64) + tile) * D + dd) * 64 + tk) = *(const uint4*)out;
   }
 }
 
