@@ -9,19 +9,26 @@
 // gives the vector rotated at the aliased position).  G is recomputed from L
 // at every step, so crossing a G boundary needs no cache work.
 //
-// Split-K: workgroup w covers keys [w*C, (w+1)*C) for every head and writes
-// unnormalised partial (max, sum, accumulator) statistics; a second kernel
-// merges them through their LogSumExp values.
+// Split-K: workgroup w covers keys [w C, (w+1) C) for every head and writes
+// unnormalised partial statistics (max, sum, accumulator) per head; a second
+// kernel merges them through their LogSumExp values.
 //
 // Inside a workgroup (4 waves), per 64-key sub-chunk:
-//   scores  each wave takes 16 keys; every lane owns one key and 16 rotary
-//           pairs (m, m + 64), so the Delta rotation is lane-local and its
-//           sin/cos are computed once per (key, m) and reused by every kv
-//           head.  S^T = K Q^T runs on v_mfma_f32_16x16x32_bf16 with the
-//           (rotated) key rows as the A operand.
-//   softmax per head over the 64 keys, online across sub-chunks.
-//   PV      vector ALU: each lane streams 4 channels of one kv head's V rows
-//           and accumulates the heads that share that kv head.
+//   angles  the workgroup fills an LDS table of cos/sin(Delta_j theta_m) for
+//           the sub-chunk's remote keys (one evaluation per (key, m), shared
+//           by every kv head);
+//   scores  wave w owns kv heads 2w and 2w+1.  Per 16-key block a lane holds
+//           one key's rotary pairs (m, m + 64) for 16 values of m, rotates
+//           them in registers and feeds them as the A operand of
+//           v_mfma_f32_16x16x32_bf16 against the query block (B operand:
+//           the kv head's q heads as columns);
+//   softmax the sub-chunk's scores of a head sit in 4 lanes x 16 values, so
+//           the max and sum need two lane exchanges; the result is online
+//           across sub-chunks;
+//   PV      half a wave per kv head: each lane streams 4 channels of the V
+//           rows (8 bytes per key) and accumulates the kv head's q heads
+//           with probabilities read from a wave-private LDS row.
+// The waves of a workgroup only meet at the angle-table barrier.
 #include "jl_internal.h"
 
 namespace {
@@ -31,8 +38,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;
 constexpr int NT = 256;
-constexpr int SUB = 64;          // keys per sub-chunk
-constexpr int PS = 132;          // floats per partial record: m, l, pad, pad, acc[128]
+constexpr int SUB = 64;            // keys per sub-chunk
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr int MAX_HQ = 64;
@@ -44,40 +50,47 @@ __device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// d index held in slot j of MFMA step kb by lane group gq (0..3): the lane
+__device__ inline uint32_t pack_bf16(float a, float b) {
+  __bf16 t[2] = {(__bf16)a, (__bf16)b};
+  return *(const uint32_t*)t;
+}
+
+// channel held in slot j of MFMA step kb by lane group gq (0..3): the lane
 // holds the rotary pairs (16 gq + x, 64 + 16 gq + x), x = 0..15.
 __device__ inline int d_of(int kb, int gq, int j) { return (kb >> 1) * 64 + 16 * gq + 8 * (kb & 1) + j; }
 
+// Partial records, laid out for the merge:
+//   part_ml [Hq][nwg][2]    (max in log2 units, sum)
+//   part_o  [Hq][nwg][128]  unnormalised accumulator
 template <int NG>
 __global__ void __launch_bounds__(NT) decode_split_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kc, const __bf16* __restrict__ vc,
-    float* __restrict__ part, int L, int Hq, int Hkv, JlHeadMap hm, int w0, int G, int nsub,
-    float scale_log2, JlFreqs fr) {
-  // slot = kvh * NG + n  <->  q head heads[slot]
-  __shared__ __align__(16) __bf16 qlds[2][MAX_HQ * D];   // [variant][slot][d]
-  __shared__ float slds[SUB * MAX_HQ];                     // [key][slot]
-  __shared__ float mrun[MAX_HQ], lrun[MAX_HQ], alpha[MAX_HQ];
+    float* __restrict__ part_ml, float* __restrict__ part_o, int L, int Hq, int Hkv, JlHeadMap hm,
+    int w0, int G, int nsub, int nwg, float scale_log2, JlFreqs fr) {
+  __shared__ __align__(16) __bf16 qlds[2][MAX_HQ * D];   // [variant][slot][d]; slot = kvh*NG + n
+  __shared__ __align__(16) float2 trig[SUB][64];          // cos/sin(Delta_j theta_m) of the sub-chunk
+  __shared__ __align__(16) float prob[4][SUB][2 * NG];    // wave-private probabilities [key][slot]
   __shared__ int heads[MAX_HQ];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i = L - 1;
   const int c_begin = blockIdx.x * nsub * SUB;
 
   if (tid < Hq) {
-    // the n-th q head of kv head k, in head order
-    int kvh = tid / NG, n = tid % NG, cnt = 0, hh = 0;
+    // slot s = kvh * NG + n  <->  the n-th q head (in head order) of kv head kvh
+    const int kvh = tid / NG, n = tid % NG;
+    int cnt = 0, hh = 0;
     for (int h = 0; h < Hq; ++h)
       if (hm.kv_of[h] == kvh) {
         if (cnt == n) hh = h;
         ++cnt;
       }
     heads[tid] = hh;
-    mrun[tid] = -INFINITY;
-    lrun[tid] = 0.f;
   }
   __syncthreads();
-  // query in both variants: base (as given) and rotated by Delta_q
   {
+    // the query in both variants: as given (base) and rotated by Delta_q
     const int dq = jl_remote_pos(i, G) - i;
     for (int e = tid; e < Hq * 64; e += NT) {
       const int slot = e >> 6, m = e & 63;
@@ -91,182 +104,205 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
       qlds[1][slot * D + m + 64] = (__bf16)(x2 * c + x1 * s);
     }
   }
-  __syncthreads();
 
-  // PV ownership: (kv head, 4 channels)
-  const int pv_kvh = tid >> 5, pv_c = (tid & 31) * 4;
+  const int kl = lane & 15, gq = lane >> 4;        // score layout: key, rotary group
+  const int half = lane >> 5, pc = (lane & 31) * 4; // PV layout: kv head of the pair, 4 channels
+  const int kv0 = 2 * wave;                          // this wave's kv heads: kv0, kv0 + 1
+  const bool wave_active = kv0 < Hkv;
+  const int my_kvh = kv0 + half;
+  const bool pv_active = my_kvh < Hkv;
   float acc[NG][4];
 #pragma unroll
   for (int n = 0; n < NG; ++n)
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[n][e] = 0.f;
+  float run_m[2] = {-INFINITY, -INFINITY};   // per column n < NG of each kv head of the pair
+  float run_l[2] = {0.f, 0.f};               // (lanes with kl = n hold head n's values)
 
-  const int kl = lane & 15, gq = lane >> 4;
   for (int sc = 0; sc < nsub; ++sc) {
     const int c0 = c_begin + sc * SUB;
     if (c0 >= L) break;
-    // ---------------- scores ----------------
-    const int j = c0 + wave * 16 + kl;                // this lane's key
-    const bool valid = j < L;
-    const int jj = valid ? j : L - 1;
-    const bool rem = valid && (i - j) >= w0;
-    const bool any_rem = __any(rem);
-    const bool any_loc = __any(valid && !rem);
-    float cs[16], sn[16];
-    if (any_rem) {
-      const int dj = jl_remote_pos(jj, G) - jj;
-#pragma unroll
-      for (int x = 0; x < 16; ++x) jl_rope_sincos(dj, fr.turn_frac[16 * gq + x], &sn[x], &cs[x]);
+    __syncthreads();                           // previous sub-chunk done with trig
+    const bool any_remote = (i - c0) >= w0;    // the sub-chunk's first key is the farthest
+    if (any_remote) {
+      for (int e = tid; e < SUB * 64; e += NT) {
+        const int kk = e >> 6, m = e & 63;
+        const int j = min(c0 + kk, L - 1);
+        float s, c;
+        jl_rope_sincos(jl_remote_pos(j, G) - j, fr.turn_frac[m], &s, &c);
+        trig[kk][m] = make_float2(c, s);
+      }
     }
-    for (int kvh = 0; kvh < Hkv; ++kvh) {
-      const __bf16* kp = kc + ((int64_t)jj * Hkv + kvh) * D;
-      uint4 kw[4];
+    __syncthreads();
+    if (!wave_active) continue;
+
+    // ---------------- scores: 4 blocks of 16 keys x 2 kv heads ----------------
+    f32x4 sco[2][4];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) kw[kb] = *(const uint4*)(kp + d_of(kb, gq, 0));
-      f32x4 sr = {}, sl = {};
-      const int ncol = lane & 15;                     // B column = slot within kv head
-      if (any_rem) {
-        // rotate pairs x: first halves in kw[0], kw[1]; second halves in kw[2], kw[3]
-        uint32_t w1[8], w2[8];
-        const uint32_t* a = (const uint32_t*)&kw[0];
-        const uint32_t* b = (const uint32_t*)&kw[2];
+    for (int p = 0; p < 2; ++p) {
+      const int kvh = min(kv0 + p, Hkv - 1);
 #pragma unroll
-        for (int x2 = 0; x2 < 8; ++x2) {
-          const float a_lo = bf_lo(a[x2]), a_hi = bf_hi(a[x2]);
-          const float b_lo = bf_lo(b[x2]), b_hi = bf_hi(b[x2]);
-          const int x = 2 * x2;
-          const float y1l = a_lo * cs[x] - b_lo * sn[x], y2l = b_lo * cs[x] + a_lo * sn[x];
-          const float y1h = a_hi * cs[x + 1] - b_hi * sn[x + 1], y2h = b_hi * cs[x + 1] + a_hi * sn[x + 1];
-          __bf16 t1[2] = {(__bf16)y1l, (__bf16)y1h};
-          __bf16 t2[2] = {(__bf16)y2l, (__bf16)y2h};
-          w1[x2] = *(const uint32_t*)t1;
-          w2[x2] = *(const uint32_t*)t2;
+      for (int blk = 0; blk < 4; ++blk) {
+        const int kk = blk * 16 + kl;
+        const int j = c0 + kk;
+        const int jj = j < L ? j : L - 1;
+        const bool rem = j < L && (i - j) >= w0;
+        const __bf16* kp = kc + ((int64_t)jj * Hkv + kvh) * D;
+        uint4 kw[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) kw[kb] = *(const uint4*)(kp + d_of(kb, gq, 0));
+        const bool any_rem = __any(rem);
+        const bool any_loc = __any(j < L && !rem);
+        f32x4 sr = {}, sl = {};
+        const int ncol = lane & 15;
+        if (any_rem) {
+          uint32_t w1[8], w2[8];
+          const uint32_t* a = (const uint32_t*)&kw[0];
+          const uint32_t* b = (const uint32_t*)&kw[2];
+#pragma unroll
+          for (int x2 = 0; x2 < 8; ++x2) {
+            const float4 cs = *(const float4*)&trig[kk][16 * gq + 2 * x2];   // (c, s) of two pairs
+            const float a_lo = bf_lo(a[x2]), a_hi = bf_hi(a[x2]);
+            const float b_lo = bf_lo(b[x2]), b_hi = bf_hi(b[x2]);
+            w1[x2] = pack_bf16(a_lo * cs.x - b_lo * cs.y, a_hi * cs.z - b_hi * cs.w);
+            w2[x2] = pack_bf16(b_lo * cs.x + a_lo * cs.y, b_hi * cs.z + a_hi * cs.w);
+          }
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            const uint32_t* src = (kb < 2) ? (w1 + 4 * kb) : (w2 + 4 * (kb - 2));
+            bf16x8 bv = {};
+            if (ncol < NG) bv = *(const bf16x8*)(&qlds[1][(kvh * NG + ncol) * D + d_of(kb, gq, 0)]);
+            sr = mfma16(*(const bf16x8*)src, bv, sr);
+          }
         }
+        if (any_loc) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const uint32_t* src = (kb < 2) ? (w1 + 4 * kb) : (w2 + 4 * (kb - 2));
-          bf16x8 av = *(const bf16x8*)src;
-          bf16x8 bv = {};
-          if (ncol < NG) bv = *(const bf16x8*)(&qlds[1][(kvh * NG + ncol) * D + d_of(kb, gq, 0)]);
-          sr = mfma16(av, bv, sr);
+          for (int kb = 0; kb < 4; ++kb) {
+            bf16x8 bv = {};
+            if (ncol < NG) bv = *(const bf16x8*)(&qlds[0][(kvh * NG + ncol) * D + d_of(kb, gq, 0)]);
+            sl = mfma16(*(const bf16x8*)&kw[kb], bv, sl);
+          }
         }
-      }
-      if (any_loc) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          bf16x8 av = *(const bf16x8*)&kw[kb];
-          bf16x8 bv = {};
-          if (ncol < NG) bv = *(const bf16x8*)(&qlds[0][(kvh * NG + ncol) * D + d_of(kb, gq, 0)]);
-          sl = mfma16(av, bv, sl);
-        }
-      }
-      // lane holds S^T[key 4 gq + e][slot ncol]
-      if (ncol < NG) {
+        // lane holds S^T[key blk*16 + 4 gq + e][column kl]
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int kk = wave * 16 + 4 * gq + e;
-          const int jk = c0 + kk;
-          float v;
-          if (jk >= L) v = -INFINITY;
-          else v = ((i - jk) >= w0 ? sr[e] : sl[e]) * scale_log2;
-          slds[kk * MAX_HQ + kvh * NG + ncol] = v;
+          const int jk = c0 + blk * 16 + 4 * gq + e;
+          const float v = ((i - jk) >= w0 ? sr[e] : sl[e]) * scale_log2;
+          sco[p][blk][e] = jk < L ? v : -INFINITY;
         }
       }
     }
-    __syncthreads();
-    // ---------------- softmax (8 threads per slot) ----------------
-    for (int base = 0; base < Hq; base += NT / 8) {
-      const int slot = base + (tid >> 3);
-      const int part8 = tid & 7;
+    // ---------------- softmax per column (q head) over the 64 keys ----------------
+    // column kl of kv head kv0 + p: lanes kl + 16 gq, values sco[p][0..3][0..3]
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
       float mx = -INFINITY;
-      if (slot < Hq) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, slds[(part8 * 8 + e) * MAX_HQ + slot]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
+      for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sco[p][blk][e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mn = fmaxf(run_m[p], mx);         // finite: every sub-chunk has a valid key
+      const float alpha = __builtin_amdgcn_exp2f(run_m[p] - mn);
       float sum = 0.f;
-      float mo = 0.f, mn = 0.f;
-      if (slot < Hq) {
-        mo = mrun[slot];
-        mn = fmaxf(mo, mx);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float* ps = &slds[(part8 * 8 + e) * MAX_HQ + slot];
-          const float p = __builtin_amdgcn_exp2f(*ps - mn);
-          *ps = p;
-          sum += p;
+      for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pr = __builtin_amdgcn_exp2f(sco[p][blk][e] - mn);
+          sum += pr;
+          if (kl < NG) prob[wave][blk * 16 + 4 * gq + e][p * NG + kl] = pr;
+        }
+      sum += __shfl_xor(sum, 16, 64);
+      sum += __shfl_xor(sum, 32, 64);
+      run_l[p] = run_l[p] * alpha + sum;
+      run_m[p] = mn;
+      // rescale the PV accumulators of this kv head's columns: lanes of half p
+      // own the accumulators, column n's alpha lives in lane n
+#pragma unroll
+      for (int n = 0; n < NG; ++n) {
+        const float a_n = __shfl(alpha, n, 64);
+        if (half == p) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[n][e] *= a_n;
         }
       }
-      sum += __shfl_xor(sum, 1, 64);
-      sum += __shfl_xor(sum, 2, 64);
-      sum += __shfl_xor(sum, 4, 64);
-      __syncthreads();   // all reads of mrun done before it is updated
-      if (slot < Hq && part8 == 0) {
-        const float a = __builtin_amdgcn_exp2f(mo - mn);   // mo = -inf on the first sub-chunk
-        alpha[slot] = a;
-        lrun[slot] = lrun[slot] * a + sum;
-        mrun[slot] = mn;
-      }
     }
-    __syncthreads();
-    // ---------------- PV ----------------
-    for (int kvh = pv_kvh; kvh < Hkv; kvh += NT / 32) {
-      // (for Hkv > 8 a thread would own several kv heads; callers keep Hkv <= 8)
-      float a[NG];
-#pragma unroll
-      for (int n = 0; n < NG; ++n) a[n] = alpha[kvh * NG + n];
-#pragma unroll
-      for (int n = 0; n < NG; ++n)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[n][e] *= a[n];
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0xc07f);              // lgkmcnt(0): prob rows written
+    // ---------------- PV: half-wave per kv head, 4 channels per lane ----------------
+    if (pv_active) {
       const int ntok = min(SUB, L - c0);
-      const __bf16* vp = vc + ((int64_t)c0 * Hkv + kvh) * D + pv_c;
-      for (int t = 0; t < ntok; ++t) {
-        const uint2 vw = *(const uint2*)(vp + (int64_t)t * Hkv * D);
-        const float v0 = bf_lo(vw.x), v1 = bf_hi(vw.x), v2 = bf_lo(vw.y), v3 = bf_hi(vw.y);
-        const float* pr = &slds[t * MAX_HQ + kvh * NG];
+      const __bf16* vp = vc + ((int64_t)c0 * Hkv + my_kvh) * D + pc;
+      const float* pr = &prob[wave][0][half * NG];
+      if (ntok == SUB) {
+#pragma unroll 16
+        for (int t = 0; t < SUB; ++t) {
+          const uint2 vw = *(const uint2*)(vp + (int64_t)t * Hkv * D);
+          const float v0 = bf_lo(vw.x), v1 = bf_hi(vw.x), v2 = bf_lo(vw.y), v3 = bf_hi(vw.y);
 #pragma unroll
-        for (int n = 0; n < NG; ++n) {
-          const float p = pr[n];
-          acc[n][0] += p * v0;
-          acc[n][1] += p * v1;
-          acc[n][2] += p * v2;
-          acc[n][3] += p * v3;
+          for (int n = 0; n < NG; ++n) {
+            const float p = pr[t * 2 * NG + n];
+            acc[n][0] += p * v0;
+            acc[n][1] += p * v1;
+            acc[n][2] += p * v2;
+            acc[n][3] += p * v3;
+          }
+        }
+      } else {
+        for (int t = 0; t < ntok; ++t) {
+          const uint2 vw = *(const uint2*)(vp + (int64_t)t * Hkv * D);
+          const float v0 = bf_lo(vw.x), v1 = bf_hi(vw.x), v2 = bf_lo(vw.y), v3 = bf_hi(vw.y);
+#pragma unroll
+          for (int n = 0; n < NG; ++n) {
+            const float p = pr[t * 2 * NG + n];
+            acc[n][0] += p * v0;
+            acc[n][1] += p * v1;
+            acc[n][2] += p * v2;
+            acc[n][3] += p * v3;
+          }
         }
       }
     }
-    __syncthreads();
   }
-  // ---------------- partials ----------------
-  float* pw = part + (int64_t)blockIdx.x * Hq * PS;
-  if (pv_kvh < Hkv) {
+  // ---------------- partial records ----------------
+  if (!wave_active) return;
+  if (pv_active) {
 #pragma unroll
     for (int n = 0; n < NG; ++n) {
-      const int slot = pv_kvh * NG + n;
-      *(float4*)(pw + slot * PS + 4 + pv_c) = make_float4(acc[n][0], acc[n][1], acc[n][2], acc[n][3]);
+      const int slot = my_kvh * NG + n;
+      *(float4*)(part_o + ((int64_t)slot * nwg + blockIdx.x) * D + pc) =
+          make_float4(acc[n][0], acc[n][1], acc[n][2], acc[n][3]);
     }
   }
-  if (tid < Hq) {
-    pw[tid * PS + 0] = mrun[tid];
-    pw[tid * PS + 1] = lrun[tid];
+  if (gq == 0 && kl < NG) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int kvh = kv0 + p;
+      if (kvh < Hkv) {
+        const int slot = kvh * NG + kl;
+        *(float2*)(part_ml + ((int64_t)slot * nwg + blockIdx.x) * 2) = make_float2(run_m[p], run_l[p]);
+      }
+    }
   }
 }
 
 // Merge of the split-K partials through their LogSumExp statistics.
-// Workgroup (slot, quarter): 32 channels of one head slot; its 256 threads
-// split the partial records 8 ways and the 32 channels 32 ways.
-__global__ void __launch_bounds__(256) decode_reduce_kernel(const float* __restrict__ part, int nwg,
+// Workgroup (slot, quarter) produces 32 channels of one head: thread
+// (group, c4) reads channels 4 c4 .. 4 c4 + 3 of partials group, group + 32,
+// ... with 16-byte loads, four partials in flight, then the 32 groups are
+// summed through LDS.
+__global__ void __launch_bounds__(256) decode_reduce_kernel(const float* __restrict__ part_ml,
+                                                            const float* __restrict__ part_o, int nwg,
                                                             int Hq, int NG, JlHeadMap hm,
                                                             __bf16* __restrict__ o,
                                                             float* __restrict__ lse) {
   __shared__ float red_m[256];
-  __shared__ float red_l[8], red_a[8][32];
+  __shared__ float red_l[32];
+  __shared__ float4 red_a[32][8];
   const int slot = blockIdx.x, quarter = blockIdx.y, tid = threadIdx.x;
-  const int c = tid & 31, grp = tid >> 5;
-  const int d = quarter * 32 + c;
-  // head of this slot (same ordering rule as the split kernel)
+  const int c4 = tid & 7, grp = tid >> 3;
   const int kvh = slot / NG, n = slot % NG;
   int cnt = 0, head = 0;
   for (int h = 0; h < Hq; ++h)
@@ -274,8 +310,9 @@ __global__ void __launch_bounds__(256) decode_reduce_kernel(const float* __restr
       if (cnt == n) head = h;
       ++cnt;
     }
+  const float2* ml = (const float2*)part_ml + (int64_t)slot * nwg;
   float M = -INFINITY;
-  for (int w = tid; w < nwg; w += 256) M = fmaxf(M, part[((int64_t)w * Hq + slot) * PS]);
+  for (int w = tid; w < nwg; w += 256) M = fmaxf(M, ml[w].x);
   red_m[tid] = M;
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
@@ -283,43 +320,67 @@ __global__ void __launch_bounds__(256) decode_reduce_kernel(const float* __restr
     __syncthreads();
   }
   M = red_m[0];
-  float l = 0.f, acc = 0.f;
-  for (int w = grp; w < nwg; w += 8) {
-    const float* r = part + ((int64_t)w * Hq + slot) * PS;
-    const float e = __builtin_amdgcn_exp2f(r[0] - M);
-    l += e * r[1];
-    acc += e * r[4 + d];
-  }
-  red_a[grp][c] = acc;
-  if (c == 0) red_l[grp] = l;
-  __syncthreads();
-  if (grp == 0) {
-    float A = 0.f, Lt = 0.f;
+  float l = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float* po = part_o + (int64_t)slot * nwg * D + quarter * 32 + c4 * 4;
+  int w = grp;
+  for (; w + 96 < nwg; w += 128) {
+    float2 r[4];
+    float4 v[4];
 #pragma unroll
-    for (int g2 = 0; g2 < 8; ++g2) {
-      A += red_a[g2][c];
+    for (int u = 0; u < 4; ++u) {
+      r[u] = ml[w + 32 * u];
+      v[u] = *(const float4*)(po + (int64_t)(w + 32 * u) * D);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float e = __builtin_amdgcn_exp2f(r[u].x - M);
+      l += e * r[u].y;
+      acc.x += e * v[u].x; acc.y += e * v[u].y; acc.z += e * v[u].z; acc.w += e * v[u].w;
+    }
+  }
+  for (; w < nwg; w += 32) {
+    const float2 r = ml[w];
+    const float4 v = *(const float4*)(po + (int64_t)w * D);
+    const float e = __builtin_amdgcn_exp2f(r.x - M);
+    l += e * r.y;
+    acc.x += e * v.x; acc.y += e * v.y; acc.z += e * v.z; acc.w += e * v.w;
+  }
+  red_a[grp][c4] = acc;
+  if (c4 == 0) red_l[grp] = l;
+  __syncthreads();
+  if (tid < 32) {
+    const int cc = tid >> 2, e = tid & 3;   // channel quarter*32 + 4 cc + e
+    float A = 0.f, Lt = 0.f;
+    for (int g2 = 0; g2 < 32; ++g2) {
+      const float4 a = red_a[g2][cc];
+      A += e == 0 ? a.x : e == 1 ? a.y : e == 2 ? a.z : a.w;
       Lt += red_l[g2];
     }
-    o[head * D + d] = (__bf16)(A / Lt);
-    if (lse != nullptr && quarter == 0 && c == 0) lse[head] = (M + __log2f(Lt)) * LN2;
+    o[head * D + quarter * 32 + tid] = (__bf16)(A / Lt);
+    if (lse != nullptr && quarter == 0 && tid == 0) lse[head] = (M + __log2f(Lt)) * LN2;
   }
 }
 
 }  // namespace
 
 static int decode_nsub(int64_t L) {
-  // about 1024 workgroups at long L, never fewer keys than one sub-chunk
-  int64_t n = L / (SUB * 1024);
+  // about 512 workgroups at long L, at least one 64-key sub-chunk each
+  int64_t n = L / (SUB * 512);
   if (n < 1) n = 1;
-  if (n > 8) n = 8;
+  if (n > 16) n = 16;
   return (int)n;
+}
+
+static int64_t decode_nwg(int64_t L) {
+  const int nsub = decode_nsub(L);
+  return (L + (int64_t)nsub * SUB - 1) / ((int64_t)nsub * SUB);
 }
 
 size_t jl_decode_workspace_bytes(int64_t L, int32_t Hq, int32_t d) {
   (void)d;
-  const int nsub = decode_nsub(L);
-  const int64_t nwg = (L + (int64_t)nsub * SUB - 1) / ((int64_t)nsub * SUB);
-  return (size_t)(nwg * Hq * PS * sizeof(float));
+  const int64_t nwg = decode_nwg(L);
+  return (size_t)(nwg * Hq * (2 + D) * sizeof(float));
 }
 
 hipError_t jl_launch_decode_bf16(const void* q, const void* k_cache, const void* v_cache, int64_t L,
@@ -327,15 +388,16 @@ hipError_t jl_launch_decode_bf16(const void* q, const void* k_cache, const void*
                                  const JlHeadMap& hm, int64_t w0, int32_t G, float scale,
                                  const JlFreqs& fr, void* workspace, hipStream_t st) {
   const int nsub = decode_nsub(L);
-  const int nwg = (int)((L + (int64_t)nsub * SUB - 1) / ((int64_t)nsub * SUB));
+  const int nwg = (int)decode_nwg(L);
   const int NG = Hq / Hkv;
   const int w0c = w0 > L ? (int)L : (int)w0;
-  float* part = (float*)workspace;
+  float* part_ml = (float*)workspace;
+  float* part_o = part_ml + (int64_t)nwg * Hq * 2;
   const float sl2 = scale * LOG2E;
-#define JL_DEC(NGV)                                                                           \
-  decode_split_kernel<NGV><<<nwg, NT, 0, st>>>((const __bf16*)q, (const __bf16*)k_cache,    \
-                                               (const __bf16*)v_cache, part, (int)L, Hq, Hkv, \
-                                               hm, w0c, G, nsub, sl2, fr)
+#define JL_DEC(NGV)                                                                          \
+  decode_split_kernel<NGV><<<nwg, NT, 0, st>>>((const __bf16*)q, (const __bf16*)k_cache,   \
+                                               (const __bf16*)v_cache, part_ml, part_o,     \
+                                               (int)L, Hq, Hkv, hm, w0c, G, nsub, nwg, sl2, fr)
   switch (NG) {
     case 1: JL_DEC(1); break;
     case 2: JL_DEC(2); break;
@@ -346,6 +408,6 @@ hipError_t jl_launch_decode_bf16(const void* q, const void* k_cache, const void*
 #undef JL_DEC
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  decode_reduce_kernel<<<dim3(Hq, 4), 256, 0, st>>>(part, nwg, Hq, NG, hm, (__bf16*)o, lse);
+  decode_reduce_kernel<<<dim3(Hq, 4), 256, 0, st>>>(part_ml, part_o, nwg, Hq, NG, hm, (__bf16*)o, lse);
   return hipGetLastError();
 }
