@@ -2,17 +2,23 @@
 
 One step = one bifocal prefill of a Qwen3-8B-shaped attention layer (32 q / 8
 kv heads, head_dim 128, bf16, RoPE base 1e6, w_pretrained 32768, w0 4096) at
-L = 131072 (G = 4) followed by one single-batch decode step against a bf16
-base-RoPE KV cache of L = 131072 keys (four caches are rotated so that the
-256 MB last-level cache cannot hold the one being read).
+L = 131072 (G = 4), followed by one single-batch decode step against a bf16
+base-RoPE KV cache of L = 131072 keys.  Four decode caches (2 GiB) are
+rotated so the 256 MB last-level cache cannot hold the one being read.
 
-Prints ONE JSON line.  `value` is prefill throughput on the three-pass FLOP
-basis F_3pass = 4 d Hq (L(L+1)/2 + 2 W), W = sum_i min(i+1, w0), divided by
-the measured prefill time.  The roofline object is for the dominant kernel
-(the MFMA attention kernel, timed with HIP events recorded on its stream
-immediately around its launches); decode is reported beside it against HBM
-bandwidth.  cpu_baseline times the fp64 oracle on a sample of query rows of
-the same layer.
+Prints ONE JSON line:
+  value     prefill throughput on the three-pass FLOP basis,
+            F_3pass = 4 d Hq (L(L+1)/2 + 2 W), W = sum_i min(i+1, w0),
+            over the whole prefill call (RoPE pre-pass included, inputs
+            resident in HBM), timed with HIP events on the stream;
+  roofline  the dominant kernel (the full-causal pass-2 launches): its
+            algorithmic FLOPs 4 d Hq L(L+1)/2 over its own duration, taken
+            from events the library records right around it, against the
+            MI355X dense bf16 MFMA peak; traffic comes from the committed
+            counter summary when it was measured on the current kernel source;
+  decode    sustained decode steps (KV bytes 2 L Hkv d 2 per step) and the
+            split-K kernel alone, against the HBM peak;
+  cpu_baseline  the fp64 oracle on a sample of query rows of the same layer.
 
     python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--no-cpu-baseline]
 """
@@ -21,6 +27,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -34,6 +41,11 @@ sys.path.insert(0, ROOT)
 METRIC = "bifocal prefill TFLOP/s (% MFMA peak) + decode KV GB/s at 128K, Qwen3-8B heads"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+CSRC = os.path.join(ROOT, "rope_context_extension_amd", "csrc")
+PASS2_TRAFFIC = (os.path.join(ROOT, "profiles", "prefill_pass2_traffic_qwen3_8b_L131072.txt"),
+                 os.path.join(CSRC, "jl_prefill_mfma.hip"))
+DECODE_TRAFFIC = (os.path.join(ROOT, "profiles", "decode_split_traffic_qwen3_8b_L131072.txt"),
+                  os.path.join(CSRC, "jl_decode.hip"))
 
 
 def log(*a):
@@ -41,13 +53,14 @@ def log(*a):
 
 
 def prefill_flops(L: int, Hq: int, d: int, w0: int):
+    """(F_3pass, F_causal): FLOPs of the three passes and of causal attention."""
     P = L * (L + 1) // 2                                   # causal pairs
     W = w0 * L - w0 * (w0 - 1) // 2 if L >= w0 else P      # window pairs, sum_i min(i+1, w0)
     return 4 * d * Hq * (P + 2 * W), 4 * d * Hq * P
 
 
 class HipEvents:
-    """hipEvent_t pairs through the HIP runtime that torch already loaded."""
+    """hipEvent_t handles through the HIP runtime that torch already loaded."""
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so")
@@ -64,6 +77,11 @@ class HipEvents:
             raise RuntimeError(f"hipEventCreate failed: {rc}")
         return e
 
+    def record(self, e, stream):
+        rc = self.hip.hipEventRecord(e, ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
+
     def elapsed_ms(self, a, b):
         self.hip.hipEventSynchronize(b)
         t = ctypes.c_float()
@@ -73,9 +91,30 @@ class HipEvents:
         return float(t.value)
 
 
+def read_traffic(which):
+    """HBM bytes per launch of a kernel from its committed counter summary
+    (FETCH_SIZE + WRITE_SIZE scaled by a plain copy's reading), or None when
+    the summary is missing or was taken on other kernel source."""
+    summary, source = which
+    if not os.path.exists(summary):
+        return None
+    fields = {}
+    for line in open(summary):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    src_hash = hashlib.sha256(open(source, "rb").read()).hexdigest()
+    if fields.get("kernel_source_sha256") != src_hash:
+        return None
+    try:
+        return int(float(fields["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(cfg, n_rows: int, seed: int = 1234):
-    """fp64 oracle on n_rows random query rows (all heads) of the prefill
-    layer; throughput on the same F_3pass-per-row basis as the GPU value."""
+    """fp64 oracle on n_rows random query rows (all heads) of the prefill layer;
+    throughput on the same F_3pass-per-row basis as the GPU value."""
     import torch
     import oracle
     import workloads as W
@@ -98,9 +137,10 @@ def cpu_baseline(cfg, n_rows: int, seed: int = 1234):
     dt = time.perf_counter() - t0
     d, Hq = cfg.head_dim, cfg.num_q_heads
     flops = sum(4 * d * Hq * ((i + 1) + 2 * min(i + 1, cfg.w0)) for i in rows)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
             "sample": f"{len(rows)} random query rows in [L/2, L) x {Hq} heads of the L={L} layer "
-                      f"(keys rotated for all rows up to the last); {dt:.1f} s"}
+                      f"(keys rotated up to the last sampled row), {dt:.1f} s, F_3pass-per-row basis"}
 
 
 def main():
@@ -109,11 +149,24 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=24)
+    ap.add_argument("--cpu-rows", type=int, default=96)
+    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy a 1 GiB buffer three times (counter calibration run)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel(), "copies": 3}), flush=True)
+        return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards by kv head "
-              f"or sequence with no exchange, so one GPU's figure is the per-GPU figure.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the path shards by "
+              f"kv head or by sequence with no exchange, so the one-GPU figure is the per-GPU figure.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -147,62 +200,66 @@ def main():
     kv_bytes = 2 * L * Hkv * d * 2
 
     ev = HipEvents()
-    stream = torch.cuda.current_stream(dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    lib = jl.lib()
 
-    def step(i, rec=None):
-        if rec is not None:
-            jl.lib().jl_set_profile_events(rec[0], rec[1])
+    def prefill():
         jl.prefill(q, k, v, w0=cfg.w0, w_pretrained=cfg.w_pretrained, rope_base=cfg.rope_base, out=o,
                    lse=lse, workspace=ws)
-        if rec is not None:
-            jl.lib().jl_set_profile_events(rec[2], rec[3])
+
+    def decode(i):
         kc, vc = caches[i % n_caches]
         jl.decode(qd, kc, vc, L, w0=dcfg.w0, w_pretrained=dcfg.w_pretrained, rope_base=dcfg.rope_base,
                   out=od, lse=lsed, workspace=wsd)
-        if rec is not None:
-            jl.lib().jl_set_profile_events(None, None)
 
     log(f"[bench] warmup {args.warmup}")
     for i in range(args.warmup):
-        step(i)
+        prefill()
+        decode(i)
     torch.cuda.synchronize()
 
-    recs = [tuple(ev.create() for _ in range(4)) for _ in range(args.steps)]
-    # decode alone, many back-to-back steps over the rotated caches
-    n_dec = 200
-    dec_ev = (ev.create(), ev.create())
+    # per step: [call start, attention start, after pass 2, attention end, call end] for
+    # prefill, and [start, after split-K, end] for decode
+    recs = [[ev.create() for _ in range(8)] for _ in range(args.steps)]
     log(f"[bench] timed {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, recs[i])
+        r = recs[i]
+        ev.record(r[0], stream)
+        lib.jl_set_profile_events(r[1], r[2], r[3])
+        prefill()
+        lib.jl_set_profile_events(None, None, None)
+        ev.record(r[4], stream)
+        lib.jl_set_profile_events(r[5], r[6], r[7])
+        decode(i)
+        lib.jl_set_profile_events(None, None, None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    pre_ms = [ev.elapsed_ms(r[0], r[1]) for r in recs]
-    dec_ms = [ev.elapsed_ms(r[2], r[3]) for r in recs]
-    jl.lib().jl_set_profile_events(None, None)
+    call_ms = float(np.mean([ev.elapsed_ms(r[0], r[4]) for r in recs]))
+    pass2_ms = float(np.mean([ev.elapsed_ms(r[1], r[2]) for r in recs]))
+    attn_ms = float(np.mean([ev.elapsed_ms(r[1], r[3]) for r in recs]))
+    split_us = float(np.mean([ev.elapsed_ms(r[5], r[6]) for r in recs])) * 1e3
+    dec_in_step_us = float(np.mean([ev.elapsed_ms(r[5], r[7]) for r in recs])) * 1e3
 
-    # sustained decode: n_dec steps between two events on the stream
+    # sustained decode: back-to-back steps over the rotated caches
+    e0, e1 = ev.create(), ev.create()
     torch.cuda.synchronize()
-    jl.lib().jl_set_profile_events(None, None)
-    ev.hip.hipEventRecord(dec_ev[0], ctypes.c_void_p(stream.cuda_stream))
-    for i in range(n_dec):
-        kc, vc = caches[i % n_caches]
-        jl.decode(qd, kc, vc, L, w0=dcfg.w0, w_pretrained=dcfg.w_pretrained, rope_base=dcfg.rope_base,
-                  out=od, lse=lsed, workspace=wsd)
-    ev.hip.hipEventRecord(dec_ev[1], ctypes.c_void_p(stream.cuda_stream))
-    dec_loop_us = ev.elapsed_ms(*dec_ev) * 1e3 / n_dec
+    ev.record(e0, stream)
+    for i in range(args.decode_steps):
+        decode(i)
+    ev.record(e1, stream)
+    dec_us = ev.elapsed_ms(e0, e1) * 1e3 / args.decode_steps
     torch.cuda.synchronize()
 
-    pre_kernel_ms = float(np.mean(pre_ms))
-    dec_kernel_us = float(np.mean(dec_ms)) * 1e3
-    ms_per_step = wall * 1e3 / args.steps
-    tflops = F3 / (pre_kernel_ms * 1e-3) / 1e12
-    dec_gbs = kv_bytes / (dec_loop_us * 1e-6) / 1e9
-    log(f"[bench] prefill kernel {pre_kernel_ms:.2f} ms -> {tflops:.1f} TFLOP/s (F_3pass), "
-        f"{Fc / (pre_kernel_ms * 1e-3) / 1e12:.1f} (F_causal); decode {dec_loop_us:.1f} us/step "
-        f"({dec_gbs:.0f} GB/s), in-step {dec_kernel_us:.1f} us")
+    tflops = F3 / (call_ms * 1e-3) / 1e12
+    pass2_tflops = Fc / (pass2_ms * 1e-3) / 1e12
+    dec_gbs = kv_bytes / (dec_us * 1e-6) / 1e9
+    split_gbs = kv_bytes / (split_us * 1e-6) / 1e9
+    log(f"[bench] prefill call {call_ms:.2f} ms -> {tflops:.1f} TFLOP/s (F_3pass); attention kernels "
+        f"{attn_ms:.2f} ms; pass 2 {pass2_ms:.2f} ms -> {pass2_tflops:.1f} TFLOP/s; decode {dec_us:.1f} "
+        f"us/step ({dec_gbs:.0f} GB/s), split-K {split_us:.1f} us ({split_gbs:.0f} GB/s)")
 
     out = {
         "metric": METRIC,
@@ -211,24 +268,32 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 3),
+        "ms_per_step": round(wall * 1e3 / args.steps, 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "Qwen3-8B attention layer: bifocal prefill L=131072 (G=4) + decode step at L=131072",
+        "config": {"workload": "Qwen3-8B-shaped attention layer: bifocal prefill at L=131072 (G=4) "
+                               "+ one decode step at L=131072",
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "L": L, "w0": cfg.w0,
                    "w_pretrained": cfg.w_pretrained, "rope_base": cfg.rope_base, "batch": 1},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
-        "prefill": {"kernel_ms": round(pre_kernel_ms, 3), "tflops_3pass": round(tflops, 2),
-                    "tflops_causal": round(Fc / (pre_kernel_ms * 1e-3) / 1e12, 2),
+        "roofline": {"bound": "mfma", "achieved": round(pass2_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(pass2_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": read_traffic(PASS2_TRAFFIC),
+                     "kernel": "prefill_pass_kernel<0> (pass 2: remote q/k, full causal)",
+                     "flops_per_launch": Fc, "ms_per_launch": round(pass2_ms, 3)},
+        "prefill": {"call_ms": round(call_ms, 3), "attention_ms": round(attn_ms, 3),
+                    "pass2_ms": round(pass2_ms, 3), "tflops_3pass": round(tflops, 2),
+                    "tflops_causal_basis": round(Fc / (call_ms * 1e-3) / 1e12, 2),
                     "flops_3pass": F3, "flops_causal": Fc},
-        "decode": {"us_per_step": round(dec_loop_us, 2), "us_in_step": round(dec_kernel_us, 2),
+        "decode": {"us_per_step": round(dec_us, 2), "us_in_step": round(dec_in_step_us, 2),
                    "kv_bytes": kv_bytes, "GB/s": round(dec_gbs, 1),
-                   "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
-                                "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": None}},
+                   "roofline": {"bound": "hbm", "achieved": round(split_gbs, 1), "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": round(split_gbs / PEAK_HBM_GBS, 4),
+                                "traffic": read_traffic(DECODE_TRAFFIC),
+                                "kernel": "decode_split_kernel", "us_per_launch": round(split_us, 2)},
+                   "step_frac_hbm": round(dec_gbs / PEAK_HBM_GBS, 4)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

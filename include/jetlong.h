@@ -25,7 +25,10 @@
  *   - Empty work (zero tokens, L == 0) returns JL_OK and launches nothing.
  *   - Layouts are row-major and contiguous.  RoPE pairs dimension m with
  *     m + d/2 and uses theta_m = rope_base^(-2m/d) (the rotary layout of the
- *     Qwen3 models the pages evaluate).  Angles are formed in fp64.
+ *     Qwen3 models the pages evaluate).  Angles are exact: theta_m / 2pi is
+ *     reduced mod 1 on the host into a 0.64 fixed-point fraction of a turn,
+ *     the device multiplies it by the integer position mod 2^64, and only
+ *     the remaining fraction of a turn goes through fp32 sin/cos.
  *   - softmax_scale <= 0 selects 1/sqrt(head_dim).  LSE outputs are the
  *     natural log of sum_j exp(softmax_scale * q.k) per (head, row), fp32.
  *   - q_to_kv: host int32[num_q_heads] giving the kv head of each q head, or

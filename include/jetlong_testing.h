@@ -36,13 +36,15 @@ int jl_test_rope_angles_device(const int32_t* pos, int64_t n, int32_t m, int32_t
                                double rope_base, float* cos_out, float* sin_out, void* hip_stream);
 
 /* Instrumentation for benchmarks: while set, every jl_bifocal_prefill and
-   jl_bifocal_decode call made on the calling thread records the hipEvent_t
+   jl_bifocal_decode call made on the calling thread records hipEvent_t
    `before` on its stream immediately before launching its attention
-   kernel(s) and `after` immediately after them (the RoPE pre-pass of prefill
-   stays outside).  Pass NULL, NULL to stop.  The events are the caller's;
+   kernels, `mid` (optional, may be NULL) right after its dominant kernel
+   (prefill: the full-causal pass-2 launches; decode: the split-K launch),
+   and `after` after the last of them.  The RoPE pre-pass of prefill stays
+   outside.  Pass NULL for all three to stop.  The events are the caller's;
    the library never creates or destroys them.  Returns JL_EINVAL if exactly
-   one of the two is NULL. */
-int jl_set_profile_events(void* before, void* after);
+   one of `before` and `after` is NULL. */
+int jl_set_profile_events(void* before, void* mid, void* after);
 
 #ifdef __cplusplus
 }

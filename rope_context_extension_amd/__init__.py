@@ -69,7 +69,7 @@ def lib() -> ctypes.CDLL:
         L.jl_test_rope_angles_device.argtypes = [c.c_void_p, c.c_int64, c.c_int32, c.c_int32, c.c_double,
                                                  c.c_void_p, c.c_void_p, c.c_void_p]
         L.jl_set_profile_events.restype = c.c_int
-        L.jl_set_profile_events.argtypes = [c.c_void_p, c.c_void_p]
+        L.jl_set_profile_events.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p]
         _lib = L
     return _lib
 

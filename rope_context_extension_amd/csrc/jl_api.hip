@@ -13,7 +13,7 @@
 namespace {
 
 thread_local char g_err[256] = "";
-thread_local hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
+thread_local hipEvent_t g_ev_before = nullptr, g_ev_mid = nullptr, g_ev_after = nullptr;
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -267,12 +267,15 @@ JL_EXPORT int jl_bifocal_decode(const void* q, const void* k_cache, const void* 
 
 // ------------------------------------------------------------------ test hooks
 
-JL_EXPORT int jl_set_profile_events(void* before, void* after) {
+JL_EXPORT int jl_set_profile_events(void* before, void* mid, void* after) {
   if ((before == nullptr) != (after == nullptr)) return fail(JL_EINVAL, "set both events or neither");
   g_ev_before = (hipEvent_t)before;
+  g_ev_mid = before == nullptr ? nullptr : (hipEvent_t)mid;
   g_ev_after = (hipEvent_t)after;
   return JL_OK;
 }
+
+hipEvent_t jl_profile_mid_event() { return g_ev_mid; }
 
 JL_EXPORT int jl_test_group_size_device(const int64_t* L, int64_t n, int64_t w_pretrained, int64_t* G_out,
                                         void* hip_stream) {

@@ -408,6 +408,7 @@ hipError_t jl_launch_decode_bf16(const void* q, const void* k_cache, const void*
 #undef JL_DEC
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (hipEvent_t mid = jl_profile_mid_event()) (void)hipEventRecord(mid, st);
   decode_reduce_kernel<<<dim3(Hq, 4), 256, 0, st>>>(part_ml, part_o, nwg, Hq, NG, hm, (__bf16*)o, lse);
   return hipGetLastError();
 }

@@ -102,6 +102,9 @@ hipError_t jl_launch_decode_bf16(const void* q, const void* k_cache, const void*
                                  const JlHeadMap& hm, int64_t w0, int32_t G, float scale,
                                  const JlFreqs& fr, void* workspace, hipStream_t st);
 
+// instrumentation: event to record after the dominant kernel, or nullptr
+hipEvent_t jl_profile_mid_event();
+
 // test hooks
 hipError_t jl_launch_test_group_size(const int64_t* L, int64_t n, int64_t w, int64_t* G,
                                      hipStream_t st);

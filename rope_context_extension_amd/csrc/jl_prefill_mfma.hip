@@ -638,6 +638,7 @@ hipError_t jl_launch_prefill_bf16(const JlPrefillWs& ws, void* o, float* lse, in
     prefill_pass_kernel<ROLE, true><<<nfirst, NT, 0, st>>>(A, hm, seqs, sc);            \
   } while (0)
   if (any_p2) JL_PASS(0);
+  if (hipEvent_t mid = jl_profile_mid_event()) (void)hipEventRecord(mid, st);
   if (any_p1) JL_PASS(1);
   if (any_p3) JL_PASS(2);
 #undef JL_PASS
