@@ -194,8 +194,10 @@ JL_EXPORT int jl_bifocal_prefill(const void* q, const void* k, const void* v, vo
   }
   ws.t_pad = pl.t_pad;
 
+  // the bf16 kernels take q pre-multiplied by scale * log2(e)
+  const float qscale = dtype == JL_BF16 ? scale * 1.4426950408889634f : 1.f;
   hipError_t e = jl_launch_rope_prepass(q, k, ws, (int)el, total_tokens, num_q_heads, num_kv_heads,
-                                        head_dim, pl.seqs, fr, st);
+                                        head_dim, pl.seqs, fr, qscale, st);
   if (e != hipSuccess) return hip_fail(e, "rope pre-pass launch");
   if (dtype == JL_BF16) {
     e = jl_launch_transpose_v(v, ws, pl.seqs, num_kv_heads, st);

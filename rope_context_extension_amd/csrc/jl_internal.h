@@ -79,10 +79,10 @@ struct JlPrefillWs {
 
 int64_t jl_prefill_t_pad(int64_t total_tokens);
 
-// rope pre-pass: writes qb, qr, kb, kr (elem = 2 for bf16, 4 for fp32)
+// rope pre-pass: writes qb, qr, kb, kr (elem = 2 for bf16, 4 for fp32); q is scaled by qscale
 hipError_t jl_launch_rope_prepass(const void* q, const void* k, const JlPrefillWs& ws, int elem_bytes,
                                   int64_t total_tokens, int32_t Hq, int32_t Hkv, int32_t d,
-                                  const JlSeqs& seqs, const JlFreqs& fr, hipStream_t st);
+                                  const JlSeqs& seqs, const JlFreqs& fr, float qscale, hipStream_t st);
 hipError_t jl_launch_transpose_v(const void* v, const JlPrefillWs& ws, const JlSeqs& seqs,
                                  int32_t Hkv, hipStream_t st);
 

@@ -399,7 +399,7 @@ struct PrefillArgs {
   int64_t t_pad;
   int64_t w0;
   int Hq;
-  float sl2;          // softmax scale * log2(e)
+  float sl2;          // factor from score products to log2 units (1: q arrives pre-scaled)
 };
 
 struct BlockCtx {
@@ -559,15 +559,474 @@ __global__ void __launch_bounds__(NT, 2) prefill_pass_kernel(PrefillArgs A, JlHe
   }
 }
 
+// ---- eight-wave ping-pong pass kernel (q rows >= 128) ---------------------
+// One workgroup = 8 waves = 256 query rows [r0, r0 + 256) of one head, with
+// r0 = 128 + 256 u (rows 0..127 of a sequence are the split-operand tile of
+// the kernel above).  Waves 0-3 (group A) own rows r0 .. r0 + 127 and waves
+// 4-7 (group B) rows r0 + 128 .. r0 + 255; wave w runs on SIMD w % 4, so each
+// SIMD holds one wave of each group.  Work advances in half-steps separated
+// by workgroup barriers; in every half-step one group issues matrix work
+// (S(k) = K_k Q^T and O += V_{k-1} P_{k-1}^T, 32 MFMAs per wave) while the
+// other runs the softmax of its last score tile on the vector ALU, and the
+// roles swap at the next half-step.  The MFMA pipe of a SIMD therefore always
+// has one wave feeding it while the other wave's exp / max / convert work
+// runs beside it.
+//
+// Half-step h (h = 0 .. 2n+1 for n key tiles): group g is in phase
+// ph = h - g; an even phase 2k is the matrix phase of tile k (S(k), PV(k-1)),
+// an odd phase 2k+1 the softmax of tile k.  K_k is read in half-steps 2k and
+// 2k+1 and V_k in 2k+2 and 2k+3; both are copied into LDS two half-steps
+// ahead (issued at half-step 2k - 2 for K_k, 2k for V_k), so two buffers of
+// each suffice and the copies are waited for only at odd half-steps.
+constexpr int PP_NT = 512;
+constexpr int PP_BQ = 256;
+// the four waves of group A issue every copy (group B's softmax phase stays
+// free of memory instructions)
+constexpr int PP_K_PER_WAVE = (KT_PIECES + 3) / 4;   // 5
+constexpr int PP_V_PER_WAVE = (VT_PIECES + 3) / 4;   // 5
+constexpr int BUF_RSRC_WORD3 = 0x00020000;           // raw buffer, 32-bit data format
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct PpDma {
+  uint32_t koff[PP_K_PER_WAVE];
+  uint32_t voff[PP_V_PER_WAVE];
+};
+
+__device__ inline PpDma make_pp_dma(int wave, int lane) {
+  PpDma p;
+#pragma unroll
+  for (int i = 0; i < PP_K_PER_WAVE; ++i) {
+    const int n = min((wave & 3) + 4 * i, KT_PIECES - 1);
+    const int off = n * 1024 + lane * 16;
+    const int r = off / KP, cb = off - r * KP;
+    p.koff[i] = (uint32_t)(r * 256 + (cb < 256 ? cb : 0));
+  }
+#pragma unroll
+  for (int i = 0; i < PP_V_PER_WAVE; ++i) {
+    const int n = min((wave & 3) + 4 * i, VT_PIECES - 1);
+    const int off = n * 1024 + lane * 16;
+    const int r = off / VP, cb = off - r * VP;
+    p.voff[i] = (uint32_t)(r * 128 + (cb < 128 ? cb : 0));
+  }
+  return p;
+}
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ inline int64_t uniform_i64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Copies one 16 KiB source tile (byte offset toff from the resource base)
+// into an LDS tile buffer: the per-lane offsets are fixed, the tile offset is
+// a scalar, so no vector address arithmetic is spent per tile.
+template <int PER_WAVE, int PIECES>
+__device__ inline void pp_issue(lds_char* buf, __amdgpu_buffer_rsrc_t rs, const uint32_t* off, uint32_t toff,
+                                int wave) {
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int n = min(wave + 4 * i, PIECES - 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + n * 1024), 16, off[i], (int)toff, 0, 0);
+  }
+}
+
+// Phase boundary: no instruction may be scheduled across it (the matrix and
+// softmax phases of the two groups must stay where the barriers put them).
+__device__ inline void pp_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ inline void pp_wait_copies() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ inline float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ inline float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Row state of a flash pass in the ping-pong kernel.  Scores arrive in log2
+// units (q is pre-scaled) and already shifted by -m: the first MFMA of each
+// score chain takes cb = (-m, ..., -m) as its accumulator input, so the
+// softmax exponentiates the MFMA output directly.
+struct PpState {
+  float m;      // stabiliser (log2 units), identical in lanes l and l ^ 32; -inf before any key
+  float l;      // this lane's partial sum of the bf16 probabilities
+};
+
+// (-m, ..., -m), or 0 while the row has no stabiliser
+__device__ inline f32x16 pp_bias(const PpState& st) {
+  const float nb = st.m == -INFINITY ? 0.f : -st.m;
+  f32x16 cb;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) cb[i] = nb;
+  return cb;
+}
+
+// S^T - m of one 64-key tile (same layout as score_tile): s[sb] holds keys
+// sb*32 + 16*(i/8) + 8*g + (i%8) of this lane's query row.
+__device__ inline void pp_scores(const lds_char* kt, const bf16x8* qf, const f32x16& cb, int lane, f32x16* s) {
+  const int g = lane >> 5;
+  const lds_char* base = kt + swap23(lane & 31) * KP + g * 16;
+  f32x16 a0 = cb, a1 = cb;
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb) {
+    const bf16x8 k0 = *(const __attribute__((address_space(3))) bf16x8*)(base + kb * 32);
+    const bf16x8 k1 = *(const __attribute__((address_space(3))) bf16x8*)(base + 32 * KP + kb * 32);
+    a0 = mfma(k0, qf[kb], a0);
+    a1 = mfma(k1, qf[kb], a1);
+  }
+  s[0] = a0;
+  s[1] = a1;
+}
+
+// o[db] += V^T[db*32 .. +31][keys] * P^T, P already bf16
+__device__ inline void pp_pv(const lds_char* vt, const bf16x8* p, int lane, f32x16* o) {
+  const lds_char* base = vt + (lane & 31) * VP + (lane >> 5) * 16;
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int c = sb * 4 + hh * 2;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        o[db] = mfma(*(const __attribute__((address_space(3))) bf16x8*)(base + db * 32 * VP + c * 16),
+                     p[2 * sb + hh], o[db]);
+    }
+}
+
+// p = bf16(exp2(s + shift)) for the 32 scores of a lane (SHIFT false: shift
+// is 0 and not applied); returns the sum of the bf16 values (the weights the
+// PV product uses), accumulated in two independent chains.
+template <bool SHIFT>
+__device__ inline float pp_exp_tile(const f32x16* s, float shift, bf16x8* p) {
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+  float sum[2] = {0.f, 0.f};
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      bf16x8 v;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        v[j] = (__bf16)__builtin_amdgcn_exp2f(SHIFT ? s[sb][8 * hh + j] + shift : s[sb][8 * hh + j]);
+      p[2 * sb + hh] = v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x2 pr = {v[2 * j], v[2 * j + 1]};
+        sum[hh] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum[hh], false);
+      }
+    }
+  return sum[0] + sum[1];
+}
+
+// Largest probability a tile may produce before the stabiliser is moved.
+// Any m keeps the result exact (lse = m + log2 l); the bound only keeps p,
+// l and the accumulators far from fp32 overflow.
+constexpr float PP_SUM_LIMIT = 4294967296.f;   // 2^32
+
+// Softmax of one tile without a row maximum in the common case: the scores
+// come shifted by the current stabiliser, so p = exp2(s) directly (done by
+// the caller, tsum = this lane's tile sum).  The wave takes the exact path
+// instead when a lane's tile sum exceeds 2^32 (a score more than ~27 above m)
+// or a row has no stabiliser yet: row maximum, rescale of the accumulators,
+// new stabiliser, exponentials again.
+__device__ inline void pp_settle(const f32x16* s, bf16x8* p, PpState& st, f32x16* o, float tsum) {
+  if (__builtin_expect(__all(tsum <= PP_SUM_LIMIT && st.m != -INFINITY), 1)) {
+    st.l += tsum;
+    return;
+  }
+  const float bias = st.m == -INFINITY ? 0.f : -st.m;   // what the score MFMAs subtracted
+  float mx = -INFINITY;
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sb][i]);
+  mx = pair_max(mx);
+  if (mx != -INFINITY) {
+    const float mn = fmaxf(st.m, mx - bias);             // exact row maximum so far
+    if (mn > st.m) {
+      const float a = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m - mn);
+      st.l *= a;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= a;
+      st.m = mn;
+    }
+  }
+  const float nb = st.m == -INFINITY ? 0.f : -st.m;
+  st.l += pp_exp_tile<true>(s, nb - bias, p);
+}
+
+__device__ inline void pp_softmax(const f32x16* s, bf16x8* p, PpState& st, f32x16* o) {
+  pp_settle(s, p, st, o, pp_exp_tile<false>(s, 0.f, p));
+}
+
+// Instruction order of a matrix phase with NM MFMAs, each fed by one LDS
+// read: the first DEPTH reads go out ahead, then every MFMA is followed by
+// the read DEPTH positions later, so LDS latency hides behind the MFMAs.
+template <int NM, int DEPTH>
+__device__ inline void pp_mfma_order() {
+  __builtin_amdgcn_sched_group_barrier(0x100, DEPTH, 0);   // LDS reads
+#pragma unroll
+  for (int i = 0; i < NM - DEPTH; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // LDS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, DEPTH, 0);
+}
+
+constexpr int PP_READ_DEPTH = 8;
+
+struct PpTiles {
+  lds_char* lds;
+  __amdgpu_buffer_rsrc_t rk, rv;
+  PpDma plan;
+  int t0, n, wave;
+};
+
+
+__device__ inline lds_char* pp_kbuf(const PpTiles& T, int k) { return T.lds + (k & 1) * KT_BYTES; }
+__device__ inline lds_char* pp_vbuf(const PpTiles& T, int k) {
+  return T.lds + 2 * KT_BYTES + (k & 1) * VT_BYTES;
+}
+
+// copies issued by group A at half-step 2j: K_{j+1} (if any) and V_j
+__device__ inline void pp_copies(const PpTiles& T, int j) {
+  if (j + 1 < T.n)
+    pp_issue<PP_K_PER_WAVE, KT_PIECES>(pp_kbuf(T, j + 1), T.rk, T.plan.koff,
+                                       (uint32_t)(T.t0 + j + 1) * (BK * 256), T.wave);
+  pp_issue<PP_V_PER_WAVE, VT_PIECES>(pp_vbuf(T, j), T.rv, T.plan.voff, (uint32_t)(T.t0 + j) * (D * BK * 2),
+                                     T.wave);
+}
+
+// The softmax phase runs at raised wave priority: its vector-ALU stream then
+// issues first on the SIMD, and the matrix-phase wave beside it still finds
+// the MFMA pipe's issue slots (one MFMA per 8 passes).  Without it the older
+// wave of the pair always wins and the younger group's softmax phase stretches.
+template <int KIND>
+__device__ inline void pp_softmax_tile(const PpTiles& T, int k, f32x16* s, bf16x8* p, PpState& st, f32x16* o,
+                                       const WaveRows& wr, int g) {
+  __builtin_amdgcn_s_setprio(2);
+  const int j0 = (T.t0 + k) * BK;
+  if (wave_needs_mask<KIND>(j0, wr)) mask_tile<KIND>(s, wr.myrow, j0, wr.w0, g);
+  pp_softmax(s, p, st, o);
+  __builtin_amdgcn_s_setprio(0);
+}
+
+// matrix phase of a wave: S_k (with the current stabiliser) and O += V_{k-1} P_{k-1}^T
+__device__ inline void pp_matrix(const PpTiles& T, int k, bool pv, const bf16x8* qf, const PpState& st,
+                                 f32x16* s, const bf16x8* p, f32x16* o, int lane) {
+  pp_scores(pp_kbuf(T, k), qf, pp_bias(st), lane, s);
+  if (pv) {
+    pp_pv(pp_vbuf(T, k - 1), p, lane, o);
+    pp_mfma_order<32, PP_READ_DEPTH>();
+  } else {
+    pp_mfma_order<16, PP_READ_DEPTH>();
+  }
+}
+
+// The two groups run mirrored straight-line loops with the same number of
+// barriers (half-step h: group A is in its matrix phase for even h, group B
+// for odd h).  K_k is read in half-steps 2k, 2k+1 and V_k in 2k+2, 2k+3;
+// group A copies K_{k+1} and V_k at the start of half-step 2k, two
+// half-steps ahead, into the buffers whose last readers finished at
+// half-step 2k-1, and waits for them at the end of half-step 2k+1.  Tiles in
+// which a wave has no pair (the last two causal tiles of group A, the first
+// two window tiles of group B) are computed anyway and masked to -inf, which
+// keeps the loops free of per-wave branches around register-resident state.
+template <int KIND>
+__device__ inline void pp_run(const PpTiles& T, const bf16x8* qf, PpState& st, f32x16* o, const WaveRows& wr,
+                              int lane) {
+  const int n = T.n;
+  const int g = lane >> 5;
+  f32x16 s[2];
+  bf16x8 p[4];
+  if (T.wave < 4)
+    pp_issue<PP_K_PER_WAVE, KT_PIECES>(pp_kbuf(T, 0), T.rk, T.plan.koff, (uint32_t)T.t0 * (BK * 256), T.wave);
+  pp_wait_copies();
+  pp_barrier();
+  if (T.wave < 4) {
+    pp_copies(T, 0);
+    pp_matrix(T, 0, false, qf, st, s, p, o, lane);
+    pp_barrier();
+    pp_softmax_tile<KIND>(T, 0, s, p, st, o, wr, g);
+    pp_wait_copies();
+    pp_barrier();
+    for (int j = 1; j < n; ++j) {
+      pp_copies(T, j);
+      pp_matrix(T, j, true, qf, st, s, p, o, lane);
+      pp_barrier();
+      pp_softmax_tile<KIND>(T, j, s, p, st, o, wr, g);
+      pp_wait_copies();
+      pp_barrier();
+    }
+    pp_pv(pp_vbuf(T, n - 1), p, lane, o);
+    pp_mfma_order<16, PP_READ_DEPTH>();
+    pp_barrier();
+    pp_barrier();
+  } else {
+    pp_barrier();
+    pp_matrix(T, 0, false, qf, st, s, p, o, lane);
+    pp_barrier();
+    for (int j = 1; j < n; ++j) {
+      pp_softmax_tile<KIND>(T, j - 1, s, p, st, o, wr, g);
+      pp_barrier();
+      pp_matrix(T, j, true, qf, st, s, p, o, lane);
+      pp_barrier();
+    }
+    pp_softmax_tile<KIND>(T, n - 1, s, p, st, o, wr, g);
+    pp_barrier();
+    pp_pv(pp_vbuf(T, n - 1), p, lane, o);
+    pp_mfma_order<16, PP_READ_DEPTH>();
+    pp_barrier();
+  }
+}
+
+template <int ROLE>
+__global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlHeadMap hm, JlSeqs seqs,
+                                                             JlSched sc) {
+  constexpr int KIND = ROLE == 0 ? 0 : 1;
+  __shared__ __align__(1024) char smem[2 * (KT_BYTES + VT_BYTES)];
+  int h, b, u;
+  if (!block_item<false>(sc, A.Hq, &h, &b, &u)) return;
+  // the work item is uniform over the block; say so, so that pointers built
+  // from it (buffer resources in particular) live in scalar registers
+  h = __builtin_amdgcn_readfirstlane(h);
+  b = __builtin_amdgcn_readfirstlane(b);
+  u = __builtin_amdgcn_readfirstlane(u);
+  const int L = __builtin_amdgcn_readfirstlane(seqs.len[b]);
+  const int r0 = JL_LO_ROWS + PP_BQ * (u - 1);
+  if (r0 >= L) return;
+  const bool only1 = A.w0 >= (int64_t)L;
+  const bool only2 = seqs.G[b] == 1 && !only1;
+  if (ROLE == 0 && only1) return;
+  if (ROLE == 1 && only2) return;
+  if (ROLE == 2 && (only1 || only2)) return;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 5;
+  const int kvh = __builtin_amdgcn_readfirstlane(hm.kv_of[h]);
+  const int64_t s0 = uniform_i64(seqs.start[b]);
+  const int w0 = A.w0 > (int64_t)L ? L : (int)A.w0;
+  const int iw = r0 + wave * 32;
+  const WaveRows wr{iw, iw + (lane & 31), w0};
+  const bool live = iw < L;             // waves past the end load nothing
+  const int tiles_end = min((r0 + PP_BQ + BK - 1) / BK, (L + BK - 1) / BK);
+  const int tw0 = (r0 - w0 + 1) > 0 ? (r0 - w0 + 1) / BK : 0;
+  const int64_t vtiles = seqs.vt_cols / 64;
+  const __bf16* ksrc = (ROLE == 1 ? A.kb : A.kr) + ((int64_t)kvh * A.t_pad + s0) * D;
+  const __bf16* vsrc =
+      A.vt + ((int64_t)kvh * vtiles + __builtin_amdgcn_readfirstlane(seqs.vstart[b]) / 64) * (D * 64);
+  PpTiles T;
+  lds_char* const lds = (lds_char*)smem;
+  T.lds = lds;
+  T.rk = __builtin_amdgcn_make_buffer_rsrc((void*)ksrc, 0, 0x7fffffff, BUF_RSRC_WORD3);
+  T.rv = __builtin_amdgcn_make_buffer_rsrc((void*)vsrc, 0, 0x7fffffff, BUF_RSRC_WORD3);
+  T.plan = make_pp_dma(wave, lane);
+  T.wave = wave;
+  bf16x8 qf[8];
+  if (live) {
+    load_q(qf, (ROLE == 1 ? A.qb : A.qr) + ((int64_t)h * A.t_pad + s0 + wr.myrow) * D, g);
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) qf[kb] = bf16x8{};
+  }
+  f32x16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+  PpState st{-INFINITY, 0.f};
+  T.t0 = ROLE == 0 || only1 ? 0 : tw0;
+  T.n = tiles_end - T.t0;
+  if (T.n > 0) pp_run<KIND>(T, qf, st, o, wr, lane);
+  const float l = pair_sum(st.l);
+  if (!live || wr.myrow >= L) return;
+  const int64_t ridx = (int64_t)h * A.total + s0 + wr.myrow;
+  if constexpr (ROLE != 2) {
+    const float lam = l > 0.f ? st.m + __log2f(l) : -INFINITY;
+    if ((ROLE == 0 && only2) || (ROLE == 1 && only1)) {
+      __bf16* orow = A.out + ((s0 + wr.myrow) * A.Hq + h) * D;
+      const float inv = 1.f / l;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          bf16x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[db][4 * q4 + e] * inv);
+          *(bf16x4*)(orow + db * 32 + 8 * q4 + 4 * g) = w;
+        }
+      if (A.lse != nullptr && g == 0) A.lse[ridx] = lam * LN2;
+      return;
+    }
+    float* orow = (ROLE == 0 ? A.o2 : A.o1) + ridx * D;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *(float4*)(orow + db * 32 + 8 * q4 + 4 * g) =
+            make_float4(o[db][4 * q4] * inv, o[db][4 * q4 + 1] * inv, o[db][4 * q4 + 2] * inv,
+                        o[db][4 * q4 + 3] * inv);
+    if (g == 0) (ROLE == 0 ? A.lse2 : A.lse1)[ridx] = lam;
+  } else {
+    const float lam1 = A.lse1[ridx];
+    const float lam2 = A.lse2[ridx];
+    const float lam3 = l > 0.f ? st.m + __log2f(l) : -INFINITY;
+    const float M = fmaxf(lam1, lam2);
+    const float z1 = __builtin_amdgcn_exp2f(lam1 - M);
+    const float z2 = __builtin_amdgcn_exp2f(lam2 - M);
+    const float z3 = __builtin_amdgcn_exp2f(lam3 - M);
+    const float c3 = l > 0.f ? __builtin_amdgcn_exp2f(st.m - M) : 0.f;
+    const float far = z2 - z3;
+    const float Z = z1 + fmaxf(far, 0.f);
+    const float inv = 1.f / Z;
+    const float* o1row = A.o1 + ridx * D;
+    const float* o2row = A.o2 + ridx * D;
+    __bf16* orow = A.out + ((s0 + wr.myrow) * A.Hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = db * 32 + 8 * q4 + 4 * g;
+        const float4 v1 = *(const float4*)(o1row + d0);
+        const float4 v2 = *(const float4*)(o2row + d0);
+        const float o1v[4] = {v1.x, v1.y, v1.z, v1.w};
+        const float o2v[4] = {v2.x, v2.y, v2.z, v2.w};
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float far_num = far > 0.f ? z2 * o2v[e] - c3 * o[db][4 * q4 + e] : 0.f;
+          w[e] = (__bf16)((z1 * o1v[e] + far_num) * inv);
+        }
+        *(bf16x4*)(orow + d0) = w;
+      }
+    if (A.lse != nullptr && g == 0) A.lse[ridx] = (M + __log2f(Z)) * LN2;
+  }
+}
+
 }  // namespace
 
 void jl_build_sched(const JlSeqs& seqs, const JlHeadMap& hm, int Hq, JlSched* sc) {
-  // q tiles >= 1 of every sequence, grouped into levels of equal count
+  // 256-row units of rows >= 128 of every sequence, grouped into levels of
+  // equal count
   int c[JL_MAX_SEQS], perm[JL_MAX_SEQS], n = 0;
   for (int b = 0; b < seqs.nseq; ++b) {
-    const int tiles = (seqs.len[b] + BQ - 1) / BQ;
-    if (tiles > 1) {
-      c[n] = tiles - 1;
+    const int units = seqs.len[b] > JL_LO_ROWS ? (seqs.len[b] - JL_LO_ROWS + PP_BQ - 1) / PP_BQ : 0;
+    if (units > 0) {
+      c[n] = units;
       perm[n] = b;
       ++n;
     }
@@ -620,7 +1079,8 @@ hipError_t jl_launch_prefill_bf16(const JlPrefillWs& ws, void* o, float* lse, in
   A.t_pad = ws.t_pad;
   A.w0 = w0;
   A.Hq = Hq;
-  A.sl2 = scale * LOG2E;
+  (void)scale;        // folded into q by the RoPE pre-pass (q * scale * log2 e)
+  A.sl2 = 1.f;
   bool any_p1 = false, any_p2 = false, any_p3 = false;
   for (int b = 0; b < seqs.nseq; ++b) {
     if (seqs.len[b] == 0) continue;
@@ -634,7 +1094,7 @@ hipError_t jl_launch_prefill_bf16(const JlPrefillWs& ws, void* o, float* lse, in
   const unsigned nfirst = (unsigned)(seqs.nseq * Hq);
 #define JL_PASS(ROLE)                                                                   \
   do {                                                                                  \
-    if (nblk) prefill_pass_kernel<ROLE, false><<<nblk, NT, 0, st>>>(A, hm, seqs, sc);   \
+    if (nblk) prefill_pp_kernel<ROLE><<<nblk, PP_NT, 0, st>>>(A, hm, seqs, sc);         \
     prefill_pass_kernel<ROLE, true><<<nfirst, NT, 0, st>>>(A, hm, seqs, sc);            \
   } while (0)
   if (any_p2) JL_PASS(0);

@@ -31,13 +31,15 @@ __device__ inline void st_split(T* hi, T* lo, float y) {
 }
 
 // One thread per (token, frequency m); it rotates pair (m, m + d/2) of every
-// q and k head of that token with one sin/cos evaluation per grid.
+// q and k head of that token with one sin/cos evaluation per grid.  q is
+// multiplied by qscale first (the bf16 path folds softmax scale * log2(e)
+// into q, so its score products come out in log2 units).
 template <typename T>
 __global__ void __launch_bounds__(256) rope_prepass_kernel(
     const T* __restrict__ q, const T* __restrict__ k, T* __restrict__ qb, T* __restrict__ qr,
     T* __restrict__ kb, T* __restrict__ kr, T* __restrict__ qb_lo, T* __restrict__ qr_lo,
     T* __restrict__ kb_lo, T* __restrict__ kr_lo, int64_t total, int64_t t_pad, int Hq, int Hkv,
-    int d, JlSeqs seqs, JlFreqs fr, int write_remote) {
+    int d, JlSeqs seqs, JlFreqs fr, int write_remote, float qscale) {
   const int half = d >> 1;
   const int tpb = 256 / half;               // tokens per block
   const int tl = threadIdx.x / half;
@@ -91,7 +93,7 @@ __global__ void __launch_bounds__(256) rope_prepass_kernel(
   const int64_t lrows = (int64_t)seqs.nseq * JL_LO_ROWS;
   for (int h = 0; h < Hq; ++h) {
     const T* x = q + (t * Hq + h) * d;
-    const float x1 = ld_f(x + m), x2 = ld_f(x + m + half);
+    const float x1 = ld_f(x + m) * qscale, x2 = ld_f(x + m + half) * qscale;
     T* yb = qb + ((int64_t)h * t_pad + t) * d;
     T* lb = lo ? qb_lo + ((int64_t)h * lrows + lrow) * d : nullptr;
     st_split(yb + m, lb ? lb + m : nullptr, x1 * cb - x2 * sb);
@@ -159,7 +161,7 @@ __global__ void __launch_bounds__(256) transpose_v_kernel(const __bf16* __restri
 
 hipError_t jl_launch_rope_prepass(const void* q, const void* k, const JlPrefillWs& ws, int elem_bytes,
                                   int64_t total_tokens, int32_t Hq, int32_t Hkv, int32_t d,
-                                  const JlSeqs& seqs, const JlFreqs& fr, hipStream_t st) {
+                                  const JlSeqs& seqs, const JlFreqs& fr, float qscale, hipStream_t st) {
   const int half = d / 2;
   const int tpb = 256 / half;
   int32_t max_len = 0;
@@ -173,12 +175,12 @@ hipError_t jl_launch_rope_prepass(const void* q, const void* k, const JlPrefillW
     rope_prepass_kernel<__bf16><<<grid, 256, 0, st>>>(
         (const __bf16*)q, (const __bf16*)k, (__bf16*)ws.qb, (__bf16*)ws.qr, (__bf16*)ws.kb,
         (__bf16*)ws.kr, (__bf16*)ws.qb_lo, (__bf16*)ws.qr_lo, (__bf16*)ws.kb_lo,
-        (__bf16*)ws.kr_lo, total_tokens, ws.t_pad, Hq, Hkv, d, seqs, fr, wr);
+        (__bf16*)ws.kr_lo, total_tokens, ws.t_pad, Hq, Hkv, d, seqs, fr, wr, qscale);
   } else {
     rope_prepass_kernel<float><<<grid, 256, 0, st>>>(
         (const float*)q, (const float*)k, (float*)ws.qb, (float*)ws.qr, (float*)ws.kb,
         (float*)ws.kr, nullptr, nullptr, nullptr, nullptr, total_tokens, ws.t_pad, Hq, Hkv, d,
-        seqs, fr, wr);
+        seqs, fr, wr, qscale);
   }
   return hipGetLastError();
 }
