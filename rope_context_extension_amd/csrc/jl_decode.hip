@@ -13,35 +13,48 @@
 // unnormalised partial statistics (max, sum, accumulator) per head; a second
 // kernel merges them through their LogSumExp values.
 //
-// Inside a workgroup (4 waves), per 64-key sub-chunk:
+// A workgroup has one wave per kv head (8 waves) and walks its keys in
+// 64-key sub-chunks:
 //   angles  the workgroup fills an LDS table of cos/sin(Delta_j theta_m) for
-//           the sub-chunk's remote keys (one evaluation per (key, m), shared
-//           by every kv head);
-//   scores  wave w owns kv heads 2w and 2w+1.  Per 16-key block a lane holds
-//           one key's rotary pairs (m, m + 64) for 16 values of m, rotates
-//           them in registers and feeds them as the A operand of
-//           v_mfma_f32_16x16x32_bf16 against the query block (B operand:
-//           the kv head's q heads as columns);
+//           the sub-chunk's remote keys, shared by every kv head.  A thread
+//           owns one m and every eighth key: it evaluates the first angle
+//           exactly and steps to the next key by composing with one of two
+//           fixed rotations (over 8 keys Delta moves by floor(8/G) - 8 or
+//           that plus one), one complex product per entry;
+//   scores  per 16-key block a lane holds one key's rotary pairs (m, m + 64)
+//           for 16 values of m, rotates them in registers and feeds them as
+//           the A operand of v_mfma_f32_16x16x32_bf16 against the query
+//           block (B operand: the kv head's q heads as columns);
 //   softmax the sub-chunk's scores of a head sit in 4 lanes x 16 values, so
 //           the max and sum need two lane exchanges; the result is online
-//           across sub-chunks;
-//   PV      half a wave per kv head: each lane streams 4 channels of the V
-//           rows (8 bytes per key) and accumulates the kv head's q heads
-//           with probabilities read from a wave-private LDS row.
-// The waves of a workgroup only meet at the angle-table barrier.
+//           across sub-chunks.  Probabilities go to a wave-private LDS row
+//           in bf16, key pairs packed;
+//   PV      O^T = V^T P^T on the same MFMA: a lane loads 16 bytes (8
+//           channels) of 8 consecutive keys, regroups them with byte
+//           permutes into one 8-key operand per channel, and the q heads are
+//           the columns again.
+// The K and V registers of a sub-chunk are refilled with the next
+// sub-chunk's rows as soon as they have been consumed (K after the scores,
+// V after PV), so every wave keeps a sub-chunk of loads in flight while it
+// computes.  The waves only meet at the angle-table barriers.
 #include "jl_internal.h"
 
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;
-constexpr int NT = 256;
+constexpr int NT = 512;           // one wave per kv head
 constexpr int SUB = 64;            // keys per sub-chunk
+constexpr int TRIG_STEP = NT / 64; // key stride of an angle-table thread
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
-constexpr int MAX_HQ = 64;
+constexpr int MAX_HKV = 8;
+constexpr int QPITCH = D + 8;      // bf16 elements per query row in LDS
+constexpr int TPITCH = 64 + 2;     // float2 entries per angle-table row
+constexpr int BUF_RSRC_WORD3 = 0x00020000;   // raw buffer, 32-bit data format
 
 __device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -50,14 +63,48 @@ __device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 __device__ inline uint32_t pack_bf16(float a, float b) {
-  __bf16 t[2] = {(__bf16)a, (__bf16)b};
-  return *(const uint32_t*)t;
+  const bf16x2 t = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, t);
 }
 
 // channel held in slot j of MFMA step kb by lane group gq (0..3): the lane
 // holds the rotary pairs (16 gq + x, 64 + 16 gq + x), x = 0..15.
 __device__ inline int d_of(int kb, int gq, int j) { return (kb >> 1) * 64 + 16 * gq + 8 * (kb & 1) + j; }
+
+// A wave's work is a sequence of units (sub-chunk, kv head of its pair).
+// The registers of a unit's K and V tiles are refilled with the next unit's
+// rows as soon as they have been consumed (K after the scores, V after PV),
+// so every wave keeps one unit of loads in flight while it computes.
+struct KTile { u32x4 w[4][4]; };     // [16-key block][MFMA step]: 16 B of one key
+struct VTile { u32x4 w[2][8]; };     // [32-key half][key]: 16 B (8 channels) of one key
+
+// Tile loads go through a buffer resource over the workgroup's own key rows
+// ([c_begin, min(c_end, L)) of both caches), so rows past L, and the rows of
+// the sub-chunk after the last, read as zero without touching memory;
+// `row0` is the sub-chunk's first key relative to c_begin and `lane_off` the
+// lane's byte offset inside the tile.
+__device__ inline void load_k(KTile& t, __amdgpu_buffer_rsrc_t rk, int row0, int row_bytes, int lane_off) {
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    const int off = (row0 + blk * 16) * row_bytes + lane_off;
+    // MFMA steps kb: channels (kb >> 1) * 64 + 8 (kb & 1) + 16 gq .. + 8
+    t.w[blk][0] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+    t.w[blk][1] = __builtin_amdgcn_raw_buffer_load_b128(rk, off + 16, 0, 0);
+    t.w[blk][2] = __builtin_amdgcn_raw_buffer_load_b128(rk, off + 128, 0, 0);
+    t.w[blk][3] = __builtin_amdgcn_raw_buffer_load_b128(rk, off + 144, 0, 0);
+  }
+}
+
+__device__ inline void load_v(VTile& t, __amdgpu_buffer_rsrc_t rv, int row0, int row_bytes, int lane_off) {
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int x = 0; x < 8; ++x)
+      t.w[kh][x] = __builtin_amdgcn_raw_buffer_load_b128(rv, (row0 + 32 * kh + x) * row_bytes + lane_off, 0, 0);
+}
 
 // Partial records, laid out for the merge:
 //   part_ml [Hq][nwg][2]    (max in log2 units, sum)
@@ -67,15 +114,19 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kc, const __bf16* __restrict__ vc,
     float* __restrict__ part_ml, float* __restrict__ part_o, int L, int Hq, int Hkv, JlHeadMap hm,
     int w0, int G, int nsub, int nwg, float scale_log2, JlFreqs fr) {
-  __shared__ __align__(16) __bf16 qlds[2][MAX_HQ * D];   // [variant][slot][d]; slot = kvh*NG + n
-  __shared__ __align__(16) float2 trig[SUB][64];          // cos/sin(Delta_j theta_m) of the sub-chunk
-  __shared__ __align__(16) float prob[4][SUB][2 * NG];    // wave-private probabilities [key][slot]
-  __shared__ int heads[MAX_HQ];
+  // Row pitches carry 16 bytes of padding: the 16 lanes of an LDS read pass
+  // fetch the same columns of different rows, which then fall on distinct
+  // banks.
+  __shared__ __align__(16) __bf16 qlds[2][MAX_HKV * NG * QPITCH];   // [variant][slot][d]; slot = kvh*NG + n
+  __shared__ __align__(16) float2 trig[SUB][TPITCH];                 // cos/sin(Delta_j theta_m) of the sub-chunk
+  __shared__ __align__(16) uint32_t prob[MAX_HKV][NG][SUB / 2];   // wave-private [q head][key pair]
+  __shared__ int heads[MAX_HKV * NG];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i = L - 1;
   const int c_begin = blockIdx.x * nsub * SUB;
+  const int nsc = min(nsub, (L - c_begin + SUB - 1) / SUB);     // sub-chunks holding keys: >= 1
 
   if (tid < Hq) {
     // slot s = kvh * NG + n  <->  the n-th q head (in head order) of kv head kvh
@@ -88,6 +139,27 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
       }
     heads[tid] = hh;
   }
+
+  const int kl = lane & 15, gq = lane >> 4;        // column / row index, lane group
+  const int kvh = wave;                              // this wave's kv head
+  // query column kl (columns past NG repeat real heads; their results are
+  // never stored)
+  const int qrow = (kvh * NG + (kl & (NG - 1))) * QPITCH;
+  const bool active = kvh < Hkv;
+  const int row_bytes = Hkv * D * 2;
+  const int nrows = min(L - c_begin, nsub * SUB);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)kc + (int64_t)c_begin * row_bytes), 0, nrows * row_bytes, BUF_RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)vc + (int64_t)c_begin * row_bytes), 0, nrows * row_bytes, BUF_RSRC_WORD3);
+  const int koff = kl * row_bytes + 256 * kvh + 32 * gq;       // key kl, channels 16 gq ..
+  const int voff = 8 * gq * row_bytes + 256 * kvh + 16 * kl;   // key 8 gq, channels 8 kl ..
+  KTile kt;
+  VTile vt;
+  if (active) {
+    load_k(kt, rk, 0, row_bytes, koff);
+    load_v(vt, rv, 0, row_bytes, voff);
+  }
   __syncthreads();
   {
     // the query in both variants: as given (base) and rotated by Delta_q
@@ -98,277 +170,265 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
       const float x1 = (float)qr[m], x2 = (float)qr[m + 64];
       float c, s;
       jl_rope_sincos(dq, fr.turn_frac[m], &s, &c);
-      qlds[0][slot * D + m] = qr[m];
-      qlds[0][slot * D + m + 64] = qr[m + 64];
-      qlds[1][slot * D + m] = (__bf16)(x1 * c - x2 * s);
-      qlds[1][slot * D + m + 64] = (__bf16)(x2 * c + x1 * s);
+      qlds[0][slot * QPITCH + m] = qr[m];
+      qlds[0][slot * QPITCH + m + 64] = qr[m + 64];
+      qlds[1][slot * QPITCH + m] = (__bf16)(x1 * c - x2 * s);
+      qlds[1][slot * QPITCH + m + 64] = (__bf16)(x2 * c + x1 * s);
     }
   }
 
-  const int kl = lane & 15, gq = lane >> 4;        // score layout: key, rotary group
-  const int half = lane >> 5, pc = (lane & 31) * 4; // PV layout: kv head of the pair, 4 channels
-  const int kv0 = 2 * wave;                          // this wave's kv heads: kv0, kv0 + 1
-  const bool wave_active = kv0 < Hkv;
-  const int my_kvh = kv0 + half;
-  const bool pv_active = my_kvh < Hkv;
-  float acc[NG][4];
-#pragma unroll
-  for (int n = 0; n < NG; ++n)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[n][e] = 0.f;
-  float run_m[2] = {-INFINITY, -INFINITY};   // per column n < NG of each kv head of the pair
-  float run_l[2] = {0.f, 0.f};               // (lanes with kl = n hold head n's values)
+  // angle-table stepping: thread (tk, tm) owns m = tm and keys tk + 8 r.
+  // Over 8 keys Delta = f(j) - j changes by dlo - 8 or dlo - 7, dlo =
+  // floor(8 / G): the second when (j mod G) + 8 >= (dlo + 1) G.
+  const int tm = tid & 63, tk = tid >> 6;
+  const int dlo = TRIG_STEP / G;
+  const int dlo_g = dlo * G, thr = dlo_g + G;
+  float lo_c, lo_s, hi_c, hi_s;
+  jl_rope_sincos(dlo - TRIG_STEP, fr.turn_frac[tm], &lo_s, &lo_c);
+  jl_rope_sincos(dlo - TRIG_STEP + 1, fr.turn_frac[tm], &hi_s, &hi_c);
 
-  for (int sc = 0; sc < nsub; ++sc) {
+  f32x4 acc[8];                                      // O^T: channel 32 gq + 8 e + c, q head kl
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float run_m = -INFINITY, run_l = 0.f;              // column kl (lanes kl + 16 gq)
+
+  for (int sc = 0; sc < nsc; ++sc) {
     const int c0 = c_begin + sc * SUB;
-    if (c0 >= L) break;
     __syncthreads();                           // previous sub-chunk done with trig
     const bool any_remote = (i - c0) >= w0;    // the sub-chunk's first key is the farthest
     if (any_remote) {
-      for (int e = tid; e < SUB * 64; e += NT) {
-        const int kk = e >> 6, m = e & 63;
-        const int j = min(c0 + kk, L - 1);
-        float s, c;
-        jl_rope_sincos(jl_remote_pos(j, G) - j, fr.turn_frac[m], &s, &c);
-        trig[kk][m] = make_float2(c, s);
+      const int j0 = c0 + tk;
+      const int f0 = jl_remote_pos(j0, G);
+      int rem = j0 - f0 * G;
+      float s, c;
+      jl_rope_sincos(f0 - j0, fr.turn_frac[tm], &s, &c);
+#pragma unroll
+      for (int r = 0; r < SUB / TRIG_STEP; ++r) {
+        trig[tk + TRIG_STEP * r][tm] = make_float2(c, s);
+        const int r8 = rem + TRIG_STEP;
+        const bool up = r8 >= thr;
+        rem = r8 - (up ? thr : dlo_g);
+        const float sc_ = up ? hi_c : lo_c, ss_ = up ? hi_s : lo_s;
+        const float cn = c * sc_ - s * ss_;
+        s = s * sc_ + c * ss_;
+        c = cn;
       }
     }
     __syncthreads();
-    if (!wave_active) continue;
+    if (!active) continue;
 
-    // ---------------- scores: 4 blocks of 16 keys x 2 kv heads ----------------
-    f32x4 sco[2][4];
+    // ---------------- scores: 4 blocks of 16 keys ----------------
+    f32x4 sco[4];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int kvh = min(kv0 + p, Hkv - 1);
+    for (int blk = 0; blk < 4; ++blk) {
+      const int kk = blk * 16 + kl;
+      const int j = c0 + kk;
+      const bool rem = j < L && (i - j) >= w0;
+      const bool any_rem = __any(rem);
+      const bool any_loc = __any(j < L && !rem);
+      f32x4 sr = {}, sl = {};
+      if (any_rem) {
+        uint32_t w1[8], w2[8];
+        const uint32_t* a = (const uint32_t*)&kt.w[blk][0];
+        const uint32_t* b = (const uint32_t*)&kt.w[blk][2];
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk) {
-        const int kk = blk * 16 + kl;
-        const int j = c0 + kk;
-        const int jj = j < L ? j : L - 1;
-        const bool rem = j < L && (i - j) >= w0;
-        const __bf16* kp = kc + ((int64_t)jj * Hkv + kvh) * D;
-        uint4 kw[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) kw[kb] = *(const uint4*)(kp + d_of(kb, gq, 0));
-        const bool any_rem = __any(rem);
-        const bool any_loc = __any(j < L && !rem);
-        f32x4 sr = {}, sl = {};
-        const int ncol = lane & 15;
-        if (any_rem) {
-          uint32_t w1[8], w2[8];
-          const uint32_t* a = (const uint32_t*)&kw[0];
-          const uint32_t* b = (const uint32_t*)&kw[2];
-#pragma unroll
-          for (int x2 = 0; x2 < 8; ++x2) {
-            const float4 cs = *(const float4*)&trig[kk][16 * gq + 2 * x2];   // (c, s) of two pairs
-            const float a_lo = bf_lo(a[x2]), a_hi = bf_hi(a[x2]);
-            const float b_lo = bf_lo(b[x2]), b_hi = bf_hi(b[x2]);
-            w1[x2] = pack_bf16(a_lo * cs.x - b_lo * cs.y, a_hi * cs.z - b_hi * cs.w);
-            w2[x2] = pack_bf16(b_lo * cs.x + a_lo * cs.y, b_hi * cs.z + a_hi * cs.w);
-          }
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb) {
-            const uint32_t* src = (kb < 2) ? (w1 + 4 * kb) : (w2 + 4 * (kb - 2));
-            bf16x8 bv = {};
-            if (ncol < NG) bv = *(const bf16x8*)(&qlds[1][(kvh * NG + ncol) * D + d_of(kb, gq, 0)]);
-            sr = mfma16(*(const bf16x8*)src, bv, sr);
-          }
+        for (int x2 = 0; x2 < 8; ++x2) {
+          const float4 cs = *(const float4*)&trig[kk][16 * gq + 2 * x2];   // (c, s) of two pairs
+          const float a_lo = bf_lo(a[x2]), a_hi = bf_hi(a[x2]);
+          const float b_lo = bf_lo(b[x2]), b_hi = bf_hi(b[x2]);
+          w1[x2] = pack_bf16(a_lo * cs.x - b_lo * cs.y, a_hi * cs.z - b_hi * cs.w);
+          w2[x2] = pack_bf16(b_lo * cs.x + a_lo * cs.y, b_hi * cs.z + a_hi * cs.w);
         }
-        if (any_loc) {
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb) {
-            bf16x8 bv = {};
-            if (ncol < NG) bv = *(const bf16x8*)(&qlds[0][(kvh * NG + ncol) * D + d_of(kb, gq, 0)]);
-            sl = mfma16(*(const bf16x8*)&kw[kb], bv, sl);
-          }
-        }
-        // lane holds S^T[key blk*16 + 4 gq + e][column kl]
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int jk = c0 + blk * 16 + 4 * gq + e;
-          const float v = ((i - jk) >= w0 ? sr[e] : sl[e]) * scale_log2;
-          sco[p][blk][e] = jk < L ? v : -INFINITY;
+        for (int kb = 0; kb < 4; ++kb) {
+          const uint32_t* src = (kb < 2) ? (w1 + 4 * kb) : (w2 + 4 * (kb - 2));
+          const bf16x8 bv = *(const bf16x8*)(&qlds[1][qrow + d_of(kb, gq, 0)]);
+          sr = mfma16(*(const bf16x8*)src, bv, sr);
         }
       }
+      if (any_loc) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const bf16x8 bv = *(const bf16x8*)(&qlds[0][qrow + d_of(kb, gq, 0)]);
+          sl = mfma16(__builtin_bit_cast(bf16x8, kt.w[blk][kb]), bv, sl);
+        }
+      }
+      // lane holds S^T[key blk*16 + 4 gq + e][column kl]
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int jk = c0 + blk * 16 + 4 * gq + e;
+        const float v = ((i - jk) >= w0 ? sr[e] : sl[e]) * scale_log2;
+        sco[blk][e] = jk < L ? v : -INFINITY;
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // K registers free: the next sub-chunk's keys
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(kt, rk, (sc + 1) * SUB, row_bytes, koff);
+    __builtin_amdgcn_sched_barrier(0);
+
     // ---------------- softmax per column (q head) over the 64 keys ----------------
-    // column kl of kv head kv0 + p: lanes kl + 16 gq, values sco[p][0..3][0..3]
+    float mx = -INFINITY;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      float mx = -INFINITY;
+    for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk)
+      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sco[blk][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mn = fmaxf(run_m, mx);            // finite: every sub-chunk has a valid key
+    const float alpha = __builtin_amdgcn_exp2f(run_m - mn);
+    float sum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sco[p][blk][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mn = fmaxf(run_m[p], mx);         // finite: every sub-chunk has a valid key
-      const float alpha = __builtin_amdgcn_exp2f(run_m[p] - mn);
-      float sum = 0.f;
+    for (int blk = 0; blk < 4; ++blk) {
+      float pr[4];
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float pr = __builtin_amdgcn_exp2f(sco[p][blk][e] - mn);
-          sum += pr;
-          if (kl < NG) prob[wave][blk * 16 + 4 * gq + e][p * NG + kl] = pr;
-        }
-      sum += __shfl_xor(sum, 16, 64);
-      sum += __shfl_xor(sum, 32, 64);
-      run_l[p] = run_l[p] * alpha + sum;
-      run_m[p] = mn;
-      // rescale the PV accumulators of this kv head's columns: lanes of half p
-      // own the accumulators, column n's alpha lives in lane n
-#pragma unroll
-      for (int n = 0; n < NG; ++n) {
-        const float a_n = __shfl(alpha, n, 64);
-        if (half == p) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[n][e] *= a_n;
-        }
+      for (int e = 0; e < 4; ++e) {
+        pr[e] = __builtin_amdgcn_exp2f(sco[blk][e] - mn);
+        sum += pr[e];
       }
+      if (kl < NG)
+        *(uint2*)&prob[wave][kl][blk * 8 + 2 * gq] = make_uint2(pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3]));
     }
+    sum += __shfl_xor(sum, 16, 64);
+    sum += __shfl_xor(sum, 32, 64);
+    run_l = run_l * alpha + sum;
+    run_m = mn;
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_s_waitcnt(0xc07f);              // lgkmcnt(0): prob rows written
-    // ---------------- PV: half-wave per kv head, 4 channels per lane ----------------
-    if (pv_active) {
-      const int ntok = min(SUB, L - c0);
-      const __bf16* vp = vc + ((int64_t)c0 * Hkv + my_kvh) * D + pc;
-      const float* pr = &prob[wave][0][half * NG];
-      if (ntok == SUB) {
-#pragma unroll 16
-        for (int t = 0; t < SUB; ++t) {
-          const uint2 vw = *(const uint2*)(vp + (int64_t)t * Hkv * D);
-          const float v0 = bf_lo(vw.x), v1 = bf_hi(vw.x), v2 = bf_lo(vw.y), v3 = bf_hi(vw.y);
+
+    // ---------------- PV: O^T += V^T P^T, 32 keys per MFMA ----------------
+    // A operand (row kl, keys 8 gq .. 8 gq + 7): channel 8 kl + c of 8 keys;
+    // B operand (column kl): probabilities of q head kl for the same keys.
 #pragma unroll
-          for (int n = 0; n < NG; ++n) {
-            const float p = pr[t * 2 * NG + n];
-            acc[n][0] += p * v0;
-            acc[n][1] += p * v1;
-            acc[n][2] += p * v2;
-            acc[n][3] += p * v3;
-          }
-        }
-      } else {
-        for (int t = 0; t < ntok; ++t) {
-          const uint2 vw = *(const uint2*)(vp + (int64_t)t * Hkv * D);
-          const float v0 = bf_lo(vw.x), v1 = bf_hi(vw.x), v2 = bf_lo(vw.y), v3 = bf_hi(vw.y);
+    for (int c = 0; c < 8; ++c) acc[c] *= alpha;
 #pragma unroll
-          for (int n = 0; n < NG; ++n) {
-            const float p = pr[t * 2 * NG + n];
-            acc[n][0] += p * v0;
-            acc[n][1] += p * v1;
-            acc[n][2] += p * v2;
-            acc[n][3] += p * v3;
-          }
+    for (int kh = 0; kh < 2; ++kh) {
+      const bf16x8 pb = *(const bf16x8*)&prob[wave][kl & (NG - 1)][16 * kh + 4 * gq];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        u32x4 lo, hi;       // channels 8 kl + 2 w and 8 kl + 2 w + 1, keys in pairs
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          lo[u] = __builtin_amdgcn_perm(vt.w[kh][2 * u + 1][w], vt.w[kh][2 * u][w], 0x05040100u);
+          hi[u] = __builtin_amdgcn_perm(vt.w[kh][2 * u + 1][w], vt.w[kh][2 * u][w], 0x07060302u);
         }
+        acc[2 * w] = mfma16(__builtin_bit_cast(bf16x8, lo), pb, acc[2 * w]);
+        acc[2 * w + 1] = mfma16(__builtin_bit_cast(bf16x8, hi), pb, acc[2 * w + 1]);
       }
     }
+    // V registers free: the next sub-chunk's values
+    __builtin_amdgcn_sched_barrier(0);
+    load_v(vt, rv, (sc + 1) * SUB, row_bytes, voff);
+    __builtin_amdgcn_sched_barrier(0);
   }
   // ---------------- partial records ----------------
-  if (!wave_active) return;
-  if (pv_active) {
+  if (!active || kl >= NG) return;
+  // output row 4 gq + e of MFMA c is channel 8 (4 gq + e) + c
+  float* dst = part_o + ((int64_t)(kvh * NG + kl) * nwg + blockIdx.x) * D + 32 * gq;
 #pragma unroll
-    for (int n = 0; n < NG; ++n) {
-      const int slot = my_kvh * NG + n;
-      *(float4*)(part_o + ((int64_t)slot * nwg + blockIdx.x) * D + pc) =
-          make_float4(acc[n][0], acc[n][1], acc[n][2], acc[n][3]);
-    }
+  for (int e = 0; e < 4; ++e) {
+    *(float4*)(dst + 8 * e) = make_float4(acc[0][e], acc[1][e], acc[2][e], acc[3][e]);
+    *(float4*)(dst + 8 * e + 4) = make_float4(acc[4][e], acc[5][e], acc[6][e], acc[7][e]);
   }
-  if (gq == 0 && kl < NG) {
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int kvh = kv0 + p;
-      if (kvh < Hkv) {
-        const int slot = kvh * NG + kl;
-        *(float2*)(part_ml + ((int64_t)slot * nwg + blockIdx.x) * 2) = make_float2(run_m[p], run_l[p]);
-      }
-    }
-  }
+  if (gq == 0)
+    *(float2*)(part_ml + ((int64_t)(kvh * NG + kl) * nwg + blockIdx.x) * 2) = make_float2(run_m, run_l);
 }
 
 // Merge of the split-K partials through their LogSumExp statistics.
-// Workgroup (slot, quarter) produces 32 channels of one head: thread
-// (group, c4) reads channels 4 c4 .. 4 c4 + 3 of partials group, group + 32,
-// ... with 16-byte loads, four partials in flight, then the 32 groups are
-// summed through LDS.
+// Workgroup (slot, part) produces 16 channels of one head: thread (grp,
+// c4) takes partials grp, grp + 64, ... (eight loads in flight per round,
+// 16 bytes of channels each) with an online max.  The 64 groups then meet
+// through lane exchanges: the common max over one lane per group, the
+// weighted sums over the 16 groups of a wave, and the 4 waves through LDS.
+constexpr int RED_GROUPS = 64;
+constexpr int RED_DEPTH = 8;
+
 __global__ void __launch_bounds__(256) decode_reduce_kernel(const float* __restrict__ part_ml,
                                                             const float* __restrict__ part_o, int nwg,
                                                             int Hq, int NG, JlHeadMap hm,
                                                             __bf16* __restrict__ o,
                                                             float* __restrict__ lse) {
-  __shared__ float red_m[256];
-  __shared__ float red_l[32];
-  __shared__ float4 red_a[32][8];
-  const int slot = blockIdx.x, quarter = blockIdx.y, tid = threadIdx.x;
-  const int c4 = tid & 7, grp = tid >> 3;
-  const int kvh = slot / NG, n = slot % NG;
-  int cnt = 0, head = 0;
-  for (int h = 0; h < Hq; ++h)
-    if (hm.kv_of[h] == kvh) {
-      if (cnt == n) head = h;
-      ++cnt;
-    }
+  __shared__ float red_m[RED_GROUPS];
+  __shared__ float red_l[4];
+  __shared__ float4 red_a[4][4];
+  const int slot = blockIdx.x, part = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int c4 = tid & 3, grp = tid >> 2;
   const float2* ml = (const float2*)part_ml + (int64_t)slot * nwg;
-  float M = -INFINITY;
-  for (int w = tid; w < nwg; w += 256) M = fmaxf(M, ml[w].x);
-  red_m[tid] = M;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) red_m[tid] = fmaxf(red_m[tid], red_m[tid + s]);
-    __syncthreads();
-  }
-  M = red_m[0];
-  float l = 0.f;
+  const float* po = part_o + (int64_t)slot * nwg * D + part * 16 + c4 * 4;
+  float m = -INFINITY, l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  const float* po = part_o + (int64_t)slot * nwg * D + quarter * 32 + c4 * 4;
-  int w = grp;
-  for (; w + 96 < nwg; w += 128) {
-    float2 r[4];
-    float4 v[4];
+  for (int wb = grp; wb < nwg; wb += RED_GROUPS * RED_DEPTH) {
+    float2 r[RED_DEPTH];
+    float4 v[RED_DEPTH];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      r[u] = ml[w + 32 * u];
-      v[u] = *(const float4*)(po + (int64_t)(w + 32 * u) * D);
+    for (int u = 0; u < RED_DEPTH; ++u) {
+      const int w = wb + RED_GROUPS * u;
+      r[u] = w < nwg ? ml[w] : make_float2(-INFINITY, 0.f);
+      v[u] = w < nwg ? *(const float4*)(po + (int64_t)w * D) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    float mu = m;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float e = __builtin_amdgcn_exp2f(r[u].x - M);
+    for (int u = 0; u < RED_DEPTH; ++u) mu = fmaxf(mu, r[u].x);
+    const float sc = __builtin_amdgcn_exp2f(m - mu);     // partial w = grp exists: mu is finite
+    l *= sc;
+    acc.x *= sc; acc.y *= sc; acc.z *= sc; acc.w *= sc;
+#pragma unroll
+    for (int u = 0; u < RED_DEPTH; ++u) {
+      const float e = __builtin_amdgcn_exp2f(r[u].x - mu);
       l += e * r[u].y;
       acc.x += e * v[u].x; acc.y += e * v[u].y; acc.z += e * v[u].z; acc.w += e * v[u].w;
     }
+    m = mu;
   }
-  for (; w < nwg; w += 32) {
-    const float2 r = ml[w];
-    const float4 v = *(const float4*)(po + (int64_t)w * D);
-    const float e = __builtin_amdgcn_exp2f(r.x - M);
-    l += e * r.y;
-    acc.x += e * v.x; acc.y += e * v.y; acc.z += e * v.z; acc.w += e * v.w;
-  }
-  red_a[grp][c4] = acc;
-  if (c4 == 0) red_l[grp] = l;
+  if (c4 == 0) red_m[grp] = m;
   __syncthreads();
-  if (tid < 32) {
-    const int cc = tid >> 2, e = tid & 3;   // channel quarter*32 + 4 cc + e
+  float M = red_m[lane];                       // group 0 holds partial 0: M is finite
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  const float wt = __builtin_amdgcn_exp2f(m - M);   // 0 for groups without partials
+  l *= wt;
+  acc.x *= wt; acc.y *= wt; acc.z *= wt; acc.w *= wt;
+#pragma unroll
+  for (int off = 4; off <= 32; off <<= 1) {      // the wave's 16 groups (lane bits 2..5)
+    l += __shfl_xor(l, off, 64);
+    acc.x += __shfl_xor(acc.x, off, 64);
+    acc.y += __shfl_xor(acc.y, off, 64);
+    acc.z += __shfl_xor(acc.z, off, 64);
+    acc.w += __shfl_xor(acc.w, off, 64);
+  }
+  if (lane < 4) red_a[wave][lane] = acc;
+  if (lane == 0) red_l[wave] = l;
+  __syncthreads();
+  if (tid < 16) {
+    const int cc = tid >> 2, e = tid & 3;   // channel part*16 + 4 cc + e
     float A = 0.f, Lt = 0.f;
-    for (int g2 = 0; g2 < 32; ++g2) {
-      const float4 a = red_a[g2][cc];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float4 a = red_a[w][cc];
       A += e == 0 ? a.x : e == 1 ? a.y : e == 2 ? a.z : a.w;
-      Lt += red_l[g2];
+      Lt += red_l[w];
     }
-    o[head * D + quarter * 32 + tid] = (__bf16)(A / Lt);
-    if (lse != nullptr && quarter == 0 && tid == 0) lse[head] = (M + __log2f(Lt)) * LN2;
+    const int kvh = slot / NG, n = slot % NG;
+    int cnt = 0, head = 0;
+    for (int h = 0; h < Hq; ++h)
+      if (hm.kv_of[h] == kvh) {
+        if (cnt == n) head = h;
+        ++cnt;
+      }
+    o[head * D + part * 16 + tid] = (__bf16)(A / Lt);
+    if (lse != nullptr && part == 0 && tid == 0) lse[head] = (M + __log2f(Lt)) * LN2;
   }
 }
 
 }  // namespace
 
 static int decode_nsub(int64_t L) {
-  // about 512 workgroups at long L, at least one 64-key sub-chunk each
-  int64_t n = L / (SUB * 512);
+  // about one workgroup per compute unit at long L, at least one 64-key
+  // sub-chunk each
+  int64_t n = L / (SUB * 256);
   if (n < 1) n = 1;
-  if (n > 16) n = 16;
+  if (n > 32) n = 32;
   return (int)n;
 }
 
@@ -409,6 +469,6 @@ hipError_t jl_launch_decode_bf16(const void* q, const void* k_cache, const void*
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (hipEvent_t mid = jl_profile_mid_event()) (void)hipEventRecord(mid, st);
-  decode_reduce_kernel<<<dim3(Hq, 4), 256, 0, st>>>(part_ml, part_o, nwg, Hq, NG, hm, (__bf16*)o, lse);
+  decode_reduce_kernel<<<dim3(Hq, 8), 256, 0, st>>>(part_ml, part_o, nwg, Hq, NG, hm, (__bf16*)o, lse);
   return hipGetLastError();
 }

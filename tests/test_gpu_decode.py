@@ -55,6 +55,9 @@ def test_qwen3_8b_decode_lengths(L):
     (1000, 16, 2, 100, 2000),    # G = 1
     (4097, 2, 2, 1, 1024),       # w0 = 1
     (5000, 32, 8, 333, 1200),    # G = 5, ragged
+    (777, 3, 3, 100, 256),       # odd kv-head count: a wave with one kv head
+    (129, 8, 1, 20, 40),         # one kv head, 8 q heads per kv head, G = 4
+    (2000, 64, 8, 200, 600),     # 64 q heads, G = 4
 ])
 def test_small_decode_cases(L, Hq, Hkv, w0, wpt):
     jl, torch = gpu_or_skip()
