@@ -34,9 +34,12 @@
 //           permutes into one 8-key operand per channel, and the q heads are
 //           the columns again.
 // The K and V registers of a sub-chunk are refilled with the next
-// sub-chunk's rows as soon as they have been consumed (K after the scores,
-// V after PV), so every wave keeps a sub-chunk of loads in flight while it
-// computes.  The waves only meet at the angle-table barriers.
+// sub-chunk's rows as soon as they have been consumed (K per 16-key block
+// of the scores, V per 32-key half of PV), so every wave keeps about a
+// sub-chunk of loads in flight while it computes, issued a few at a time.
+// The angle table is double-buffered; the waves synchronise only through a
+// workgroup counter of finished fills, so a wave waits for the others'
+// share of the next table, never for their attention work.
 #include "jl_internal.h"
 
 namespace {
@@ -48,7 +51,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int D = 128;
 constexpr int NT = 512;           // one wave per kv head
 constexpr int SUB = 64;            // keys per sub-chunk
-constexpr int TRIG_STEP = NT / 64; // key stride of an angle-table thread
+constexpr int NWAVES = NT / 64;
+constexpr int TRIG_STEP = NWAVES;  // key stride of an angle-table thread
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr int MAX_HKV = 8;
@@ -70,6 +74,20 @@ __device__ inline uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, t);
 }
 
+// The lane's index, produced where it is used: addresses built from it are
+// not kept in a register across the key loop (they would only be needed
+// once per sub-chunk, and the register file is full).
+__device__ inline int lane_now() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// x.lo * y.lo + x.hi * y.hi in fp32 (v_dot2_f32_bf16)
+__device__ inline float dot2(bf16x2 x, uint32_t y) {
+  return __builtin_amdgcn_fdot2_f32_bf16(x, __builtin_bit_cast(bf16x2, y), 0.f, false);
+}
+
 // channel held in slot j of MFMA step kb by lane group gq (0..3): the lane
 // holds the rotary pairs (16 gq + x, 64 + 16 gq + x), x = 0..15.
 __device__ inline int d_of(int kb, int gq, int j) { return (kb >> 1) * 64 + 16 * gq + 8 * (kb & 1) + j; }
@@ -86,24 +104,55 @@ struct VTile { u32x4 w[2][8]; };     // [32-key half][key]: 16 B (8 channels) of
 // the sub-chunk after the last, read as zero without touching memory;
 // `row0` is the sub-chunk's first key relative to c_begin and `lane_off` the
 // lane's byte offset inside the tile.
-__device__ inline void load_k(KTile& t, __amdgpu_buffer_rsrc_t rk, int row0, int row_bytes, int lane_off) {
-#pragma unroll
-  for (int blk = 0; blk < 4; ++blk) {
-    const int off = (row0 + blk * 16) * row_bytes + lane_off;
-    // MFMA steps kb: channels (kb >> 1) * 64 + 8 (kb & 1) + 16 gq .. + 8
-    t.w[blk][0] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
-    t.w[blk][1] = __builtin_amdgcn_raw_buffer_load_b128(rk, off + 16, 0, 0);
-    t.w[blk][2] = __builtin_amdgcn_raw_buffer_load_b128(rk, off + 128, 0, 0);
-    t.w[blk][3] = __builtin_amdgcn_raw_buffer_load_b128(rk, off + 144, 0, 0);
-  }
+__device__ inline void load_k_blk(KTile& t, int blk, __amdgpu_buffer_rsrc_t rk, int row0, int row_bytes,
+                                  int lane_off) {
+  const int off = (row0 + blk * 16) * row_bytes + lane_off;
+  // MFMA steps kb: channels (kb >> 1) * 64 + 8 (kb & 1) + 16 gq .. + 8
+  t.w[blk][0] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+  t.w[blk][1] = __builtin_amdgcn_raw_buffer_load_b128(rk, off + 16, 0, 0);
+  t.w[blk][2] = __builtin_amdgcn_raw_buffer_load_b128(rk, off + 128, 0, 0);
+  t.w[blk][3] = __builtin_amdgcn_raw_buffer_load_b128(rk, off + 144, 0, 0);
 }
 
-__device__ inline void load_v(VTile& t, __amdgpu_buffer_rsrc_t rv, int row0, int row_bytes, int lane_off) {
+__device__ inline void load_v_half(VTile& t, int kh, __amdgpu_buffer_rsrc_t rv, int row0, int row_bytes,
+                                   int lane_off) {
 #pragma unroll
-  for (int kh = 0; kh < 2; ++kh)
+  for (int x = 0; x < 8; ++x)
+    t.w[kh][x] = __builtin_amdgcn_raw_buffer_load_b128(rv, (row0 + 32 * kh + x) * row_bytes + lane_off, 0, 0);
+}
+
+// Waits until the workgroup counter reaches `target`.  Every wave adds one
+// per sub-chunk whatever it computes, so the count always arrives; the bound
+// only keeps a broken invariant from hanging the device (the caller then
+// poisons its results).
+__device__ inline bool wait_count(const int* counter, int target) {
+  for (int it = 0; it < (1 << 22); ++it) {
+    const int v = __hip_atomic_load(counter, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (__builtin_amdgcn_readfirstlane(v) >= target) return true;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return false;
+}
+
+// Thread (tk, tm)'s part of a sub-chunk's angle table: m = tm, keys tk + 8 r,
+// stepping the thread's angle chain (advanced to the next sub-chunk).
+__device__ inline void fill_trig(uint2 (*tb)[TPITCH], float4* chain, float4 st, int tid, int tm, int tk,
+                                 int thr, int dlo_g) {
+  const float4 ch = chain[tid];
+  float c = ch.x, s = ch.y;
+  int rem = __float_as_int(ch.z);
 #pragma unroll
-    for (int x = 0; x < 8; ++x)
-      t.w[kh][x] = __builtin_amdgcn_raw_buffer_load_b128(rv, (row0 + 32 * kh + x) * row_bytes + lane_off, 0, 0);
+  for (int r = 0; r < SUB / TRIG_STEP; ++r) {
+    tb[tk + TRIG_STEP * r][tm] = make_uint2(pack_bf16(c, -s), pack_bf16(s, c));
+    const int r8 = rem + TRIG_STEP;
+    const bool up = r8 >= thr;
+    rem = r8 - (up ? thr : dlo_g);
+    const float sc_ = up ? st.z : st.x, ss_ = up ? st.w : st.y;
+    const float cn = c * sc_ - s * ss_;
+    s = s * sc_ + c * ss_;
+    c = cn;
+  }
+  chain[tid] = make_float4(c, s, __int_as_float(rem), 0.f);
 }
 
 // Partial records, laid out for the merge:
@@ -118,9 +167,19 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
   // fetch the same columns of different rows, which then fall on distinct
   // banks.
   __shared__ __align__(16) __bf16 qlds[2][MAX_HKV * NG * QPITCH];   // [variant][slot][d]; slot = kvh*NG + n
-  __shared__ __align__(16) float2 trig[SUB][TPITCH];                 // cos/sin(Delta_j theta_m) of the sub-chunk
+  // angle table of the sub-chunk: per (key, m) the bf16 pairs (c, -s) and
+  // (s, c) of c, s = cos, sin(Delta_j theta_m), the two dot products of a
+  // rotation
+  __shared__ __align__(16) uint2 trig[2][SUB][TPITCH];   // double-buffered: [sub-chunk & 1]
   __shared__ __align__(16) uint32_t prob[MAX_HKV][NG][SUB / 2];   // wave-private [q head][key pair]
   __shared__ int heads[MAX_HKV * NG];
+  // per m the two angle-table step rotations, per thread its angle chain
+  // (cos, sin, j mod G) at its next key.  Both live in LDS so that no memory
+  // load but the tile prefetches sits in the key loop: the load counter is
+  // in order, and waiting on anything else would wait on the prefetches too.
+  __shared__ float4 steps[64];
+  __shared__ float4 chain[NT];
+  __shared__ int tables_done;            // angle-table fills finished, one per wave and sub-chunk
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -157,8 +216,10 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
   KTile kt;
   VTile vt;
   if (active) {
-    load_k(kt, rk, 0, row_bytes, koff);
-    load_v(vt, rv, 0, row_bytes, voff);
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) load_k_blk(kt, blk, rk, 0, row_bytes, koff);
+    load_v_half(vt, 0, rv, 0, row_bytes, voff);
+    load_v_half(vt, 1, rv, 0, row_bytes, voff);
   }
   __syncthreads();
   {
@@ -177,45 +238,45 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
     }
   }
 
-  // angle-table stepping: thread (tk, tm) owns m = tm and keys tk + 8 r.
-  // Over 8 keys Delta = f(j) - j changes by dlo - 8 or dlo - 7, dlo =
-  // floor(8 / G): the second when (j mod G) + 8 >= (dlo + 1) G.
+  // angle-table stepping: thread (tk, tm) owns m = tm and keys tk + 8 r of
+  // every sub-chunk.  Over 8 keys Delta = f(j) - j changes by dlo - 8 or
+  // dlo - 7, dlo = floor(8 / G): the second when (j mod G) + 8 >= (dlo + 1) G.
+  // The first angle is exact; each later one is the previous composed with
+  // the step (one complex product, about an fp32 ulp each).
   const int tm = tid & 63, tk = tid >> 6;
   const int dlo = TRIG_STEP / G;
   const int dlo_g = dlo * G, thr = dlo_g + G;
-  float lo_c, lo_s, hi_c, hi_s;
-  jl_rope_sincos(dlo - TRIG_STEP, fr.turn_frac[tm], &lo_s, &lo_c);
-  jl_rope_sincos(dlo - TRIG_STEP + 1, fr.turn_frac[tm], &hi_s, &hi_c);
+  {
+    const uint64_t tf = fr.turn_frac[tm];
+    float4 st;   // (cos, sin) of both steps for m = tm
+    jl_rope_sincos(dlo - TRIG_STEP, tf, &st.y, &st.x);
+    jl_rope_sincos(dlo - TRIG_STEP + 1, tf, &st.w, &st.z);
+    steps[tm] = st;    // every wave writes the same values
+    const int j0 = c_begin + tk;
+    const int f0 = jl_remote_pos(j0, G);
+    float s, c;
+    jl_rope_sincos(f0 - j0, tf, &s, &c);
+    chain[tid] = make_float4(c, s, __int_as_float(j0 - f0 * G), 0.f);
+    if ((i - c_begin) >= w0) fill_trig(trig[0], chain, st, tid, tm, tk, thr, dlo_g);
+  }
 
   f32x4 acc[8];                                      // O^T: channel 32 gq + 8 e + c, q head kl
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   float run_m = -INFINITY, run_l = 0.f;              // column kl (lanes kl + 16 gq)
+  if (tid == 0) tables_done = 0;
+  __syncthreads();
+  bool in_time = true;
 
   for (int sc = 0; sc < nsc; ++sc) {
     const int c0 = c_begin + sc * SUB;
-    __syncthreads();                           // previous sub-chunk done with trig
-    const bool any_remote = (i - c0) >= w0;    // the sub-chunk's first key is the farthest
-    if (any_remote) {
-      const int j0 = c0 + tk;
-      const int f0 = jl_remote_pos(j0, G);
-      int rem = j0 - f0 * G;
-      float s, c;
-      jl_rope_sincos(f0 - j0, fr.turn_frac[tm], &s, &c);
-#pragma unroll
-      for (int r = 0; r < SUB / TRIG_STEP; ++r) {
-        trig[tk + TRIG_STEP * r][tm] = make_float2(c, s);
-        const int r8 = rem + TRIG_STEP;
-        const bool up = r8 >= thr;
-        rem = r8 - (up ? thr : dlo_g);
-        const float sc_ = up ? hi_c : lo_c, ss_ = up ? hi_s : lo_s;
-        const float cn = c * sc_ - s * ss_;
-        s = s * sc_ + c * ss_;
-        c = cn;
-      }
-    }
-    __syncthreads();
-    if (!active) continue;
+    // sub-chunk sc's table is complete once every wave has counted its fill
+    // of it (made in the previous sub-chunk)
+    if (sc > 0) in_time &= wait_count(&tables_done, NWAVES * sc);
+    const bool fill_next = sc + 1 < nsc && (i - (c0 + SUB)) >= w0;
+    const uint2 (*tb)[TPITCH] = trig[sc & 1];
+    float alpha = 1.f;
+    if (active) {
 
     // ---------------- scores: 4 blocks of 16 keys ----------------
     f32x4 sco[4];
@@ -228,22 +289,26 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
       const bool any_loc = __any(j < L && !rem);
       f32x4 sr = {}, sl = {};
       if (any_rem) {
-        uint32_t w1[8], w2[8];
         const uint32_t* a = (const uint32_t*)&kt.w[blk][0];
         const uint32_t* b = (const uint32_t*)&kt.w[blk][2];
+        // pairs 8 h .. 8 h + 7 of the lane feed MFMA steps kb = h (rotated
+        // k[m]) and kb = 2 + h (rotated k[m + 64])
 #pragma unroll
-        for (int x2 = 0; x2 < 8; ++x2) {
-          const float4 cs = *(const float4*)&trig[kk][16 * gq + 2 * x2];   // (c, s) of two pairs
-          const float a_lo = bf_lo(a[x2]), a_hi = bf_hi(a[x2]);
-          const float b_lo = bf_lo(b[x2]), b_hi = bf_hi(b[x2]);
-          w1[x2] = pack_bf16(a_lo * cs.x - b_lo * cs.y, a_hi * cs.z - b_hi * cs.w);
-          w2[x2] = pack_bf16(b_lo * cs.x + a_lo * cs.y, b_hi * cs.z + a_hi * cs.w);
-        }
+        for (int h = 0; h < 2; ++h) {
+          u32x4 w1, w2;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const uint32_t* src = (kb < 2) ? (w1 + 4 * kb) : (w2 + 4 * (kb - 2));
-          const bf16x8 bv = *(const bf16x8*)(&qlds[1][qrow + d_of(kb, gq, 0)]);
-          sr = mfma16(*(const bf16x8*)src, bv, sr);
+          for (int x = 0; x < 4; ++x) {
+            const int x2 = 4 * h + x;    // pairs 2 x2 and 2 x2 + 1: (a, b) = (k[m], k[m + 64])
+            const uint4 t = *(const uint4*)&tb[kk][16 * gq + 2 * x2];
+            const bf16x2 ab_lo = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(b[x2], a[x2], 0x05040100u));
+            const bf16x2 ab_hi = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(b[x2], a[x2], 0x07060302u));
+            w1[x] = pack_bf16(dot2(ab_lo, t.x), dot2(ab_hi, t.z));     // a c - b s
+            w2[x] = pack_bf16(dot2(ab_lo, t.y), dot2(ab_hi, t.w));     // a s + b c
+          }
+          const bf16x8 q1 = *(const bf16x8*)(&qlds[1][qrow + d_of(h, gq, 0)]);
+          const bf16x8 q2 = *(const bf16x8*)(&qlds[1][qrow + d_of(2 + h, gq, 0)]);
+          sr = mfma16(__builtin_bit_cast(bf16x8, w1), q1, sr);
+          sr = mfma16(__builtin_bit_cast(bf16x8, w2), q2, sr);
         }
       }
       if (any_loc) {
@@ -260,12 +325,9 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
         const float v = ((i - jk) >= w0 ? sr[e] : sl[e]) * scale_log2;
         sco[blk][e] = jk < L ? v : -INFINITY;
       }
-      __builtin_amdgcn_sched_barrier(0);
+      // the block's K registers are free: the next sub-chunk's block
+      load_k_blk(kt, blk, rk, (sc + 1) * SUB, row_bytes, koff);
     }
-    // K registers free: the next sub-chunk's keys
-    __builtin_amdgcn_sched_barrier(0);
-    load_k(kt, rk, (sc + 1) * SUB, row_bytes, koff);
-    __builtin_amdgcn_sched_barrier(0);
 
     // ---------------- softmax per column (q head) over the 64 keys ----------------
     float mx = -INFINITY;
@@ -276,7 +338,7 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float mn = fmaxf(run_m, mx);            // finite: every sub-chunk has a valid key
-    const float alpha = __builtin_amdgcn_exp2f(run_m - mn);
+    alpha = __builtin_amdgcn_exp2f(run_m - mn);
     float sum = 0.f;
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
@@ -287,15 +349,27 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
         sum += pr[e];
       }
       if (kl < NG)
-        *(uint2*)&prob[wave][kl][blk * 8 + 2 * gq] = make_uint2(pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3]));
+        {
+          const int ln = lane_now();
+          *(uint2*)&prob[wave][ln & 15][blk * 8 + 2 * (ln >> 4)] =
+              make_uint2(pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3]));
+        }
     }
     sum += __shfl_xor(sum, 16, 64);
     sum += __shfl_xor(sum, 32, 64);
     run_l = run_l * alpha + sum;
     run_m = mn;
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(0xc07f);              // lgkmcnt(0): prob rows written
+    }   // active
 
+    // the next sub-chunk's angle table goes to the other buffer, whose last
+    // readers (this sub-chunk's predecessor) all passed the previous barrier
+    // Its last readers finished sub-chunk sc - 1's scores before counting
+    // that sub-chunk's fill, which this wave has waited for.
+    if (fill_next) fill_trig(trig[(sc + 1) & 1], chain, steps[tm], tid, tm, tk, thr, dlo_g);
+    __builtin_amdgcn_s_waitcnt(0xc07f);              // lgkmcnt(0): table and prob rows written
+    if (lane == 0) __hip_atomic_fetch_add(&tables_done, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+
+    if (active) {
     // ---------------- PV: O^T += V^T P^T, 32 keys per MFMA ----------------
     // A operand (row kl, keys 8 gq .. 8 gq + 7): channel 8 kl + c of 8 keys;
     // B operand (column kl): probabilities of q head kl for the same keys.
@@ -303,7 +377,8 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
     for (int c = 0; c < 8; ++c) acc[c] *= alpha;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
-      const bf16x8 pb = *(const bf16x8*)&prob[wave][kl & (NG - 1)][16 * kh + 4 * gq];
+      const int ln = lane_now();
+      const bf16x8 pb = *(const bf16x8*)&prob[wave][ln & (NG - 1)][16 * kh + 4 * (ln >> 4)];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         u32x4 lo, hi;       // channels 8 kl + 2 w and 8 kl + 2 w + 1, keys in pairs
@@ -315,12 +390,12 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
         acc[2 * w] = mfma16(__builtin_bit_cast(bf16x8, lo), pb, acc[2 * w]);
         acc[2 * w + 1] = mfma16(__builtin_bit_cast(bf16x8, hi), pb, acc[2 * w + 1]);
       }
+      // the half's V registers are free: the next sub-chunk's half
+      load_v_half(vt, kh, rv, (sc + 1) * SUB, row_bytes, voff);
     }
-    // V registers free: the next sub-chunk's values
-    __builtin_amdgcn_sched_barrier(0);
-    load_v(vt, rv, (sc + 1) * SUB, row_bytes, voff);
-    __builtin_amdgcn_sched_barrier(0);
+    }   // active
   }
+  if (!in_time) run_l = NAN;                   // a count that never came: fail loudly
   // ---------------- partial records ----------------
   if (!active || kl >= NG) return;
   // output row 4 gq + e of MFMA c is channel 8 (4 gq + e) + c
