@@ -37,9 +37,9 @@
 // sub-chunk's rows as soon as they have been consumed (K per 16-key block
 // of the scores, V per 32-key half of PV), so every wave keeps about a
 // sub-chunk of loads in flight while it computes, issued a few at a time.
-// The angle table is double-buffered; the waves synchronise only through a
-// workgroup counter of finished fills, so a wave waits for the others'
-// share of the next table, never for their attention work.
+// The angle table has three buffers, filled two sub-chunks ahead; the waves
+// synchronise only through a workgroup counter of finished sub-chunks, so a
+// wave may run up to a sub-chunk ahead of the slowest one.
 #include "jl_internal.h"
 
 namespace {
@@ -53,6 +53,7 @@ constexpr int NT = 512;           // one wave per kv head
 constexpr int SUB = 64;            // keys per sub-chunk
 constexpr int NWAVES = NT / 64;
 constexpr int TRIG_STEP = NWAVES;  // key stride of an angle-table thread
+constexpr int NTRIG = 3;           // angle-table buffers
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr int MAX_HKV = 8;
@@ -170,7 +171,7 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
   // angle table of the sub-chunk: per (key, m) the bf16 pairs (c, -s) and
   // (s, c) of c, s = cos, sin(Delta_j theta_m), the two dot products of a
   // rotation
-  __shared__ __align__(16) uint2 trig[2][SUB][TPITCH];   // double-buffered: [sub-chunk & 1]
+  __shared__ __align__(16) uint2 trig[NTRIG][SUB][TPITCH];   // [sub-chunk % NTRIG]
   __shared__ __align__(16) uint32_t prob[MAX_HKV][NG][SUB / 2];   // wave-private [q head][key pair]
   __shared__ int heads[MAX_HKV * NG];
   // per m the two angle-table step rotations, per thread its angle chain
@@ -257,7 +258,10 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
     float s, c;
     jl_rope_sincos(f0 - j0, tf, &s, &c);
     chain[tid] = make_float4(c, s, __int_as_float(j0 - f0 * G), 0.f);
-    if ((i - c_begin) >= w0) fill_trig(trig[0], chain, st, tid, tm, tk, thr, dlo_g);
+    if ((i - c_begin) >= w0) {
+      fill_trig(trig[0], chain, st, tid, tm, tk, thr, dlo_g);
+      if (nsc > 1 && (i - (c_begin + SUB)) >= w0) fill_trig(trig[1], chain, st, tid, tm, tk, thr, dlo_g);
+    }
   }
 
   f32x4 acc[8];                                      // O^T: channel 32 gq + 8 e + c, q head kl
@@ -270,11 +274,10 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
 
   for (int sc = 0; sc < nsc; ++sc) {
     const int c0 = c_begin + sc * SUB;
-    // sub-chunk sc's table is complete once every wave has counted its fill
-    // of it (made in the previous sub-chunk)
-    if (sc > 0) in_time &= wait_count(&tables_done, NWAVES * sc);
-    const bool fill_next = sc + 1 < nsc && (i - (c0 + SUB)) >= w0;
-    const uint2 (*tb)[TPITCH] = trig[sc & 1];
+    // sub-chunk sc's table was filled two sub-chunks ago (or before the
+    // loop): every wave has counted that
+    if (sc >= 2) in_time &= wait_count(&tables_done, NWAVES * (sc - 1));
+    const uint2 (*tb)[TPITCH] = trig[sc % NTRIG];
     float alpha = 1.f;
     if (active) {
 
@@ -360,14 +363,8 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
     run_l = run_l * alpha + sum;
     run_m = mn;
     }   // active
-
-    // the next sub-chunk's angle table goes to the other buffer, whose last
-    // readers (this sub-chunk's predecessor) all passed the previous barrier
-    // Its last readers finished sub-chunk sc - 1's scores before counting
-    // that sub-chunk's fill, which this wave has waited for.
-    if (fill_next) fill_trig(trig[(sc + 1) & 1], chain, steps[tm], tid, tm, tk, thr, dlo_g);
-    __builtin_amdgcn_s_waitcnt(0xc07f);              // lgkmcnt(0): table and prob rows written
-    if (lane == 0) __hip_atomic_fetch_add(&tables_done, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0xc07f);              // lgkmcnt(0): prob rows written
 
     if (active) {
     // ---------------- PV: O^T += V^T P^T, 32 keys per MFMA ----------------
@@ -394,6 +391,15 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
       load_v_half(vt, kh, rv, (sc + 1) * SUB, row_bytes, voff);
     }
     }   // active
+
+    // sub-chunk sc + 2's table goes to the buffer of sub-chunk sc - 1, whose
+    // readers are done once every wave has counted sub-chunk sc - 1
+    if (sc + 2 < nsc && (i - (c0 + 2 * SUB)) >= w0) {
+      if (sc >= 1) in_time &= wait_count(&tables_done, NWAVES * sc);
+      fill_trig(trig[(sc + 2) % NTRIG], chain, steps[tm], tid, tm, tk, thr, dlo_g);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);              // lgkmcnt(0): table rows written
+    if (lane == 0) __hip_atomic_fetch_add(&tables_done, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   if (!in_time) run_l = NAN;                   // a count that never came: fail loudly
   // ---------------- partial records ----------------
