@@ -122,6 +122,34 @@ __device__ inline void load_v_half(VTile& t, int kh, __amdgpu_buffer_rsrc_t rv, 
     t.w[kh][x] = __builtin_amdgcn_raw_buffer_load_b128(rv, (row0 + 32 * kh + x) * row_bytes + lane_off, 0, 0);
 }
 
+// Scores of one 16-key block against the rotated query columns: the lane's
+// key rows k[m], k[m + 64] (4 x 16 bytes, pairs 16 gq ..) are rotated by the
+// key's table angles with dot2 and fed as MFMA A operands; steps kb = h take
+// rotated k[m] and kb = 2 + h rotated k[m + 64] for pairs 8 h .. 8 h + 7.
+__device__ inline f32x4 remote_block(const u32x4 (&kw)[4], const uint2* trow, const __bf16* qcol, int gq) {
+  const uint32_t* a = (const uint32_t*)&kw[0];
+  const uint32_t* b = (const uint32_t*)&kw[2];
+  f32x4 sr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    u32x4 w1, w2;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int x2 = 4 * h + x;    // pairs 2 x2 and 2 x2 + 1: (a, b) = (k[m], k[m + 64])
+      const uint4 t = *(const uint4*)&trow[16 * gq + 2 * x2];
+      const bf16x2 ab_lo = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(b[x2], a[x2], 0x05040100u));
+      const bf16x2 ab_hi = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(b[x2], a[x2], 0x07060302u));
+      w1[x] = pack_bf16(dot2(ab_lo, t.x), dot2(ab_hi, t.z));     // a c - b s
+      w2[x] = pack_bf16(dot2(ab_lo, t.y), dot2(ab_hi, t.w));     // a s + b c
+    }
+    const bf16x8 q1 = *(const bf16x8*)(qcol + d_of(h, gq, 0));
+    const bf16x8 q2 = *(const bf16x8*)(qcol + d_of(2 + h, gq, 0));
+    sr = mfma16(__builtin_bit_cast(bf16x8, w1), q1, sr);
+    sr = mfma16(__builtin_bit_cast(bf16x8, w2), q2, sr);
+  }
+  return sr;
+}
+
 // Waits until the workgroup counter reaches `target`.  Every wave adds one
 // per sub-chunk whatever it computes, so the count always arrives; the bound
 // only keeps a broken invariant from hanging the device (the caller then
@@ -224,16 +252,17 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
   }
   __syncthreads();
   {
-    // the query in both variants: as given (base) and rotated by Delta_q
+    // the query in both variants, scaled by scale * log2 e: as given (base)
+    // and rotated by Delta_q
     const int dq = jl_remote_pos(i, G) - i;
     for (int e = tid; e < Hq * 64; e += NT) {
       const int slot = e >> 6, m = e & 63;
       const __bf16* qr = q + heads[slot] * D;
-      const float x1 = (float)qr[m], x2 = (float)qr[m + 64];
+      const float x1 = (float)qr[m] * scale_log2, x2 = (float)qr[m + 64] * scale_log2;
       float c, s;
       jl_rope_sincos(dq, fr.turn_frac[m], &s, &c);
-      qlds[0][slot * QPITCH + m] = qr[m];
-      qlds[0][slot * QPITCH + m + 64] = qr[m + 64];
+      qlds[0][slot * QPITCH + m] = (__bf16)x1;
+      qlds[0][slot * QPITCH + m + 64] = (__bf16)x2;
       qlds[1][slot * QPITCH + m] = (__bf16)(x1 * c - x2 * s);
       qlds[1][slot * QPITCH + m + 64] = (__bf16)(x2 * c + x1 * s);
     }
@@ -282,54 +311,33 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
     if (active) {
 
     // ---------------- scores: 4 blocks of 16 keys ----------------
+    // lane holds S^T[key blk*16 + 4 gq + e][column kl], in log2 units (the
+    // query carries scale * log2 e)
     f32x4 sco[4];
+    {
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
-      const int kk = blk * 16 + kl;
-      const int j = c0 + kk;
-      const bool rem = j < L && (i - j) >= w0;
-      const bool any_rem = __any(rem);
-      const bool any_loc = __any(j < L && !rem);
-      f32x4 sr = {}, sl = {};
-      if (any_rem) {
-        const uint32_t* a = (const uint32_t*)&kt.w[blk][0];
-        const uint32_t* b = (const uint32_t*)&kt.w[blk][2];
-        // pairs 8 h .. 8 h + 7 of the lane feed MFMA steps kb = h (rotated
-        // k[m]) and kb = 2 + h (rotated k[m + 64])
+      for (int blk = 0; blk < 4; ++blk) {
+        const int kk = blk * 16 + kl;
+        const int j = c0 + kk;
+        const bool rem = j < L && (i - j) >= w0;
+        const bool any_rem = __any(rem);
+        const bool any_loc = __any(j < L && !rem);
+        f32x4 sr = {}, sl = {};
+        if (any_rem) sr = remote_block(kt.w[blk], tb[kk], &qlds[1][qrow], gq);
+        if (any_loc) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          u32x4 w1, w2;
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            const int x2 = 4 * h + x;    // pairs 2 x2 and 2 x2 + 1: (a, b) = (k[m], k[m + 64])
-            const uint4 t = *(const uint4*)&tb[kk][16 * gq + 2 * x2];
-            const bf16x2 ab_lo = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(b[x2], a[x2], 0x05040100u));
-            const bf16x2 ab_hi = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(b[x2], a[x2], 0x07060302u));
-            w1[x] = pack_bf16(dot2(ab_lo, t.x), dot2(ab_hi, t.z));     // a c - b s
-            w2[x] = pack_bf16(dot2(ab_lo, t.y), dot2(ab_hi, t.w));     // a s + b c
+          for (int kb = 0; kb < 4; ++kb) {
+            const bf16x8 bv = *(const bf16x8*)(&qlds[0][qrow + d_of(kb, gq, 0)]);
+            sl = mfma16(__builtin_bit_cast(bf16x8, kt.w[blk][kb]), bv, sl);
           }
-          const bf16x8 q1 = *(const bf16x8*)(&qlds[1][qrow + d_of(h, gq, 0)]);
-          const bf16x8 q2 = *(const bf16x8*)(&qlds[1][qrow + d_of(2 + h, gq, 0)]);
-          sr = mfma16(__builtin_bit_cast(bf16x8, w1), q1, sr);
-          sr = mfma16(__builtin_bit_cast(bf16x8, w2), q2, sr);
         }
-      }
-      if (any_loc) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const bf16x8 bv = *(const bf16x8*)(&qlds[0][qrow + d_of(kb, gq, 0)]);
-          sl = mfma16(__builtin_bit_cast(bf16x8, kt.w[blk][kb]), bv, sl);
+        for (int e = 0; e < 4; ++e) {
+          const int jk = c0 + blk * 16 + 4 * gq + e;
+          sco[blk][e] = jk >= L ? -INFINITY : (i - jk) >= w0 ? sr[e] : sl[e];
         }
+        load_k_blk(kt, blk, rk, (sc + 1) * SUB, row_bytes, koff);
       }
-      // lane holds S^T[key blk*16 + 4 gq + e][column kl]
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int jk = c0 + blk * 16 + 4 * gq + e;
-        const float v = ((i - jk) >= w0 ? sr[e] : sl[e]) * scale_log2;
-        sco[blk][e] = jk < L ? v : -INFINITY;
-      }
-      // the block's K registers are free: the next sub-chunk's block
-      load_k_blk(kt, blk, rk, (sc + 1) * SUB, row_bytes, koff);
     }
 
     // ---------------- softmax per column (q head) over the 64 keys ----------------
