@@ -281,7 +281,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(pass2_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pass2_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": read_traffic(PASS2_TRAFFIC),
-                     "kernel": "prefill_pass_kernel<0> (pass 2: remote q/k, full causal)",
+                     "kernel": "prefill_pp_kernel<0> + prefill_pass_kernel<0, true> (pass 2: remote "
+                               "q/k, full causal; the second kernel takes the first 128 rows)",
                      "flops_per_launch": Fc, "ms_per_launch": round(pass2_ms, 3)},
         "prefill": {"call_ms": round(call_ms, 3), "attention_ms": round(attn_ms, 3),
                     "pass2_ms": round(pass2_ms, 3), "tflops_3pass": round(tflops, 2),
