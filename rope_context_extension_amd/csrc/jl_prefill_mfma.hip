@@ -811,23 +811,23 @@ __device__ inline void pp_copies(const PpTiles& T, int j) {
                                      T.wave);
 }
 
-// The softmax phase runs at raised wave priority: its vector-ALU stream then
-// issues first on the SIMD, and the matrix-phase wave beside it still finds
-// the MFMA pipe's issue slots (one MFMA per 8 passes).  Without it the older
-// wave of the pair always wins and the younger group's softmax phase stretches.
 template <int KIND>
 __device__ inline void pp_softmax_tile(const PpTiles& T, int k, f32x16* s, bf16x8* p, PpState& st, f32x16* o,
                                        const WaveRows& wr, int g) {
-  __builtin_amdgcn_s_setprio(2);
   const int j0 = (T.t0 + k) * BK;
   if (wave_needs_mask<KIND>(j0, wr)) mask_tile<KIND>(s, wr.myrow, j0, wr.w0, g);
   pp_softmax(s, p, st, o);
-  __builtin_amdgcn_s_setprio(0);
 }
 
-// matrix phase of a wave: S_k (with the current stabiliser) and O += V_{k-1} P_{k-1}^T
+// Matrix phase of a wave: S_k (with the current stabiliser) and O += V_{k-1}
+// P_{k-1}^T.  It runs at raised wave priority: an MFMA then issues as soon as
+// the pipe takes it, once per 8 passes, and the softmax-phase wave beside it
+// on the SIMD fills every other issue slot.  With the priority on the softmax
+// side instead (or on neither), vector-ALU bursts hold back MFMA issue and the
+// pipe idles (measured: about 2% of the whole prefill).
 __device__ inline void pp_matrix(const PpTiles& T, int k, bool pv, const bf16x8* qf, const PpState& st,
                                  f32x16* s, const bf16x8* p, f32x16* o, int lane) {
+  __builtin_amdgcn_s_setprio(2);
   pp_scores(pp_kbuf(T, k), qf, pp_bias(st), lane, s);
   if (pv) {
     pp_pv(pp_vbuf(T, k - 1), p, lane, o);
@@ -835,6 +835,7 @@ __device__ inline void pp_matrix(const PpTiles& T, int k, bool pv, const bf16x8*
   } else {
     pp_mfma_order<16, PP_READ_DEPTH>();
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // The two groups run mirrored straight-line loops with the same number of
