@@ -658,12 +658,16 @@ __device__ inline float pair_sum(float x) {
 }
 
 // Row state of a flash pass in the ping-pong kernel.  Scores arrive in log2
-// units (q is pre-scaled); the softmax exponentiates s - m with one add per
-// score (kept out of the matrix phase, which issues nothing but MFMAs and
-// their LDS reads).
+// units (q is pre-scaled) and already shifted by -m: the first MFMA of each
+// score chain takes the register tile cb = (-m, ..., -m) as its accumulator
+// input, so the softmax exponentiates the MFMA output directly.  cb lives
+// across tiles and is rewritten only when the stabiliser moves, which keeps
+// both the shift and its set-up out of the per-tile vector-ALU work (the
+// vector ALU and the MFMA pipe of one SIMD hardly overlap).
 struct PpState {
   float m;      // stabiliser (log2 units), identical in lanes l and l ^ 32; -inf before any key
   float l;      // this lane's partial sum of the bf16 probabilities
+  f32x16 cb;    // (-m, ..., -m), 0 while the row has no stabiliser: the score MFMAs' accumulator input
 };
 
 // -m, or 0 while the row has no stabiliser
@@ -671,10 +675,10 @@ __device__ inline float pp_shift(const PpState& st) { return st.m == -INFINITY ?
 
 // S^T of one 64-key tile (same layout as score_tile): s[sb] holds keys
 // sb*32 + 16*(i/8) + 8*g + (i%8) of this lane's query row.
-__device__ inline void pp_scores(const lds_char* kt, const bf16x8* qf, int lane, f32x16* s) {
+__device__ inline void pp_scores(const lds_char* kt, const bf16x8* qf, const f32x16& cb, int lane, f32x16* s) {
   const int g = lane >> 5;
   const lds_char* base = kt + swap23(lane & 31) * KP + g * 16;
-  f32x16 a0 = {}, a1 = {};
+  f32x16 a0 = cb, a1 = cb;
 #pragma unroll
   for (int kb = 0; kb < 8; ++kb) {
     const bf16x8 k0 = *(const __attribute__((address_space(3))) bf16x8*)(base + kb * 32);
@@ -701,9 +705,10 @@ __device__ inline void pp_pv(const lds_char* vt, const bf16x8* p, int lane, f32x
     }
 }
 
-// p = bf16(exp2(s + shift)) for the 32 scores of a lane; returns the sum of
-// the bf16 values (the weights the PV product uses), accumulated in two
-// independent chains.
+// p = bf16(exp2(s + shift)) for the 32 scores of a lane (SHIFT false: shift
+// is 0 and not applied); returns the sum of the bf16 values (the weights the
+// PV product uses), accumulated in two independent chains.
+template <bool SHIFT>
 __device__ inline float pp_exp_tile(const f32x16* s, float shift, bf16x8* p) {
   const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
   float sum[2] = {0.f, 0.f};
@@ -714,7 +719,7 @@ __device__ inline float pp_exp_tile(const f32x16* s, float shift, bf16x8* p) {
       bf16x8 v;
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        v[j] = (__bf16)__builtin_amdgcn_exp2f(s[sb][8 * hh + j] + shift);
+        v[j] = (__bf16)__builtin_amdgcn_exp2f(SHIFT ? s[sb][8 * hh + j] + shift : s[sb][8 * hh + j]);
       p[2 * sb + hh] = v;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -730,9 +735,9 @@ __device__ inline float pp_exp_tile(const f32x16* s, float shift, bf16x8* p) {
 // l and the accumulators far from fp32 overflow.
 constexpr float PP_SUM_LIMIT = 4294967296.f;   // 2^32
 
-// Softmax of one tile without a row maximum in the common case: p =
-// exp2(s - m) with the current stabiliser (done by the caller, tsum = this
-// lane's tile sum).  The wave takes the exact path instead when a lane's tile
+// Softmax of one tile without a row maximum in the common case: the scores
+// come shifted by the current stabiliser, so p = exp2(s) directly (done by
+// the caller, tsum = this lane's tile sum).  The wave takes the exact path instead when a lane's tile
 // sum exceeds 2^32 (a score more than ~27 above m) or a row has no stabiliser
 // yet: row maximum, rescale of the accumulators, new stabiliser,
 // exponentials again.
@@ -741,6 +746,7 @@ __device__ inline void pp_settle(const f32x16* s, bf16x8* p, PpState& st, f32x16
     st.l += tsum;
     return;
   }
+  const float bias = pp_shift(st);                       // what the score MFMAs added
   float mx = -INFINITY;
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb)
@@ -748,7 +754,7 @@ __device__ inline void pp_settle(const f32x16* s, bf16x8* p, PpState& st, f32x16
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sb][i]);
   mx = pair_max(mx);
   if (mx != -INFINITY) {
-    const float mn = fmaxf(st.m, mx);                    // exact row maximum so far
+    const float mn = fmaxf(st.m, mx - bias);             // exact row maximum so far
     if (mn > st.m) {
       const float a = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m - mn);
       st.l *= a;
@@ -757,11 +763,14 @@ __device__ inline void pp_settle(const f32x16* s, bf16x8* p, PpState& st, f32x16
       st.m = mn;
     }
   }
-  st.l += pp_exp_tile(s, pp_shift(st), p);
+  const float nb = pp_shift(st);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) st.cb[i] = nb;
+  st.l += pp_exp_tile<true>(s, nb - bias, p);
 }
 
 __device__ inline void pp_softmax(const f32x16* s, bf16x8* p, PpState& st, f32x16* o) {
-  pp_settle(s, p, st, o, pp_exp_tile(s, pp_shift(st), p));
+  pp_settle(s, p, st, o, pp_exp_tile<false>(s, 0.f, p));
 }
 
 // Instruction order of a matrix phase with NM MFMAs, each fed by one LDS
@@ -810,16 +819,16 @@ __device__ inline void pp_softmax_tile(const PpTiles& T, int k, f32x16* s, bf16x
   pp_softmax(s, p, st, o);
 }
 
-// Matrix phase of a wave: S_k and O += V_{k-1}
+// Matrix phase of a wave: S_k (shifted by the current stabiliser) and O += V_{k-1}
 // P_{k-1}^T.  It runs at raised wave priority: an MFMA then issues as soon as
 // the pipe takes it, once per 8 passes, and the softmax-phase wave beside it
 // on the SIMD fills every other issue slot.  With the priority on the softmax
 // side instead (or on neither), vector-ALU bursts hold back MFMA issue and the
 // pipe idles (measured: about 2% of the whole prefill).
-__device__ inline void pp_matrix(const PpTiles& T, int k, bool pv, const bf16x8* qf, f32x16* s, const bf16x8* p,
-                                 f32x16* o, int lane) {
+__device__ inline void pp_matrix(const PpTiles& T, int k, bool pv, const bf16x8* qf, const PpState& st, f32x16* s,
+                                 const bf16x8* p, f32x16* o, int lane) {
   __builtin_amdgcn_s_setprio(2);
-  pp_scores(pp_kbuf(T, k), qf, lane, s);
+  pp_scores(pp_kbuf(T, k), qf, st.cb, lane, s);
   if (pv) {
     pp_pv(pp_vbuf(T, k - 1), p, lane, o);
     pp_mfma_order<32, PP_READ_DEPTH>();
@@ -851,14 +860,14 @@ __device__ inline void pp_run(const PpTiles& T, const bf16x8* qf, PpState& st, f
   pp_barrier();
   if (T.wave < 4) {
     pp_copies(T, 0);
-    pp_matrix(T, 0, false, qf, s, p, o, lane);
+    pp_matrix(T, 0, false, qf, st, s, p, o, lane);
     pp_barrier();
     pp_softmax_tile<KIND>(T, 0, s, p, st, o, wr, g);
     pp_wait_copies();
     pp_barrier();
     for (int j = 1; j < n; ++j) {
       pp_copies(T, j);
-      pp_matrix(T, j, true, qf, s, p, o, lane);
+      pp_matrix(T, j, true, qf, st, s, p, o, lane);
       pp_barrier();
       pp_softmax_tile<KIND>(T, j, s, p, st, o, wr, g);
       pp_wait_copies();
@@ -870,12 +879,12 @@ __device__ inline void pp_run(const PpTiles& T, const bf16x8* qf, PpState& st, f
     pp_barrier();
   } else {
     pp_barrier();
-    pp_matrix(T, 0, false, qf, s, p, o, lane);
+    pp_matrix(T, 0, false, qf, st, s, p, o, lane);
     pp_barrier();
     for (int j = 1; j < n; ++j) {
       pp_softmax_tile<KIND>(T, j - 1, s, p, st, o, wr, g);
       pp_barrier();
-      pp_matrix(T, j, true, qf, s, p, o, lane);
+      pp_matrix(T, j, true, qf, st, s, p, o, lane);
       pp_barrier();
     }
     pp_softmax_tile<KIND>(T, n - 1, s, p, st, o, wr, g);
@@ -939,7 +948,7 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
   f32x16 o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16{};
-  PpState st{-INFINITY, 0.f};
+  PpState st{-INFINITY, 0.f, f32x16{}};
   T.t0 = ROLE == 0 || only1 ? 0 : tw0;
   T.n = tiles_end - T.t0;
   if (T.n > 0) pp_run<KIND>(T, qf, st, o, wr, lane);
