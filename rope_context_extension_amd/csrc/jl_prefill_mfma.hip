@@ -193,12 +193,16 @@ constexpr float RESCALE_LOG2 = 8.f;
 // 0 <= dist < w0 (window).  Masked scores become -inf.
 template <int KIND>
 __device__ inline void mask_tile(f32x16* s, int myrow, int j0, int w0, int g) {
+  const int d0 = myrow - j0 - 8 * g;
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int dist = myrow - (j0 + key_of(sb, i, g));
-      const bool keep = KIND == 0 ? dist >= 0 : (dist >= 0 && dist < w0);
+      // dist = myrow - (j0 + key) = d0 - c with the lane-independent part c
+      // of the key offset; the window test 0 <= dist < w0 is one unsigned
+      // compare
+      const int c = key_of(sb, i, 0);
+      const bool keep = KIND == 0 ? d0 >= c : (uint32_t)(d0 - c) < (uint32_t)w0;
       s[sb][i] = keep ? s[sb][i] : -INFINITY;
     }
 }
@@ -815,6 +819,12 @@ template <int KIND>
 __device__ inline void pp_softmax_tile(const PpTiles& T, int k, f32x16* s, bf16x8* p, PpState& st, f32x16* o,
                                        const WaveRows& wr, int g) {
   const int j0 = (T.t0 + k) * BK;
+  if (!wave_has_work<KIND>(j0, wr)) {
+    // no pair of the wave's rows in this tile: P = 0, the row state is unchanged
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = bf16x8{};
+    return;
+  }
   if (wave_needs_mask<KIND>(j0, wr)) mask_tile<KIND>(s, wr.myrow, j0, wr.w0, g);
   pp_softmax(s, p, st, o);
 }
@@ -848,8 +858,9 @@ __device__ inline void pp_matrix(const PpTiles& T, int k, bool pv, const bf16x8*
 // the longer ones (its matrix phase starts every tile), so it carries no copy
 // work (measured: about 1% against group A issuing the copies).  Tiles in
 // which a wave has no pair (the last two causal tiles of group A, the first
-// two window tiles of group B) are computed anyway and masked to -inf, which
-// keeps the loops free of per-wave branches around register-resident state.
+// two window tiles of group B) keep their MFMAs, which keeps the loops free
+// of per-wave branches around register-resident state; their softmax only
+// writes P = 0.
 template <int KIND>
 __device__ inline void pp_run(const PpTiles& T, const bf16x8* qf, PpState& st, f32x16* o, const WaveRows& wr,
                               int lane) {
