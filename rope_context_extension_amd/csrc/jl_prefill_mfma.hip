@@ -909,11 +909,23 @@ __device__ inline void pp_run(const PpTiles& T, const bf16x8* qf, PpState& st, f
   }
 }
 
+// Pass 1's normalised output of a 256-row tile, kept in LDS between the two
+// window passes of ROLE 3: 64 bf16 per lane, chunk c (8 values) of thread t
+// at (c * PP_NT + t) * 16 bytes.  o1 enters the merge with a positive weight
+// only (the cancelling pair is o2 and o3), so bf16 holds it within the
+// output's own rounding.
+constexpr int O1_BYTES = PP_NT * 128;
+
+// ROLE 0: pass 2 (full causal, remote q/k).  ROLE 3: passes 1 and 3 of the
+// tile one after the other (window, base q/k, then window, remote q/k) and
+// the inclusion-exclusion merge with pass 2's output; sequences with
+// w0 >= L run pass 1 over the whole causal range and write O directly.
 template <int ROLE>
 __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlHeadMap hm, JlSeqs seqs,
                                                              JlSched sc) {
+  static_assert(ROLE == 0 || ROLE == 3, "pass roles of the 256-row kernel");
   constexpr int KIND = ROLE == 0 ? 0 : 1;
-  __shared__ __align__(1024) char smem[2 * (KT_BYTES + VT_BYTES)];
+  __shared__ __align__(1024) char smem[2 * (KT_BYTES + VT_BYTES) + (ROLE == 3 ? O1_BYTES : 0)];
   int h, b, u;
   if (!block_item<false>(sc, A.Hq, &h, &b, &u)) return;
   // the work item is uniform over the block; say so, so that pointers built
@@ -927,8 +939,7 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
   const bool only1 = A.w0 >= (int64_t)L;
   const bool only2 = seqs.G[b] == 1 && !only1;
   if (ROLE == 0 && only1) return;
-  if (ROLE == 1 && only2) return;
-  if (ROLE == 2 && (only1 || only2)) return;
+  if (ROLE == 3 && only2) return;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -942,7 +953,8 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
   const int tiles_end = min((r0 + PP_BQ + BK - 1) / BK, (L + BK - 1) / BK);
   const int tw0 = (r0 - w0 + 1) > 0 ? (r0 - w0 + 1) / BK : 0;
   const int64_t vtiles = seqs.vt_cols / 64;
-  const __bf16* ksrc = (ROLE == 1 ? A.kb : A.kr) + ((int64_t)kvh * A.t_pad + s0) * D;
+  const int64_t krow = ((int64_t)kvh * A.t_pad + s0) * D;
+  const __bf16* ksrc = (ROLE == 3 ? A.kb : A.kr) + krow;
   const __bf16* vsrc =
       A.vt + ((int64_t)kvh * vtiles + __builtin_amdgcn_readfirstlane(seqs.vstart[b]) / 64) * (D * 64);
   PpTiles T;
@@ -954,7 +966,7 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
   T.wave = wave;
   bf16x8 qf[8];
   if (live) {
-    load_q(qf, (ROLE == 1 ? A.qb : A.qr) + ((int64_t)h * A.t_pad + s0 + wr.myrow) * D, g);
+    load_q(qf, (ROLE == 3 ? A.qb : A.qr) + ((int64_t)h * A.t_pad + s0 + wr.myrow) * D, g);
   } else {
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) qf[kb] = bf16x8{};
@@ -967,26 +979,29 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
   T.n = tiles_end - T.t0;
   if (T.n > 0) pp_run<KIND>(T, qf, st, o, wr, lane);
   const float l = pair_sum(st.l);
-  if (!live || wr.myrow >= L) return;
+  const float lam = l > 0.f ? st.m + __log2f(l) : -INFINITY;
   const int64_t ridx = (int64_t)h * A.total + s0 + wr.myrow;
-  if constexpr (ROLE != 2) {
-    const float lam = l > 0.f ? st.m + __log2f(l) : -INFINITY;
-    if ((ROLE == 0 && only2) || (ROLE == 1 && only1)) {
-      __bf16* orow = A.out + ((s0 + wr.myrow) * A.Hq + h) * D;
-      const float inv = 1.f / l;
+  const bool row_ok = live && wr.myrow < L;
+  if (ROLE == 0 ? only2 : only1) {
+    // the pass is the whole attention of the sequence
+    if (!row_ok) return;
+    __bf16* orow = A.out + ((s0 + wr.myrow) * A.Hq + h) * D;
+    const float inv = 1.f / l;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          bf16x4 w;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[db][4 * q4 + e] * inv);
-          *(bf16x4*)(orow + db * 32 + 8 * q4 + 4 * g) = w;
-        }
-      if (A.lse != nullptr && g == 0) A.lse[ridx] = lam * LN2;
-      return;
-    }
-    float* orow = (ROLE == 0 ? A.o2 : A.o1) + ridx * D;
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[db][4 * q4 + e] * inv);
+        *(bf16x4*)(orow + db * 32 + 8 * q4 + 4 * g) = w;
+      }
+    if (A.lse != nullptr && g == 0) A.lse[ridx] = lam * LN2;
+    return;
+  }
+  if constexpr (ROLE == 0) {
+    if (!row_ok) return;
+    float* orow = A.o2 + ridx * D;
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -995,39 +1010,63 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
         *(float4*)(orow + db * 32 + 8 * q4 + 4 * g) =
             make_float4(o[db][4 * q4] * inv, o[db][4 * q4 + 1] * inv, o[db][4 * q4 + 2] * inv,
                         o[db][4 * q4 + 3] * inv);
-    if (g == 0) (ROLE == 0 ? A.lse2 : A.lse1)[ridx] = lam;
+    if (g == 0) A.lse2[ridx] = lam;
   } else {
-    const float lam1 = A.lse1[ridx];
+    // pass 1 done: o1 (normalised, bf16) to LDS, lam1 stays in a register
+    const float lam1 = lam;
+    {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      __attribute__((address_space(3))) bf16x8* o1s =
+          (__attribute__((address_space(3))) bf16x8*)(lds + 2 * (KT_BYTES + VT_BYTES)) + tid;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        bf16x8 w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = (__bf16)(o[c >> 1][8 * (c & 1) + e] * inv);
+        o1s[c * PP_NT] = w;
+      }
+    }
+    // pass 3: the same window tiles with remote q/k
+    T.rk = __builtin_amdgcn_make_buffer_rsrc((void*)(A.kr + krow), 0, 0x7fffffff, BUF_RSRC_WORD3);
+    if (live) load_q(qf, A.qr + ((int64_t)h * A.t_pad + s0 + wr.myrow) * D, g);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+    st = PpState{-INFINITY, 0.f, f32x16{}};
+    if (T.n > 0) pp_run<KIND>(T, qf, st, o, wr, lane);
+    const float l3 = pair_sum(st.l);
+    if (!row_ok) return;
     const float lam2 = A.lse2[ridx];
-    const float lam3 = l > 0.f ? st.m + __log2f(l) : -INFINITY;
+    const float lam3 = l3 > 0.f ? st.m + __log2f(l3) : -INFINITY;
     const float M = fmaxf(lam1, lam2);
     const float z1 = __builtin_amdgcn_exp2f(lam1 - M);
     const float z2 = __builtin_amdgcn_exp2f(lam2 - M);
     const float z3 = __builtin_amdgcn_exp2f(lam3 - M);
-    const float c3 = l > 0.f ? __builtin_amdgcn_exp2f(st.m - M) : 0.f;
+    const float c3 = l3 > 0.f ? __builtin_amdgcn_exp2f(st.m - M) : 0.f;
     const float far = z2 - z3;
     const float Z = z1 + fmaxf(far, 0.f);
     const float inv = 1.f / Z;
-    const float* o1row = A.o1 + ridx * D;
     const float* o2row = A.o2 + ridx * D;
+    const __attribute__((address_space(3))) bf16x8* o1s =
+        (const __attribute__((address_space(3))) bf16x8*)(lds + 2 * (KT_BYTES + VT_BYTES)) + tid;
     __bf16* orow = A.out + ((s0 + wr.myrow) * A.Hq + h) * D;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int c = 0; c < 8; ++c) {
+      const bf16x8 v1 = o1s[c * PP_NT];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
+      for (int hq = 0; hq < 2; ++hq) {
+        const int db = c >> 1, q4 = 2 * (c & 1) + hq;
         const int d0 = db * 32 + 8 * q4 + 4 * g;
-        const float4 v1 = *(const float4*)(o1row + d0);
         const float4 v2 = *(const float4*)(o2row + d0);
-        const float o1v[4] = {v1.x, v1.y, v1.z, v1.w};
         const float o2v[4] = {v2.x, v2.y, v2.z, v2.w};
         bf16x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float far_num = far > 0.f ? z2 * o2v[e] - c3 * o[db][4 * q4 + e] : 0.f;
-          w[e] = (__bf16)((z1 * o1v[e] + far_num) * inv);
+          w[e] = (__bf16)((z1 * (float)v1[4 * hq + e] + far_num) * inv);
         }
         *(bf16x4*)(orow + d0) = w;
       }
+    }
     if (A.lse != nullptr && g == 0) A.lse[ridx] = (M + __log2f(Z)) * LN2;
   }
 }
@@ -1107,15 +1146,17 @@ hipError_t jl_launch_prefill_bf16(const JlPrefillWs& ws, void* o, float* lse, in
   }
   const unsigned nblk = (unsigned)sc.total_units * (unsigned)Hq;   // multiple of 8 when xcd_heads
   const unsigned nfirst = (unsigned)(seqs.nseq * Hq);
-#define JL_PASS(ROLE)                                                                   \
-  do {                                                                                  \
-    if (nblk) prefill_pp_kernel<ROLE><<<nblk, PP_NT, 0, st>>>(A, hm, seqs, sc);         \
-    prefill_pass_kernel<ROLE, true><<<nfirst, NT, 0, st>>>(A, hm, seqs, sc);            \
-  } while (0)
-  if (any_p2) JL_PASS(0);
+  // rows >= 128 in 256-row tiles (pass 2, then passes 1 and 3 fused); the
+  // first 128 rows of every sequence in the split-operand kernel, pass by pass
+  if (any_p2) {
+    if (nblk) prefill_pp_kernel<0><<<nblk, PP_NT, 0, st>>>(A, hm, seqs, sc);
+    prefill_pass_kernel<0, true><<<nfirst, NT, 0, st>>>(A, hm, seqs, sc);
+  }
   if (hipEvent_t mid = jl_profile_mid_event()) (void)hipEventRecord(mid, st);
-  if (any_p1) JL_PASS(1);
-  if (any_p3) JL_PASS(2);
-#undef JL_PASS
+  if (any_p1) {
+    if (nblk) prefill_pp_kernel<3><<<nblk, PP_NT, 0, st>>>(A, hm, seqs, sc);
+    prefill_pass_kernel<1, true><<<nfirst, NT, 0, st>>>(A, hm, seqs, sc);
+  }
+  if (any_p3) prefill_pass_kernel<2, true><<<nfirst, NT, 0, st>>>(A, hm, seqs, sc);
   return hipGetLastError();
 }
