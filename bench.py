@@ -149,7 +149,7 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=96)
+    ap.add_argument("--cpu-rows", type=int, default=320)
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer three times (counter calibration run)")
