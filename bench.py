@@ -18,6 +18,9 @@ Prints ONE JSON line:
             counter summary when it was measured on the current kernel source;
   decode    sustained decode steps (KV bytes 2 L Hkv d 2 per step) and the
             split-K kernel alone, against the HBM peak;
+  overhead  the bifocal calls over plain attention at the same shapes (the same
+            library with w_pretrained = L, i.e. G = 1: plain causal RoPE prefill
+            and Delta-free decode);
   cpu_baseline  the fp64 oracle on a sample of query rows of the same layer.
 
     python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--no-cpu-baseline]
@@ -253,13 +256,44 @@ def main():
     dec_us = ev.elapsed_ms(e0, e1) * 1e3 / args.decode_steps
     torch.cuda.synchronize()
 
+    # overhead against plain attention at the same shapes: G = 1 (w_pretrained = L) makes every
+    # aliased position the absolute one, so the same library runs plain causal RoPE attention
+    # (prefill: one full-causal pass) and Delta-free decode (every key on the base path)
+    def prefill_plain():
+        jl.prefill(q, k, v, w0=cfg.w0, w_pretrained=L, rope_base=cfg.rope_base, out=o, lse=lse,
+                   workspace=ws)
+
+    def decode_plain(i):
+        kc, vc = caches[i % n_caches]
+        jl.decode(qd, kc, vc, L, w0=dcfg.w0, w_pretrained=L, rope_base=dcfg.rope_base, out=od, lse=lsed,
+                  workspace=wsd)
+
+    prefill_plain()
+    torch.cuda.synchronize()
+    pe = [(ev.create(), ev.create()) for _ in range(3)]
+    for a_, b_ in pe:
+        ev.record(a_, stream)
+        prefill_plain()
+        ev.record(b_, stream)
+    plain_ms = float(np.mean([ev.elapsed_ms(a_, b_) for a_, b_ in pe]))
+    for i in range(8):
+        decode_plain(i)
+    torch.cuda.synchronize()
+    ev.record(e0, stream)
+    for i in range(args.decode_steps):
+        decode_plain(i)
+    ev.record(e1, stream)
+    dec_plain_us = ev.elapsed_ms(e0, e1) * 1e3 / args.decode_steps
+    torch.cuda.synchronize()
+
     tflops = F3 / (call_ms * 1e-3) / 1e12
     pass2_tflops = Fc / (pass2_ms * 1e-3) / 1e12
     dec_gbs = kv_bytes / (dec_us * 1e-6) / 1e9
     split_gbs = kv_bytes / (split_us * 1e-6) / 1e9
     log(f"[bench] prefill call {call_ms:.2f} ms -> {tflops:.1f} TFLOP/s (F_3pass); attention kernels "
         f"{attn_ms:.2f} ms; pass 2 {pass2_ms:.2f} ms -> {pass2_tflops:.1f} TFLOP/s; decode {dec_us:.1f} "
-        f"us/step ({dec_gbs:.0f} GB/s), split-K {split_us:.1f} us ({split_gbs:.0f} GB/s)")
+        f"us/step ({dec_gbs:.0f} GB/s), split-K {split_us:.1f} us ({split_gbs:.0f} GB/s); plain causal "
+        f"prefill {plain_ms:.2f} ms, Delta-free decode {dec_plain_us:.1f} us")
 
     out = {
         "metric": METRIC,
@@ -295,6 +329,10 @@ def main():
                                 "traffic": read_traffic(DECODE_TRAFFIC),
                                 "kernel": "decode_split_kernel", "us_per_launch": round(split_us, 2)},
                    "step_frac_hbm": round(dec_gbs / PEAK_HBM_GBS, 4)},
+        "overhead": {"prefill_plain_causal_ms": round(plain_ms, 3),
+                     "prefill_bifocal_over_plain": round(call_ms / plain_ms, 4),
+                     "decode_plain_us_per_step": round(dec_plain_us, 2),
+                     "decode_bifocal_over_plain": round(dec_us / dec_plain_us, 4)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -539,7 +539,9 @@ hipError_t jl_launch_decode_bf16(const void* q, const void* k_cache, const void*
   const int nsub = decode_nsub(L);
   const int nwg = (int)decode_nwg(L);
   const int NG = Hq / Hkv;
-  const int w0c = w0 > L ? (int)L : (int)w0;
+  // With G = 1 the aliased positions are the absolute ones (Delta = 0): every
+  // key takes the base path, and the angle table is never built.
+  const int w0c = (w0 > L || G == 1) ? (int)L : (int)w0;
   float* part_ml = (float*)workspace;
   float* part_o = part_ml + (int64_t)nwg * Hq * 2;
   const float sl2 = scale * LOG2E;
