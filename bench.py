@@ -286,6 +286,24 @@ def main():
     dec_plain_us = ev.elapsed_ms(e0, e1) * 1e3 / args.decode_steps
     torch.cuda.synchronize()
 
+    # decode step time on both sides of the G boundaries (the cache is the same; only L moves)
+    def decode_at(Lx, i):
+        kc, vc = caches[i % n_caches]
+        jl.decode(qd, kc, vc, Lx, w0=dcfg.w0, w_pretrained=dcfg.w_pretrained, rope_base=dcfg.rope_base,
+                  out=od, lse=lsed, workspace=wsd)
+
+    boundary = {}
+    for Lx in (32768, 32769, 65536, 65537):
+        for i in range(4):
+            decode_at(Lx, i)
+        torch.cuda.synchronize()
+        ev.record(e0, stream)
+        for i in range(100):
+            decode_at(Lx, i)
+        ev.record(e1, stream)
+        boundary[str(Lx)] = round(ev.elapsed_ms(e0, e1) * 1e3 / 100, 2)
+    torch.cuda.synchronize()
+
     tflops = F3 / (call_ms * 1e-3) / 1e12
     pass2_tflops = Fc / (pass2_ms * 1e-3) / 1e12
     dec_gbs = kv_bytes / (dec_us * 1e-6) / 1e9
@@ -332,7 +350,8 @@ def main():
         "overhead": {"prefill_plain_causal_ms": round(plain_ms, 3),
                      "prefill_bifocal_over_plain": round(call_ms / plain_ms, 4),
                      "decode_plain_us_per_step": round(dec_plain_us, 2),
-                     "decode_bifocal_over_plain": round(dec_us / dec_plain_us, 4)},
+                     "decode_bifocal_over_plain": round(dec_us / dec_plain_us, 4),
+                     "decode_us_per_step_across_g_boundaries": boundary},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

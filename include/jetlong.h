@@ -121,6 +121,23 @@ int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_cache, i
                       int64_t w_pretrained, double rope_base, float softmax_scale,
                       void* workspace, size_t* workspace_bytes, void* hip_stream);
 
+/*
+ * Base RoPE of n consecutive rows: y[r][h][:] = R(pos0 + r) x[r][h][:],
+ * half-split pairs (m, m + head_dim/2) at theta_m = rope_base^(-2m/head_dim),
+ * with the same angle arithmetic as the prefill's base grid.  It builds or
+ * extends the decode cache of keys rotated at their absolute positions and
+ * rotates the newest query (technical summary, Methodology item 2: the cache
+ * holds base keys; the correction rotation is decode's own business).
+ *
+ *   x, y       [n_rows, num_heads, head_dim] dtype, device; y may equal x
+ *              (in place), otherwise the ranges must not overlap
+ *   pos0       position of row 0, >= 0; pos0 + n_rows - 1 < 2^31
+ *   head_dim   even, <= 128
+ *   n_rows == 0 does nothing.
+ */
+int jl_rope_rows(const void* x, void* y, int64_t n_rows, int32_t num_heads, int32_t head_dim,
+                 jl_dtype dtype, int64_t pos0, double rope_base, void* hip_stream);
+
 /* Message describing the last non-JL_OK return on the calling thread. */
 const char* jl_last_error(void);
 

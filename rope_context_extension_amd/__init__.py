@@ -61,6 +61,9 @@ def lib() -> ctypes.CDLL:
             c.c_void_p, c.c_void_p, c.c_void_p, c.c_int64, c.c_void_p, c.c_void_p,
             c.c_int32, c.c_int32, c.POINTER(c.c_int32), c.c_int32, c.c_int, c.c_int64, c.c_int64,
             c.c_double, c.c_float, c.c_void_p, c.POINTER(c.c_size_t), c.c_void_p]
+        L.jl_rope_rows.restype = c.c_int
+        L.jl_rope_rows.argtypes = [c.c_void_p, c.c_void_p, c.c_int64, c.c_int32, c.c_int32, c.c_int,
+                                   c.c_int64, c.c_double, c.c_void_p]
         L.jl_test_group_size_device.restype = c.c_int
         L.jl_test_group_size_device.argtypes = [c.c_void_p, c.c_int64, c.c_int64, c.c_void_p, c.c_void_p]
         L.jl_test_remote_pos_device.restype = c.c_int
@@ -209,3 +212,18 @@ def decode(q, k_cache, v_cache, L: int, *, w0: int, w_pretrained: int, rope_base
                                    0.0 if scale is None else float(scale), _ptr(workspace),
                                    ctypes.byref(n), _stream(q.device)))
     return o, (lse if return_lse else None)
+
+
+def rope_rows(x, pos0: int, *, rope_base: float, out=None):
+    """Base RoPE of the rows of x [n, H, d] (bf16 or fp32) at positions pos0,
+    pos0 + 1, ...; out may be x itself.  Returns out."""
+    import torch
+    if x.dim() != 3 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [n, H, d] tensor")
+    o = torch.empty_like(x) if out is None else out
+    if o.shape != x.shape or o.dtype != x.dtype or not o.is_contiguous():
+        raise ValueError("out must match x")
+    n, H, d = x.shape
+    _check(lib().jl_rope_rows(_ptr(x), _ptr(o), n, H, d, _dtype_code(x), int(pos0), float(rope_base),
+                              _stream(x.device)))
+    return o

@@ -267,6 +267,26 @@ JL_EXPORT int jl_bifocal_decode(const void* q, const void* k_cache, const void* 
   return JL_OK;
 }
 
+JL_EXPORT int jl_rope_rows(const void* x, void* y, int64_t n_rows, int32_t num_heads, int32_t head_dim,
+                           jl_dtype dtype, int64_t pos0, double rope_base, void* hip_stream) {
+  if (dtype != JL_BF16 && dtype != JL_FP32) return fail(JL_EINVAL, "unknown dtype %d", (int)dtype);
+  if (n_rows < 0) return fail(JL_EINVAL, "n_rows < 0");
+  if (pos0 < 0) return fail(JL_EINVAL, "pos0 < 0");
+  if (num_heads < 1) return fail(JL_EINVAL, "num_heads must be >= 1");
+  if (head_dim < 2 || head_dim % 2 || head_dim / 2 > JL_MAX_HALF)
+    return fail(JL_EUNSUPPORTED, "head_dim must be even and <= %d", 2 * JL_MAX_HALF);
+  if (!(rope_base > 0.0) || !isfinite(rope_base)) return fail(JL_EINVAL, "rope_base must be finite and > 0");
+  if (n_rows > 0 && pos0 + n_rows - 1 > (int64_t)INT32_MAX) return fail(JL_EUNSUPPORTED, "positions >= 2^31");
+  if (n_rows == 0) return JL_OK;
+  if (!x || !y) return fail(JL_EINVAL, "x and y must be device pointers");
+  JlFreqs fr;
+  build_freqs(&fr, head_dim, rope_base);
+  hipError_t e = jl_launch_rope_rows(x, y, dtype == JL_BF16 ? 2 : 4, n_rows, num_heads, head_dim, pos0, fr,
+                                     (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "rope launch");
+  return JL_OK;
+}
+
 // ------------------------------------------------------------------ test hooks
 
 JL_EXPORT int jl_set_profile_events(void* before, void* mid, void* after) {

@@ -83,6 +83,9 @@ int64_t jl_prefill_t_pad(int64_t total_tokens);
 hipError_t jl_launch_rope_prepass(const void* q, const void* k, const JlPrefillWs& ws, int elem_bytes,
                                   int64_t total_tokens, int32_t Hq, int32_t Hkv, int32_t d,
                                   const JlSeqs& seqs, const JlFreqs& fr, float qscale, hipStream_t st);
+// base RoPE of n rows [n][H][d] at positions pos0 .. pos0 + n - 1 (y may alias x)
+hipError_t jl_launch_rope_rows(const void* x, void* y, int elem_bytes, int64_t n, int32_t H, int32_t d,
+                               int64_t pos0, const JlFreqs& fr, hipStream_t st);
 hipError_t jl_launch_transpose_v(const void* v, const JlPrefillWs& ws, const JlSeqs& seqs,
                                  int32_t Hkv, hipStream_t st);
 

@@ -121,6 +121,31 @@ __global__ void __launch_bounds__(256) rope_prepass_kernel(
   }
 }
 
+// Base RoPE of n consecutive rows x[r][h][:] at positions pos0 + r (one
+// thread per (row, m), every head of the row with one sin/cos evaluation):
+// the rotation the prefill pre-pass applies on the base grid, for callers
+// that build or extend a decode cache of base-rotated keys, or rotate the
+// newest query (technical summary on gist.science, Methodology item 2: the
+// cache holds keys rotated at their absolute positions).  y may alias x.
+template <typename T>
+__global__ void __launch_bounds__(256) rope_rows_kernel(const T* x, T* y, int64_t n, int H, int d,
+                                                        int64_t pos0, JlFreqs fr) {
+  const int half = d >> 1;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n * half) return;
+  const int64_t r = e / half;
+  const int m = (int)(e - r * half);
+  float c, s;
+  jl_rope_sincos((int32_t)(pos0 + r), fr.turn_frac[m], &s, &c);
+  for (int h = 0; h < H; ++h) {
+    const T* xr = x + (r * H + h) * d;
+    T* yr = y + (r * H + h) * d;
+    const float x1 = ld_f(xr + m), x2 = ld_f(xr + m + half);
+    st_f(yr + m, x1 * c - x2 * s);
+    st_f(yr + m + half, x2 * c + x1 * s);
+  }
+}
+
 // v [T][Hkv][128] bf16 -> vt [Hkv][vt_cols / 64][128][64] (V^T in 64-key
 // tiles), 64 tokens of one sequence per block through LDS; keys past the
 // sequence end are zero.
@@ -192,5 +217,16 @@ hipError_t jl_launch_transpose_v(const void* v, const JlPrefillWs& ws, const JlS
   if (max_len == 0) return hipSuccess;
   dim3 grid((unsigned)((max_len + 63) / 64), (unsigned)Hkv, (unsigned)seqs.nseq);
   transpose_v_kernel<<<grid, 256, 0, st>>>((const __bf16*)v, (__bf16*)ws.vt, seqs.vt_cols, Hkv, seqs);
+  return hipGetLastError();
+}
+
+hipError_t jl_launch_rope_rows(const void* x, void* y, int elem_bytes, int64_t n, int32_t H, int32_t d,
+                               int64_t pos0, const JlFreqs& fr, hipStream_t st) {
+  const int64_t work = n * (d / 2);
+  const unsigned blocks = (unsigned)((work + 255) / 256);
+  if (elem_bytes == 2)
+    rope_rows_kernel<__bf16><<<blocks, 256, 0, st>>>((const __bf16*)x, (__bf16*)y, n, H, d, pos0, fr);
+  else
+    rope_rows_kernel<float><<<blocks, 256, 0, st>>>((const float*)x, (float*)y, n, H, d, pos0, fr);
   return hipGetLastError();
 }

@@ -132,3 +132,18 @@ def test_decode_workspace_too_small_is_enospc():
     _, n = _dec()
     rc, _ = _dec(ws=0x1000, nbytes=n - 1)
     assert rc == JL_ENOSPC
+
+
+def test_rope_rows_rejects_before_launch():
+    f = L.jl_rope_rows
+    assert f(None, None, 0, 2, 128, jl.BF16, 0, 1e4, None) == JL_OK            # empty: no-op
+    assert f(None, None, -1, 2, 128, jl.BF16, 0, 1e4, None) == JL_EINVAL
+    assert f(None, None, 4, 2, 128, jl.BF16, -1, 1e4, None) == JL_EINVAL
+    assert f(None, None, 4, 0, 128, jl.BF16, 0, 1e4, None) == JL_EINVAL
+    assert f(None, None, 4, 2, 127, jl.BF16, 0, 1e4, None) == JL_EUNSUPPORTED
+    assert f(None, None, 4, 2, 256, jl.BF16, 0, 1e4, None) == JL_EUNSUPPORTED
+    assert f(None, None, 4, 2, 128, jl.BF16, 2**31 - 2, 1e4, None) == JL_EUNSUPPORTED
+    assert f(None, None, 4, 2, 128, jl.BF16, 0, -1.0, None) == JL_EINVAL
+    assert f(None, None, 4, 2, 128, 7, 0, 1e4, None) == JL_EINVAL
+    assert f(None, None, 4, 2, 128, jl.BF16, 0, 1e4, None) == JL_EINVAL       # null pointers
+    assert b"device pointers" in L.jl_last_error()
