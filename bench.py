@@ -18,6 +18,10 @@ Prints ONE JSON line:
             counter summary when it was measured on the current kernel source;
   decode    sustained decode steps (KV bytes 2 L Hkv d 2 per step) and the
             split-K kernel alone, against the HBM peak;
+  disjoint_merge  the same prefill with the far pairs computed directly (a
+            window pass on the base grid plus a far-only pass on the remote
+            grid, merged with two positive weights): exactly the causal pair
+            count, so its actual FLOPs are 4 d Hq L(L+1)/2;
   overhead  the bifocal calls over plain attention at the same shapes (the same
             library with w_pretrained = L, i.e. G = 1: plain causal RoPE prefill
             and Delta-free decode);
@@ -53,6 +57,14 @@ DECODE_TRAFFIC = (os.path.join(ROOT, "profiles", "decode_split_traffic_qwen3_8b_
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def far_flops(L: int, Hq: int, d: int, w0: int, first_rows: int = 128):
+    """FLOPs of the far-only pass over rows >= first_rows: 4 d Hq sum_i max(0, i + 1 - w0)."""
+    n = max(0, L - max(w0, first_rows))              # rows with far keys beyond first_rows
+    hi = L - w0                                      # far count of the last row
+    lo = hi - n + 1
+    return 4 * d * Hq * (n * (lo + hi) // 2) if n > 0 else 0
 
 
 def prefill_flops(L: int, Hq: int, d: int, w0: int):
@@ -256,6 +268,30 @@ def main():
     dec_us = ev.elapsed_ms(e0, e1) * 1e3 / args.decode_steps
     torch.cuda.synchronize()
 
+    # the disjoint merge variant on the same inputs (own output buffers)
+    od_ = torch.empty_like(o)
+    lsed_ = torch.empty_like(lse)
+
+    def prefill_disjoint():
+        jl.prefill(q, k, v, w0=cfg.w0, w_pretrained=cfg.w_pretrained, rope_base=cfg.rope_base, out=od_,
+                   lse=lsed_, workspace=ws, disjoint=True)
+
+    prefill_disjoint()
+    torch.cuda.synchronize()
+    drec = [[ev.create() for _ in range(5)] for _ in range(3)]
+    for r in drec:
+        ev.record(r[0], stream)
+        lib.jl_set_profile_events(r[1], r[2], r[3])
+        prefill_disjoint()
+        lib.jl_set_profile_events(None, None, None)
+        ev.record(r[4], stream)
+    torch.cuda.synchronize()
+    dj_ms = float(np.mean([ev.elapsed_ms(r[0], r[4]) for r in drec]))
+    dj_far_ms = float(np.mean([ev.elapsed_ms(r[1], r[2]) for r in drec]))
+    Ff = far_flops(L, Hq, d, cfg.w0)
+    dj_do = float((od_.float() - o.float()).abs().max().item())
+    del od_, lsed_
+
     # overhead against plain attention at the same shapes: G = 1 (w_pretrained = L) makes every
     # aliased position the absolute one, so the same library runs plain causal RoPE attention
     # (prefill: one full-causal pass) and Delta-free decode (every key on the base path)
@@ -311,7 +347,8 @@ def main():
     log(f"[bench] prefill call {call_ms:.2f} ms -> {tflops:.1f} TFLOP/s (F_3pass); attention kernels "
         f"{attn_ms:.2f} ms; pass 2 {pass2_ms:.2f} ms -> {pass2_tflops:.1f} TFLOP/s; decode {dec_us:.1f} "
         f"us/step ({dec_gbs:.0f} GB/s), split-K {split_us:.1f} us ({split_gbs:.0f} GB/s); plain causal "
-        f"prefill {plain_ms:.2f} ms, Delta-free decode {dec_plain_us:.1f} us")
+        f"prefill {plain_ms:.2f} ms, Delta-free decode {dec_plain_us:.1f} us; disjoint merge {dj_ms:.2f} ms "
+        f"(far pass {dj_far_ms:.2f} ms)")
 
     out = {
         "metric": METRIC,
@@ -347,6 +384,13 @@ def main():
                                 "traffic": read_traffic(DECODE_TRAFFIC),
                                 "kernel": "decode_split_kernel", "us_per_launch": round(split_us, 2)},
                    "step_frac_hbm": round(dec_gbs / PEAK_HBM_GBS, 4)},
+        "disjoint_merge": {"call_ms": round(dj_ms, 3), "tflops_actual": round(Fc / (dj_ms * 1e-3) / 1e12, 2),
+                           "frac_actual": round(Fc / (dj_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                           "three_pass_over_disjoint": round(call_ms / dj_ms, 4),
+                           "far_pass_ms": round(dj_far_ms, 3),
+                           "far_pass_tflops": round(Ff / (dj_far_ms * 1e-3) / 1e12, 2),
+                           "far_pass_flops": Ff,
+                           "max_abs_diff_vs_three_pass": dj_do},
         "overhead": {"prefill_plain_causal_ms": round(plain_ms, 3),
                      "prefill_bifocal_over_plain": round(call_ms / plain_ms, 4),
                      "decode_plain_us_per_step": round(dec_plain_us, 2),

@@ -96,6 +96,28 @@ int jl_bifocal_prefill(const void* q, const void* k, const void* v, void* o, flo
                        size_t* workspace_bytes, void* hip_stream);
 
 /*
+ * The same bifocal prefill with the far pairs computed directly instead of as
+ * a difference of two passes (technical summary, Methodology item 2: pairs
+ * inside the local window see base-RoPE q/k, all farther pairs see the
+ * remote grid).  Rows >= 128 of every sequence run the window pass on the
+ * base grid and one pass over the pairs with i - j >= w0 on the remote grid,
+ * merged as out = (z1 o1 + zf of) / (z1 + zf): both weights are positive, so
+ * no term cancels (the three-pass form subtracts z3 o3 from z2 o2, which
+ * loses relative precision where the far mass is small against the window
+ * mass).  Rows < 128 of a sequence take the three-pass path.
+ *
+ * Arguments, layouts, workspace size (query it through jl_bifocal_prefill or
+ * this call: they are equal) and errors are those of jl_bifocal_prefill;
+ * JL_FP32 is JL_EUNSUPPORTED here.
+ */
+int jl_bifocal_prefill_disjoint(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const int64_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                                int32_t num_q_heads, int32_t num_kv_heads, const int32_t* q_to_kv,
+                                int32_t head_dim, jl_dtype dtype, int64_t w0, int64_t w_pretrained,
+                                double rope_base, float softmax_scale, void* workspace,
+                                size_t* workspace_bytes, void* hip_stream);
+
+/*
  * One single-batch generation step against a KV cache of base-RoPE keys
  * (technical summary, Methodology item 2: the cache holds uncompressed base
  * keys at their absolute positions; the correction rotation Delta is applied

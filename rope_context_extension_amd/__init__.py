@@ -49,13 +49,14 @@ def lib() -> ctypes.CDLL:
         L.jl_group_size.argtypes = [c.c_int64, c.c_int64]
         L.jl_last_error.restype = c.c_char_p
         L.jl_last_error.argtypes = []
-        L.jl_bifocal_prefill.restype = c.c_int
-        L.jl_bifocal_prefill.argtypes = [
-            c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,      # q k v o lse
-            c.POINTER(c.c_int64), c.c_int32, c.c_int64,                       # cu_seqlens nseq T
-            c.c_int32, c.c_int32, c.POINTER(c.c_int32),                       # Hq Hkv q_to_kv
-            c.c_int32, c.c_int, c.c_int64, c.c_int64, c.c_double, c.c_float,  # d dtype w0 wpt base scale
-            c.c_void_p, c.POINTER(c.c_size_t), c.c_void_p]                    # ws ws_bytes stream
+        for f in (L.jl_bifocal_prefill, L.jl_bifocal_prefill_disjoint):
+            f.restype = c.c_int
+            f.argtypes = [
+                c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,      # q k v o lse
+                c.POINTER(c.c_int64), c.c_int32, c.c_int64,                       # cu_seqlens nseq T
+                c.c_int32, c.c_int32, c.POINTER(c.c_int32),                       # Hq Hkv q_to_kv
+                c.c_int32, c.c_int, c.c_int64, c.c_int64, c.c_double, c.c_float,  # d dtype w0 wpt base scale
+                c.c_void_p, c.POINTER(c.c_size_t), c.c_void_p]                    # ws ws_bytes stream
         L.jl_bifocal_decode.restype = c.c_int
         L.jl_bifocal_decode.argtypes = [
             c.c_void_p, c.c_void_p, c.c_void_p, c.c_int64, c.c_void_p, c.c_void_p,
@@ -121,10 +122,10 @@ def _dtype_code(t) -> int:
 
 
 def _prefill_call(q, k, v, o, lse, cu, nseq, T, Hq, Hkv, kvmap, d, dt, w0, w_pt, base, scale,
-                  ws, ws_bytes, stream):
-    return lib().jl_bifocal_prefill(q, k, v, o, lse, cu, nseq, T, Hq, Hkv, kvmap, d, dt, int(w0),
-                                    int(w_pt), float(base), float(scale), ws, ctypes.byref(ws_bytes),
-                                    stream)
+                  ws, ws_bytes, stream, disjoint=False):
+    fn = lib().jl_bifocal_prefill_disjoint if disjoint else lib().jl_bifocal_prefill
+    return fn(q, k, v, o, lse, cu, nseq, T, Hq, Hkv, kvmap, d, dt, int(w0), int(w_pt), float(base),
+              float(scale), ws, ctypes.byref(ws_bytes), stream)
 
 
 def prefill_workspace_bytes(total_tokens: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
@@ -140,10 +141,12 @@ def prefill_workspace_bytes(total_tokens: int, num_q_heads: int, num_kv_heads: i
 
 def prefill(q, k, v, *, w0: int, w_pretrained: int, rope_base: float, cu_seqlens=None,
             scale: Optional[float] = None, q_to_kv=None, out=None, lse=None, return_lse=True,
-            workspace=None):
+            workspace=None, disjoint: bool = False):
     """Bifocal causal prefill.  q [T, Hq, d], k/v [T, Hkv, d] raw projections
     (bf16 or fp32, CUDA, contiguous).  Returns (o [T, Hq, d], lse [Hq, T] fp32
-    or None).  cu_seqlens: host list of packed sequence offsets."""
+    or None).  cu_seqlens: host list of packed sequence offsets.  disjoint:
+    merge the window pass with a far-only pass instead of the three-pass
+    inclusion-exclusion (bf16 only)."""
     import torch
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be GPU tensors")
@@ -167,7 +170,8 @@ def prefill(q, k, v, *, w0: int, w_pretrained: int, rope_base: float, cu_seqlens
     n = ctypes.c_size_t(workspace.numel())
     _check(_prefill_call(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse) if return_lse else None,
                          cu, nseq, T, Hq, Hkv, kvmap, d, dt, w0, w_pretrained, rope_base,
-                         0.0 if scale is None else scale, _ptr(workspace), n, _stream(q.device)))
+                         0.0 if scale is None else scale, _ptr(workspace), n, _stream(q.device),
+                         disjoint))
     return o, (lse if return_lse else None)
 
 

@@ -82,12 +82,12 @@ JL_EXPORT int64_t jl_group_size(int64_t L, int64_t w_pretrained) {
 
 JL_EXPORT const char* jl_last_error(void) { return g_err; }
 
-JL_EXPORT int jl_bifocal_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
-                                 const int64_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
-                                 int32_t num_q_heads, int32_t num_kv_heads, const int32_t* q_to_kv,
-                                 int32_t head_dim, jl_dtype dtype, int64_t w0, int64_t w_pretrained,
-                                 double rope_base, float softmax_scale, void* workspace,
-                                 size_t* workspace_bytes, void* hip_stream) {
+static int prefill_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int64_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                        int32_t num_q_heads, int32_t num_kv_heads, const int32_t* q_to_kv,
+                        int32_t head_dim, jl_dtype dtype, int64_t w0, int64_t w_pretrained,
+                        double rope_base, float softmax_scale, void* workspace,
+                        size_t* workspace_bytes, void* hip_stream, bool disjoint) {
   if (workspace_bytes == nullptr) return fail(JL_EINVAL, "workspace_bytes is NULL");
   if (total_tokens < 0) return fail(JL_EINVAL, "total_tokens < 0");
   if (dtype != JL_BF16 && dtype != JL_FP32) return fail(JL_EINVAL, "unknown dtype %d", (int)dtype);
@@ -96,6 +96,7 @@ JL_EXPORT int jl_bifocal_prefill(const void* q, const void* k, const void* v, vo
   JlHeadMap hm;
   rc = build_head_map(&hm, num_q_heads, num_kv_heads, q_to_kv);
   if (rc) return rc;
+  if (disjoint && dtype != JL_BF16) return fail(JL_EUNSUPPORTED, "the disjoint merge is built for bf16 only");
   if (dtype == JL_BF16 && head_dim != 128) return fail(JL_EUNSUPPORTED, "bf16 prefill needs head_dim 128");
   if (dtype == JL_FP32 && head_dim != 64 && head_dim != 128)
     return fail(JL_EUNSUPPORTED, "fp32 prefill needs head_dim 64 or 128");
@@ -204,7 +205,7 @@ JL_EXPORT int jl_bifocal_prefill(const void* q, const void* k, const void* v, vo
     if (e != hipSuccess) return hip_fail(e, "v transpose launch");
     if (g_ev_before) (void)hipEventRecord(g_ev_before, st);
     e = jl_launch_prefill_bf16(ws, o, lse, total_tokens, num_q_heads, num_kv_heads, hm, pl.seqs, w0,
-                               scale, pl.max_len, st);
+                               scale, pl.max_len, disjoint, st);
     if (e != hipSuccess) return hip_fail(e, "bf16 prefill launch");
     if (g_ev_after) (void)hipEventRecord(g_ev_after, st);
   } else {
@@ -215,6 +216,28 @@ JL_EXPORT int jl_bifocal_prefill(const void* q, const void* k, const void* v, vo
     if (g_ev_after) (void)hipEventRecord(g_ev_after, st);
   }
   return JL_OK;
+}
+
+JL_EXPORT int jl_bifocal_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 const int64_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                                 int32_t num_q_heads, int32_t num_kv_heads, const int32_t* q_to_kv,
+                                 int32_t head_dim, jl_dtype dtype, int64_t w0, int64_t w_pretrained,
+                                 double rope_base, float softmax_scale, void* workspace,
+                                 size_t* workspace_bytes, void* hip_stream) {
+  return prefill_impl(q, k, v, o, lse, cu_seqlens, num_seqs, total_tokens, num_q_heads, num_kv_heads, q_to_kv,
+                      head_dim, dtype, w0, w_pretrained, rope_base, softmax_scale, workspace, workspace_bytes,
+                      hip_stream, false);
+}
+
+JL_EXPORT int jl_bifocal_prefill_disjoint(const void* q, const void* k, const void* v, void* o, float* lse,
+                                          const int64_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                                          int32_t num_q_heads, int32_t num_kv_heads, const int32_t* q_to_kv,
+                                          int32_t head_dim, jl_dtype dtype, int64_t w0, int64_t w_pretrained,
+                                          double rope_base, float softmax_scale, void* workspace,
+                                          size_t* workspace_bytes, void* hip_stream) {
+  return prefill_impl(q, k, v, o, lse, cu_seqlens, num_seqs, total_tokens, num_q_heads, num_kv_heads, q_to_kv,
+                      head_dim, dtype, w0, w_pretrained, rope_base, softmax_scale, workspace, workspace_bytes,
+                      hip_stream, true);
 }
 
 JL_EXPORT int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_cache, int64_t L,

@@ -94,9 +94,11 @@ hipError_t jl_launch_prefill_fp32(const JlPrefillWs& ws, const float* v, float* 
                                   const JlHeadMap& hm, const JlSeqs& seqs, int64_t w0, float scale,
                                   int32_t max_len, hipStream_t st);
 
+// disjoint: rows >= 128 merge pass 1 with a far-only pass (pairs i - j >= w0)
+// instead of pass 2 minus pass 3
 hipError_t jl_launch_prefill_bf16(const JlPrefillWs& ws, void* o, float* lse, int64_t total_tokens,
                                   int32_t Hq, int32_t Hkv, const JlHeadMap& hm, const JlSeqs& seqs,
-                                  int64_t w0, float scale, int32_t max_len, hipStream_t st);
+                                  int64_t w0, float scale, int32_t max_len, bool disjoint, hipStream_t st);
 
 // decode
 size_t jl_decode_workspace_bytes(int64_t L, int32_t Hq, int32_t d);

@@ -190,7 +190,8 @@ struct PassState {
 constexpr float RESCALE_LOG2 = 8.f;
 
 // Index masks of a tile: KIND 0 keeps dist >= 0 (causal), KIND 1 keeps
-// 0 <= dist < w0 (window).  Masked scores become -inf.
+// 0 <= dist < w0 (window), KIND 2 keeps dist >= w0 (the far pairs).  Masked
+// scores become -inf.
 template <int KIND>
 __device__ inline void mask_tile(f32x16* s, int myrow, int j0, int w0, int g) {
   const int d0 = myrow - j0 - 8 * g;
@@ -202,7 +203,7 @@ __device__ inline void mask_tile(f32x16* s, int myrow, int j0, int w0, int g) {
       // of the key offset; the window test 0 <= dist < w0 is one unsigned
       // compare
       const int c = key_of(sb, i, 0);
-      const bool keep = KIND == 0 ? d0 >= c : (uint32_t)(d0 - c) < (uint32_t)w0;
+      const bool keep = KIND == 0 ? d0 >= c : KIND == 2 ? d0 - w0 >= c : (uint32_t)(d0 - c) < (uint32_t)w0;
       s[sb][i] = keep ? s[sb][i] : -INFINITY;
     }
 }
@@ -263,13 +264,14 @@ struct WaveRows {
 // Does this wave have any (causal / window) pair in the key tile at j0?
 template <int KIND>
 __device__ inline bool wave_has_work(int j0, const WaveRows& wr) {
-  if (j0 > wr.iw + 31) return false;
+  if (j0 > wr.iw + 31 - (KIND == 2 ? wr.w0 : 0)) return false;
   if (KIND == 1 && j0 + BK - 1 < wr.iw - wr.w0 + 1) return false;
   return true;
 }
 
 template <int KIND>
 __device__ inline bool wave_needs_mask(int j0, const WaveRows& wr) {
+  if (KIND == 2) return j0 + BK - 1 > wr.iw - wr.w0;         // some pair has dist < w0
   bool m = j0 + BK - 1 > wr.iw;                              // some pair has dist < 0
   if (KIND == 1) m = m || (j0 < wr.iw + 31 - wr.w0 + 1);     // some pair has dist >= w0
   return m;
@@ -403,6 +405,7 @@ struct PrefillArgs {
   int64_t t_pad;
   int64_t w0;
   int Hq;
+  int disjoint;       // far-only pass + window pass instead of the three passes (rows >= 128)
   float sl2;          // factor from score products to log2 units (1: q arrives pre-scaled)
 };
 
@@ -920,11 +923,16 @@ constexpr int O1_BYTES = PP_NT * 128;
 // tile one after the other (window, base q/k, then window, remote q/k) and
 // the inclusion-exclusion merge with pass 2's output; sequences with
 // w0 >= L run pass 1 over the whole causal range and write O directly.
+// The disjoint variant: ROLE 4 is the far pass (remote q/k, pairs with
+// i - j >= w0 only, written where pass 2's output goes) and ROLE 5 is pass 1
+// merged with it, O = (z1 o1 + zf of) / (z1 + zf), which has no cancelling
+// terms; ROLE 0 then serves only the G = 1 sequences.
 template <int ROLE>
 __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlHeadMap hm, JlSeqs seqs,
                                                              JlSched sc) {
-  static_assert(ROLE == 0 || ROLE == 3, "pass roles of the 256-row kernel");
-  constexpr int KIND = ROLE == 0 ? 0 : 1;
+  static_assert(ROLE == 0 || ROLE == 3 || ROLE == 4 || ROLE == 5, "pass roles of the 256-row kernel");
+  constexpr int KIND = ROLE == 0 ? 0 : ROLE == 4 ? 2 : 1;
+  constexpr bool BASE = ROLE == 3 || ROLE == 5;      // the first pass runs on the base grid
   __shared__ __align__(1024) char smem[2 * (KT_BYTES + VT_BYTES) + (ROLE == 3 ? O1_BYTES : 0)];
   int h, b, u;
   if (!block_item<false>(sc, A.Hq, &h, &b, &u)) return;
@@ -938,8 +946,9 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
   if (r0 >= L) return;
   const bool only1 = A.w0 >= (int64_t)L;
   const bool only2 = seqs.G[b] == 1 && !only1;
-  if (ROLE == 0 && only1) return;
-  if (ROLE == 3 && only2) return;
+  if (ROLE == 0 && (only1 || (A.disjoint && !only2))) return;
+  if ((ROLE == 3 || ROLE == 5) && only2) return;
+  if (ROLE == 4 && (only1 || only2)) return;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -954,7 +963,7 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
   const int tw0 = (r0 - w0 + 1) > 0 ? (r0 - w0 + 1) / BK : 0;
   const int64_t vtiles = seqs.vt_cols / 64;
   const int64_t krow = ((int64_t)kvh * A.t_pad + s0) * D;
-  const __bf16* ksrc = (ROLE == 3 ? A.kb : A.kr) + krow;
+  const __bf16* ksrc = (BASE ? A.kb : A.kr) + krow;
   const __bf16* vsrc =
       A.vt + ((int64_t)kvh * vtiles + __builtin_amdgcn_readfirstlane(seqs.vstart[b]) / 64) * (D * 64);
   PpTiles T;
@@ -966,7 +975,7 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
   T.wave = wave;
   bf16x8 qf[8];
   if (live) {
-    load_q(qf, (ROLE == 3 ? A.qb : A.qr) + ((int64_t)h * A.t_pad + s0 + wr.myrow) * D, g);
+    load_q(qf, (BASE ? A.qb : A.qr) + ((int64_t)h * A.t_pad + s0 + wr.myrow) * D, g);
   } else {
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) qf[kb] = bf16x8{};
@@ -975,8 +984,14 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16{};
   PpState st{-INFINITY, 0.f, f32x16{}};
-  T.t0 = ROLE == 0 || only1 ? 0 : tw0;
-  T.n = tiles_end - T.t0;
+  T.t0 = ROLE == 0 || ROLE == 4 || only1 ? 0 : tw0;
+  int t_end = tiles_end;
+  if (ROLE == 4) {
+    // far pairs of the tile's rows end at key r0 + 255 - w0
+    const int last = r0 + PP_BQ - 1 - w0;
+    t_end = last < 0 ? 0 : min(tiles_end, last / BK + 1);
+  }
+  T.n = t_end - T.t0;
   if (T.n > 0) pp_run<KIND>(T, qf, st, o, wr, lane);
   const float l = pair_sum(st.l);
   const float lam = l > 0.f ? st.m + __log2f(l) : -INFINITY;
@@ -999,7 +1014,8 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
     if (A.lse != nullptr && g == 0) A.lse[ridx] = lam * LN2;
     return;
   }
-  if constexpr (ROLE == 0) {
+  if constexpr (ROLE == 0 || ROLE == 4) {
+    // rows without a far key (i < w0) store o = 0 and lam = -inf
     if (!row_ok) return;
     float* orow = A.o2 + ridx * D;
     const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -1011,6 +1027,31 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
             make_float4(o[db][4 * q4] * inv, o[db][4 * q4 + 1] * inv, o[db][4 * q4 + 2] * inv,
                         o[db][4 * q4 + 3] * inv);
     if (g == 0) A.lse2[ridx] = lam;
+  } else if constexpr (ROLE == 5) {
+    // disjoint merge: window (base grid) and far (remote grid) are two
+    // halves of one softmax, so both weights are positive
+    if (!row_ok) return;
+    const float lamf = A.lse2[ridx];
+    const float M = fmaxf(lam, lamf);                    // lam is finite: the diagonal is in the window
+    const float c1 = __builtin_amdgcn_exp2f(st.m - M);   // o carries exp2(s - st.m)
+    const float zf = __builtin_amdgcn_exp2f(lamf - M);
+    const float Z = __builtin_amdgcn_exp2f(lam - M) + zf;
+    const float inv = 1.f / Z;
+    const float* ofrow = A.o2 + ridx * D;
+    __bf16* orow = A.out + ((s0 + wr.myrow) * A.Hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = db * 32 + 8 * q4 + 4 * g;
+        const float4 vf = *(const float4*)(ofrow + d0);
+        const float ofv[4] = {vf.x, vf.y, vf.z, vf.w};
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)((c1 * o[db][4 * q4 + e] + zf * ofv[e]) * inv);
+        *(bf16x4*)(orow + d0) = w;
+      }
+    if (A.lse != nullptr && g == 0) A.lse[ridx] = (M + __log2f(Z)) * LN2;
   } else {
     // pass 1 done: o1 (normalised, bf16) to LDS, lam1 stays in a register
     const float lam1 = lam;
@@ -1108,7 +1149,7 @@ void jl_build_sched(const JlSeqs& seqs, const JlHeadMap& hm, int Hq, JlSched* sc
 
 hipError_t jl_launch_prefill_bf16(const JlPrefillWs& ws, void* o, float* lse, int64_t total_tokens,
                                   int32_t Hq, int32_t Hkv, const JlHeadMap& hm, const JlSeqs& seqs,
-                                  int64_t w0, float scale, int32_t max_len, hipStream_t st) {
+                                  int64_t w0, float scale, int32_t max_len, bool disjoint, hipStream_t st) {
   (void)Hkv;
   (void)max_len;
   JlSched sc;
@@ -1133,9 +1174,10 @@ hipError_t jl_launch_prefill_bf16(const JlPrefillWs& ws, void* o, float* lse, in
   A.t_pad = ws.t_pad;
   A.w0 = w0;
   A.Hq = Hq;
+  A.disjoint = disjoint ? 1 : 0;
   (void)scale;        // folded into q by the RoPE pre-pass (q * scale * log2 e)
   A.sl2 = 1.f;
-  bool any_p1 = false, any_p2 = false, any_p3 = false;
+  bool any_p1 = false, any_p2 = false, any_p3 = false, any_only2 = false;
   for (int b = 0; b < seqs.nseq; ++b) {
     if (seqs.len[b] == 0) continue;
     const bool only1 = w0 >= (int64_t)seqs.len[b];
@@ -1143,18 +1185,26 @@ hipError_t jl_launch_prefill_bf16(const JlPrefillWs& ws, void* o, float* lse, in
     any_p1 |= !only2;
     any_p2 |= !only1;
     any_p3 |= !only1 && !only2;
+    any_only2 |= only2;
   }
   const unsigned nblk = (unsigned)sc.total_units * (unsigned)Hq;   // multiple of 8 when xcd_heads
   const unsigned nfirst = (unsigned)(seqs.nseq * Hq);
   // rows >= 128 in 256-row tiles (pass 2, then passes 1 and 3 fused); the
   // first 128 rows of every sequence in the split-operand kernel, pass by pass
+  // disjoint: 256-row tiles run the far pass, then pass 1 merged with it
+  // (pass 2 only for the G = 1 sequences); the first 128 rows as above
   if (any_p2) {
-    if (nblk) prefill_pp_kernel<0><<<nblk, PP_NT, 0, st>>>(A, hm, seqs, sc);
+    if (nblk && (!disjoint || any_only2)) prefill_pp_kernel<0><<<nblk, PP_NT, 0, st>>>(A, hm, seqs, sc);
     prefill_pass_kernel<0, true><<<nfirst, NT, 0, st>>>(A, hm, seqs, sc);
   }
+  if (disjoint && any_p3 && nblk) prefill_pp_kernel<4><<<nblk, PP_NT, 0, st>>>(A, hm, seqs, sc);
+  // profiling mark after the dominant launch of either form (pass 2, or the far pass)
   if (hipEvent_t mid = jl_profile_mid_event()) (void)hipEventRecord(mid, st);
   if (any_p1) {
-    if (nblk) prefill_pp_kernel<3><<<nblk, PP_NT, 0, st>>>(A, hm, seqs, sc);
+    if (nblk) {
+      if (disjoint) prefill_pp_kernel<5><<<nblk, PP_NT, 0, st>>>(A, hm, seqs, sc);
+      else prefill_pp_kernel<3><<<nblk, PP_NT, 0, st>>>(A, hm, seqs, sc);
+    }
     prefill_pass_kernel<1, true><<<nfirst, NT, 0, st>>>(A, hm, seqs, sc);
   }
   if (any_p3) prefill_pass_kernel<2, true><<<nfirst, NT, 0, st>>>(A, hm, seqs, sc);

@@ -33,12 +33,12 @@ def test_group_size_rejects():
     assert b"w_pretrained" in L.jl_last_error()
 
 
-def _pf(**kw):
+def _pf(fn="jl_bifocal_prefill", **kw):
     a = dict(q=None, k=None, v=None, o=None, lse=None, cu=None, nseq=1, T=256, Hq=4, Hkv=2, kvmap=None,
              d=128, dt=jl.BF16, w0=16, wpt=64, base=10000.0, scale=0.0, ws=None, nbytes=0)
     a.update(kw)
     n = ctypes.c_size_t(a["nbytes"])
-    rc = L.jl_bifocal_prefill(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"], a["nseq"], a["T"],
+    rc = getattr(L, fn)(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"], a["nseq"], a["T"],
                               a["Hq"], a["Hkv"], a["kvmap"], a["d"], a["dt"], a["w0"], a["wpt"],
                               a["base"], a["scale"], a["ws"], ctypes.byref(n), None)
     return rc, n.value
@@ -93,6 +93,19 @@ def test_prefill_null_tensor_is_einval():
     rc, n = _pf()
     rc2, _ = _pf(ws=0x1000, nbytes=n)
     assert rc2 == JL_EINVAL
+
+
+def test_disjoint_prefill_host_checks():
+    # same workspace as the three-pass call, same argument checks, bf16 only
+    rc, n = _pf()
+    rcd, nd = _pf(fn="jl_bifocal_prefill_disjoint")
+    assert rc == rcd == JL_OK and n == nd
+    rc, _ = _pf(fn="jl_bifocal_prefill_disjoint", dt=jl.FP32, d=64)
+    assert rc == JL_EUNSUPPORTED and b"bf16" in L.jl_last_error()
+    assert _pf(fn="jl_bifocal_prefill_disjoint", Hq=3, Hkv=2)[0] == JL_EINVAL
+    assert _pf(fn="jl_bifocal_prefill_disjoint", ws=0x1000, nbytes=n - 1, q=0x1000, k=0x1000, v=0x1000,
+               o=0x1000)[0] == JL_ENOSPC
+    assert _pf(fn="jl_bifocal_prefill_disjoint", ws=0x1000, nbytes=n)[0] == JL_EINVAL
 
 
 def _dec(**kw):

@@ -42,12 +42,14 @@ def _np(t):
     return t.double().numpy()
 
 
-def _check_full(jl, torch, L, Hq, Hkv, d, dtype, w0, wpt, base, seed, q_to_kv=None, cu=None):
-    _say(f"[prefill] L={L} Hq={Hq} Hkv={Hkv} d={d} {dtype} w0={w0} wpt={wpt} cu={cu} seed={seed}")
+def _check_full(jl, torch, L, Hq, Hkv, d, dtype, w0, wpt, base, seed, q_to_kv=None, cu=None,
+                disjoint=False):
+    _say(f"[prefill] L={L} Hq={Hq} Hkv={Hkv} d={d} {dtype} w0={w0} wpt={wpt} cu={cu} seed={seed} "
+         f"disjoint={disjoint}")
     T = L if cu is None else cu[-1]
     q, k, v = _inputs(torch, T, Hq, Hkv, d, dtype, seed)
     o, lse = _run(jl, torch, q, k, v, w0=w0, w_pretrained=wpt, rope_base=base, q_to_kv=q_to_kv,
-                  cu_seqlens=cu)
+                  cu_seqlens=cu, disjoint=disjoint)
     cus = [0, T] if cu is None else cu
     for b in range(len(cus) - 1):
         s0, s1 = cus[b], cus[b + 1]
@@ -118,6 +120,67 @@ def test_bf16_varlen_small():
                 cu=[0, 700, 701, 701, 1330, 1600])
 
 
+@pytest.mark.parametrize("L,Hq,Hkv,w0,wpt", [
+    (1000, 4, 2, 200, 300),        # G = 4, several q tiles, ragged tail
+    (777, 2, 1, 64, 200),          # G = 4, w0 = one key tile
+    (1500, 2, 2, 1, 700),          # w0 = 1
+    (640, 4, 1, 0, 160),           # w0 = 0: the far pass is the causal pass
+    (600, 2, 1, 700, 100),         # w0 >= L
+    (900, 4, 2, 100, 5000),        # G = 1
+    (1100, 2, 1, 300, 200),        # far keys begin inside the second 256-row tile
+    (129, 2, 1, 33, 40),
+    (2, 2, 1, 1, 1),
+])
+def test_bf16_disjoint_full_rows(L, Hq, Hkv, w0, wpt):
+    jl, torch = gpu_or_skip()
+    _check_full(jl, torch, L, Hq, Hkv, 128, "bf16", w0, wpt, 1e6, seed=L + 1, disjoint=True)
+
+
+def test_bf16_disjoint_varlen_and_head_map():
+    # a G = 1 sequence, a single token, an empty one, a w0 >= L one and two G > 1 ones
+    jl, torch = gpu_or_skip()
+    _check_full(jl, torch, None, 4, 2, 128, "bf16", 96, 200, 1e6, seed=11, q_to_kv=[1, 1, 0, 0],
+                cu=[0, 150, 151, 151, 240, 900, 1600], disjoint=True)
+
+
+def test_bf16_disjoint_matches_three_pass():
+    # the two merges compute the same attention: their outputs agree to the
+    # bf16 output rounding of the two paths
+    jl, torch = gpu_or_skip()
+    q, k, v = _inputs(torch, 2000, 4, 2, 128, "bf16", 21)
+    kw = dict(w0=300, w_pretrained=500, rope_base=1e6)
+    o3, l3 = _run(jl, torch, q, k, v, **kw)
+    od, ld = _run(jl, torch, q, k, v, disjoint=True, **kw)
+    _say(f"[prefill] disjoint vs three-pass: max|do|={max_abs(od, o3):.3e} lse rel={lse_rel_err(ld, l3):.3e}")
+    assert max_abs(od, o3) <= BF16_O_ATOL and lse_rel_err(ld, l3) <= BF16_LSE_RTOL
+
+
+def test_bf16_disjoint_small_far_mass():
+    """q = k = one fixed direction (plus noise) with a large norm: every
+    score peaks at distance 0, so nearly all mass sits in the window, and the
+    remote grid's window mass (distances shrunk G = 8 times) is several times
+    the base grid's.  The three-pass merge then forms the small far mass as a
+    difference of two larger window-dominated terms; the disjoint merge adds
+    two positive terms.  Both against the oracle, every row."""
+    jl, torch = gpu_or_skip()
+    L, Hq, Hkv, d, w0, wpt = 1536, 2, 1, 128, 256, 192
+    g = torch.Generator("cpu").manual_seed(23)
+    c = torch.randn((d,), generator=g)
+    c = c / c.norm() * (12.0 * d ** 0.5) ** 0.5          # scale * |c|^2 = 12 at distance 0
+    q = (c + 0.1 * torch.randn((L, Hq, d), generator=g)).bfloat16()
+    k = (c + 0.1 * torch.randn((L, Hkv, d), generator=g)).bfloat16()
+    v = torch.randn((L, Hkv, d), generator=g).bfloat16()
+    kw = dict(w0=w0, w_pretrained=wpt, rope_base=1e4)
+    oo, ll = oracle.prefill(_np(q), _np(k), _np(v), **kw)
+    errs = {}
+    for dj in (False, True):
+        o, lse = _run(jl, torch, q, k, v, disjoint=dj, **kw)
+        errs[dj] = (max_abs(o, oo), lse_rel_err(lse, ll))
+    _say(f"[prefill] small far mass: three-pass max|do|={errs[False][0]:.3e} lse rel={errs[False][1]:.3e}; "
+         f"disjoint max|do|={errs[True][0]:.3e} lse rel={errs[True][1]:.3e}")
+    assert errs[True][0] <= BF16_O_ATOL and errs[True][1] <= BF16_LSE_RTOL
+
+
 def test_bf16_empty_is_noop():
     jl, torch = gpu_or_skip()
     q = torch.empty((0, 2, 128), dtype=torch.bfloat16, device="cuda")
@@ -127,12 +190,13 @@ def test_bf16_empty_is_noop():
     assert o.shape == (0, 2, 128) and lse.shape == (2, 0)
 
 
-def _check_sampled(jl, torch, cfg, n_random, seqs_to_check=None):
+def _check_sampled(jl, torch, cfg, n_random, seqs_to_check=None, disjoint=False):
     q, k, v = W.make_prefill_inputs(cfg)
     cu = W.cu_seqlens_of(cfg.seqlens)
-    _say(f"[prefill] {cfg.name} T={cfg.total_tokens} w0={cfg.w0}")
+    _say(f"[prefill] {cfg.name} T={cfg.total_tokens} w0={cfg.w0} disjoint={disjoint}")
     o, lse = jl.prefill(q.cuda(), k.cuda(), v.cuda(), w0=cfg.w0, w_pretrained=cfg.w_pretrained,
-                        rope_base=cfg.rope_base, cu_seqlens=cu if len(cfg.seqlens) > 1 else None)
+                        rope_base=cfg.rope_base, cu_seqlens=cu if len(cfg.seqlens) > 1 else None,
+                        disjoint=disjoint)
     torch.cuda.synchronize()
     worst_o, worst_l = 0.0, 0.0
     for b in (range(len(cfg.seqlens)) if seqs_to_check is None else seqs_to_check):
@@ -185,6 +249,18 @@ def test_qwen3_1p7b_64k_g2():
 def test_qwen3_8b_128k_g4():
     jl, torch = gpu_or_skip()
     _check_sampled(jl, torch, W.QWEN3_8B_128K, n_random=8)
+
+
+def test_qwen3_8b_128k_g4_disjoint():
+    jl, torch = gpu_or_skip()
+    _check_sampled(jl, torch, W.QWEN3_8B_128K, n_random=8, disjoint=True)
+
+
+def test_disjoint_rejects_fp32():
+    jl, torch = gpu_or_skip()
+    x = torch.zeros((8, 2, 64), device="cuda")
+    with pytest.raises(jl.JetLongError):
+        jl.prefill(x, x, x, w0=2, w_pretrained=4, rope_base=1e4, disjoint=True)
 
 
 def test_qwen3_4b_varlen():
