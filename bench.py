@@ -16,8 +16,10 @@ Prints ONE JSON line:
             from events the library records right around it, against the
             MI355X dense bf16 MFMA peak; traffic comes from the committed
             counter summary when it was measured on the current kernel source;
-  decode    sustained decode steps (KV bytes 2 L Hkv d 2 per step) and the
-            split-K kernel alone, against the HBM peak;
+  decode    sustained decode steps (KV bytes 2 L Hkv d 2 per step; both
+            kernels of a step, timed over back-to-back steps, since a HIP
+            event pair around one ~100 us kernel adds several us of its own)
+            against the HBM peak;
   disjoint_merge  the same prefill with the far pairs computed directly (a
             window pass on the base grid plus a far-only pass on the remote
             grid, merged with two positive weights): exactly the causal pair
@@ -27,7 +29,10 @@ Prints ONE JSON line:
             and Delta-free decode);
   cpu_baseline  the fp64 oracle on a sample of query rows of the same layer.
 
-    python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--no-cpu-baseline] [--headline-only]
+
+--headline-only skips the disjoint-merge, plain-attention and G-boundary runs, so
+that in a profiler run every dispatch of a kernel has the headline shape.
 """
 
 from __future__ import annotations
@@ -166,6 +171,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=320)
     ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the disjoint-merge, plain-attention and G-boundary runs (profiling runs: every "
+                         "dispatch of a kernel then has the headline shape)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer three times (counter calibration run)")
     args = ap.parse_args()
@@ -255,7 +263,6 @@ def main():
     call_ms = float(np.mean([ev.elapsed_ms(r[0], r[4]) for r in recs]))
     pass2_ms = float(np.mean([ev.elapsed_ms(r[1], r[2]) for r in recs]))
     attn_ms = float(np.mean([ev.elapsed_ms(r[1], r[3]) for r in recs]))
-    split_us = float(np.mean([ev.elapsed_ms(r[5], r[6]) for r in recs])) * 1e3
     dec_in_step_us = float(np.mean([ev.elapsed_ms(r[5], r[7]) for r in recs])) * 1e3
 
     # sustained decode: back-to-back steps over the rotated caches
@@ -268,87 +275,104 @@ def main():
     dec_us = ev.elapsed_ms(e0, e1) * 1e3 / args.decode_steps
     torch.cuda.synchronize()
 
-    # the disjoint merge variant on the same inputs (own output buffers)
-    od_ = torch.empty_like(o)
-    lsed_ = torch.empty_like(lse)
+    def run_extras():
+        """The disjoint-merge variant, plain attention at the same shapes and decode steps on both
+        sides of the G boundaries, on the inputs above."""
+        # the disjoint merge variant on the same inputs (own output buffers)
+        od_ = torch.empty_like(o)
+        lsed_ = torch.empty_like(lse)
 
-    def prefill_disjoint():
-        jl.prefill(q, k, v, w0=cfg.w0, w_pretrained=cfg.w_pretrained, rope_base=cfg.rope_base, out=od_,
-                   lse=lsed_, workspace=ws, disjoint=True)
+        def prefill_disjoint():
+            jl.prefill(q, k, v, w0=cfg.w0, w_pretrained=cfg.w_pretrained, rope_base=cfg.rope_base, out=od_,
+                       lse=lsed_, workspace=ws, disjoint=True)
 
-    prefill_disjoint()
-    torch.cuda.synchronize()
-    drec = [[ev.create() for _ in range(5)] for _ in range(3)]
-    for r in drec:
-        ev.record(r[0], stream)
-        lib.jl_set_profile_events(r[1], r[2], r[3])
         prefill_disjoint()
-        lib.jl_set_profile_events(None, None, None)
-        ev.record(r[4], stream)
-    torch.cuda.synchronize()
-    dj_ms = float(np.mean([ev.elapsed_ms(r[0], r[4]) for r in drec]))
-    dj_far_ms = float(np.mean([ev.elapsed_ms(r[1], r[2]) for r in drec]))
-    Ff = far_flops(L, Hq, d, cfg.w0)
-    dj_do = float((od_.float() - o.float()).abs().max().item())
-    del od_, lsed_
+        torch.cuda.synchronize()
+        drec = [[ev.create() for _ in range(5)] for _ in range(3)]
+        for r in drec:
+            ev.record(r[0], stream)
+            lib.jl_set_profile_events(r[1], r[2], r[3])
+            prefill_disjoint()
+            lib.jl_set_profile_events(None, None, None)
+            ev.record(r[4], stream)
+        torch.cuda.synchronize()
+        dj_ms = float(np.mean([ev.elapsed_ms(r[0], r[4]) for r in drec]))
+        dj_far_ms = float(np.mean([ev.elapsed_ms(r[1], r[2]) for r in drec]))
+        Ff = far_flops(L, Hq, d, cfg.w0)
+        dj_do = float((od_.float() - o.float()).abs().max().item())
+        del od_, lsed_
 
-    # overhead against plain attention at the same shapes: G = 1 (w_pretrained = L) makes every
-    # aliased position the absolute one, so the same library runs plain causal RoPE attention
-    # (prefill: one full-causal pass) and Delta-free decode (every key on the base path)
-    def prefill_plain():
-        jl.prefill(q, k, v, w0=cfg.w0, w_pretrained=L, rope_base=cfg.rope_base, out=o, lse=lse,
-                   workspace=ws)
+        # overhead against plain attention at the same shapes: G = 1 (w_pretrained = L) makes every
+        # aliased position the absolute one, so the same library runs plain causal RoPE attention
+        # (prefill: one full-causal pass) and Delta-free decode (every key on the base path)
+        def prefill_plain():
+            jl.prefill(q, k, v, w0=cfg.w0, w_pretrained=L, rope_base=cfg.rope_base, out=o, lse=lse,
+                       workspace=ws)
 
-    def decode_plain(i):
-        kc, vc = caches[i % n_caches]
-        jl.decode(qd, kc, vc, L, w0=dcfg.w0, w_pretrained=L, rope_base=dcfg.rope_base, out=od, lse=lsed,
-                  workspace=wsd)
+        def decode_plain(i):
+            kc, vc = caches[i % n_caches]
+            jl.decode(qd, kc, vc, L, w0=dcfg.w0, w_pretrained=L, rope_base=dcfg.rope_base, out=od, lse=lsed,
+                      workspace=wsd)
 
-    prefill_plain()
-    torch.cuda.synchronize()
-    pe = [(ev.create(), ev.create()) for _ in range(3)]
-    for a_, b_ in pe:
-        ev.record(a_, stream)
         prefill_plain()
-        ev.record(b_, stream)
-    plain_ms = float(np.mean([ev.elapsed_ms(a_, b_) for a_, b_ in pe]))
-    for i in range(8):
-        decode_plain(i)
-    torch.cuda.synchronize()
-    ev.record(e0, stream)
-    for i in range(args.decode_steps):
-        decode_plain(i)
-    ev.record(e1, stream)
-    dec_plain_us = ev.elapsed_ms(e0, e1) * 1e3 / args.decode_steps
-    torch.cuda.synchronize()
-
-    # decode step time on both sides of the G boundaries (the cache is the same; only L moves)
-    def decode_at(Lx, i):
-        kc, vc = caches[i % n_caches]
-        jl.decode(qd, kc, vc, Lx, w0=dcfg.w0, w_pretrained=dcfg.w_pretrained, rope_base=dcfg.rope_base,
-                  out=od, lse=lsed, workspace=wsd)
-
-    boundary = {}
-    for Lx in (32768, 32769, 65536, 65537):
-        for i in range(4):
-            decode_at(Lx, i)
+        torch.cuda.synchronize()
+        pe = [(ev.create(), ev.create()) for _ in range(3)]
+        for a_, b_ in pe:
+            ev.record(a_, stream)
+            prefill_plain()
+            ev.record(b_, stream)
+        plain_ms = float(np.mean([ev.elapsed_ms(a_, b_) for a_, b_ in pe]))
+        for i in range(8):
+            decode_plain(i)
         torch.cuda.synchronize()
         ev.record(e0, stream)
-        for i in range(100):
-            decode_at(Lx, i)
+        for i in range(args.decode_steps):
+            decode_plain(i)
         ev.record(e1, stream)
-        boundary[str(Lx)] = round(ev.elapsed_ms(e0, e1) * 1e3 / 100, 2)
-    torch.cuda.synchronize()
+        dec_plain_us = ev.elapsed_ms(e0, e1) * 1e3 / args.decode_steps
+        torch.cuda.synchronize()
+
+        # decode step time on both sides of the G boundaries (the cache is the same; only L moves)
+        def decode_at(Lx, i):
+            kc, vc = caches[i % n_caches]
+            jl.decode(qd, kc, vc, Lx, w0=dcfg.w0, w_pretrained=dcfg.w_pretrained, rope_base=dcfg.rope_base,
+                      out=od, lse=lsed, workspace=wsd)
+
+        boundary = {}
+        for Lx in (32768, 32769, 65536, 65537):
+            for i in range(4):
+                decode_at(Lx, i)
+            torch.cuda.synchronize()
+            ev.record(e0, stream)
+            for i in range(100):
+                decode_at(Lx, i)
+            ev.record(e1, stream)
+            boundary[str(Lx)] = round(ev.elapsed_ms(e0, e1) * 1e3 / 100, 2)
+        torch.cuda.synchronize()
+        dj = {"call_ms": round(dj_ms, 3), "tflops_actual": round(Fc / (dj_ms * 1e-3) / 1e12, 2),
+              "frac_actual": round(Fc / (dj_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+              "three_pass_over_disjoint": round(call_ms / dj_ms, 4),
+              "far_pass_ms": round(dj_far_ms, 3),
+              "far_pass_tflops": round(Ff / (dj_far_ms * 1e-3) / 1e12, 2),
+              "far_pass_flops": Ff,
+              "max_abs_diff_vs_three_pass": dj_do}
+        ov = {"prefill_plain_causal_ms": round(plain_ms, 3),
+              "prefill_bifocal_over_plain": round(call_ms / plain_ms, 4),
+              "decode_plain_us_per_step": round(dec_plain_us, 2),
+              "decode_bifocal_over_plain": round(dec_us / dec_plain_us, 4),
+              "decode_us_per_step_across_g_boundaries": boundary}
+        log(f"[bench] plain causal prefill {plain_ms:.2f} ms, Delta-free decode {dec_plain_us:.1f} us; "
+            f"disjoint merge {dj_ms:.2f} ms (far pass {dj_far_ms:.2f} ms)")
+        return dj, ov
+
+    dj_obj, ov_obj = (None, None) if args.headline_only else run_extras()
 
     tflops = F3 / (call_ms * 1e-3) / 1e12
     pass2_tflops = Fc / (pass2_ms * 1e-3) / 1e12
     dec_gbs = kv_bytes / (dec_us * 1e-6) / 1e9
-    split_gbs = kv_bytes / (split_us * 1e-6) / 1e9
     log(f"[bench] prefill call {call_ms:.2f} ms -> {tflops:.1f} TFLOP/s (F_3pass); attention kernels "
         f"{attn_ms:.2f} ms; pass 2 {pass2_ms:.2f} ms -> {pass2_tflops:.1f} TFLOP/s; decode {dec_us:.1f} "
-        f"us/step ({dec_gbs:.0f} GB/s), split-K {split_us:.1f} us ({split_gbs:.0f} GB/s); plain causal "
-        f"prefill {plain_ms:.2f} ms, Delta-free decode {dec_plain_us:.1f} us; disjoint merge {dj_ms:.2f} ms "
-        f"(far pass {dj_far_ms:.2f} ms)")
+        f"us/step ({dec_gbs:.0f} GB/s)")
 
     out = {
         "metric": METRIC,
@@ -379,23 +403,14 @@ def main():
                     "flops_3pass": F3, "flops_causal": Fc},
         "decode": {"us_per_step": round(dec_us, 2), "us_in_step": round(dec_in_step_us, 2),
                    "kv_bytes": kv_bytes, "GB/s": round(dec_gbs, 1),
-                   "roofline": {"bound": "hbm", "achieved": round(split_gbs, 1), "peak": PEAK_HBM_GBS,
-                                "unit": "GB/s", "frac": round(split_gbs / PEAK_HBM_GBS, 4),
+                   "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
                                 "traffic": read_traffic(DECODE_TRAFFIC),
-                                "kernel": "decode_split_kernel", "us_per_launch": round(split_us, 2)},
+                                "kernel": "decode_split_kernel + decode_reduce_kernel (one step, timed "
+                                          "over back-to-back steps)", "us_per_launch": round(dec_us, 2)},
                    "step_frac_hbm": round(dec_gbs / PEAK_HBM_GBS, 4)},
-        "disjoint_merge": {"call_ms": round(dj_ms, 3), "tflops_actual": round(Fc / (dj_ms * 1e-3) / 1e12, 2),
-                           "frac_actual": round(Fc / (dj_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                           "three_pass_over_disjoint": round(call_ms / dj_ms, 4),
-                           "far_pass_ms": round(dj_far_ms, 3),
-                           "far_pass_tflops": round(Ff / (dj_far_ms * 1e-3) / 1e12, 2),
-                           "far_pass_flops": Ff,
-                           "max_abs_diff_vs_three_pass": dj_do},
-        "overhead": {"prefill_plain_causal_ms": round(plain_ms, 3),
-                     "prefill_bifocal_over_plain": round(call_ms / plain_ms, 4),
-                     "decode_plain_us_per_step": round(dec_plain_us, 2),
-                     "decode_bifocal_over_plain": round(dec_us / dec_plain_us, 4),
-                     "decode_us_per_step_across_g_boundaries": boundary},
+        "disjoint_merge": dj_obj,
+        "overhead": ov_obj,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
