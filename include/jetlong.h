@@ -54,7 +54,7 @@ typedef enum {
 
 typedef enum { JL_BF16 = 0, JL_FP32 = 1 } jl_dtype;
 
-/* Largest number of packed sequences one jl_bifocal_prefill call accepts. */
+/* Largest number of sequences one jl_bifocal_prefill or jl_bifocal_decode_batch call accepts. */
 #define JL_MAX_SEQS 64
 
 /*
@@ -142,6 +142,36 @@ int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_cache, i
                       const int32_t* q_to_kv, int32_t head_dim, jl_dtype dtype, int64_t w0,
                       int64_t w_pretrained, double rope_base, float softmax_scale,
                       void* workspace, size_t* workspace_bytes, void* hip_stream);
+
+/*
+ * One generation step for each of num_seqs independent sequences with their
+ * own lengths (ragged), in one call: sequence b is exactly jl_bifocal_decode
+ * with L = lens[b], its own G = jl_group_size(lens[b]) and its own query
+ * (technical summary, Methodology item 2, applied per sequence: every
+ * sequence keeps its base-RoPE cache rows and gets its own correction
+ * rotation; the pages measure one sequence only).
+ *
+ *   q          [num_seqs, num_q_heads, head_dim] bf16; q[b] is rotated by base
+ *              RoPE at position lens[b] - 1
+ *   k_cache, v_cache  [cache_rows, num_kv_heads, head_dim] bf16, read only;
+ *              sequence b's key j (rotated at absolute position j) is row
+ *              row0[b] + j.  Ranges of different sequences may overlap.
+ *   row0, lens host int64[num_seqs]: row0[b] >= 0, 0 <= lens[b] < 2^31,
+ *              row0[b] + lens[b] <= cache_rows (else JL_EINVAL)
+ *   num_seqs   1 .. JL_MAX_SEQS
+ *   o          [num_seqs, num_q_heads, head_dim] bf16 (written)
+ *   lse        [num_seqs, num_q_heads] fp32, or NULL
+ *   Sequences with lens[b] == 0 are skipped: their o rows and lse entries
+ *   are not written.  Workspace: two-call protocol as in jl_bifocal_decode;
+ *   its size depends on lens.  The other arguments and errors are those of
+ *   jl_bifocal_decode.
+ */
+int jl_bifocal_decode_batch(const void* q, const void* k_cache, const void* v_cache, int64_t cache_rows,
+                            const int64_t* row0, const int64_t* lens, int32_t num_seqs, void* o,
+                            float* lse, int32_t num_q_heads, int32_t num_kv_heads,
+                            const int32_t* q_to_kv, int32_t head_dim, jl_dtype dtype, int64_t w0,
+                            int64_t w_pretrained, double rope_base, float softmax_scale,
+                            void* workspace, size_t* workspace_bytes, void* hip_stream);
 
 /*
  * Base RoPE of n consecutive rows: y[r][h][:] = R(pos0 + r) x[r][h][:],

@@ -18,6 +18,7 @@ import os
 from typing import Optional, Sequence
 
 __all__ = ["group_size", "prefill", "prefill_workspace_bytes", "decode", "decode_workspace_bytes",
+           "decode_batch", "decode_batch_workspace_bytes", "rope_rows",
            "lib", "JetLongError", "LIB_PATH", "BF16", "FP32"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjetlong.so")
@@ -62,6 +63,13 @@ def lib() -> ctypes.CDLL:
             c.c_void_p, c.c_void_p, c.c_void_p, c.c_int64, c.c_void_p, c.c_void_p,
             c.c_int32, c.c_int32, c.POINTER(c.c_int32), c.c_int32, c.c_int, c.c_int64, c.c_int64,
             c.c_double, c.c_float, c.c_void_p, c.POINTER(c.c_size_t), c.c_void_p]
+        L.jl_bifocal_decode_batch.restype = c.c_int
+        L.jl_bifocal_decode_batch.argtypes = [
+            c.c_void_p, c.c_void_p, c.c_void_p, c.c_int64,                    # q k_cache v_cache cache_rows
+            c.POINTER(c.c_int64), c.POINTER(c.c_int64), c.c_int32,            # row0 lens num_seqs
+            c.c_void_p, c.c_void_p, c.c_int32, c.c_int32, c.POINTER(c.c_int32),  # o lse Hq Hkv q_to_kv
+            c.c_int32, c.c_int, c.c_int64, c.c_int64, c.c_double, c.c_float,  # d dtype w0 wpt base scale
+            c.c_void_p, c.POINTER(c.c_size_t), c.c_void_p]                    # ws ws_bytes stream
         L.jl_rope_rows.restype = c.c_int
         L.jl_rope_rows.argtypes = [c.c_void_p, c.c_void_p, c.c_int64, c.c_int32, c.c_int32, c.c_int,
                                    c.c_int64, c.c_double, c.c_void_p]
@@ -215,6 +223,65 @@ def decode(q, k_cache, v_cache, L: int, *, w0: int, w_pretrained: int, rope_base
                                    int(w0), int(w_pretrained), float(rope_base),
                                    0.0 if scale is None else float(scale), _ptr(workspace),
                                    ctypes.byref(n), _stream(q.device)))
+    return o, (lse if return_lse else None)
+
+
+def _packed_rows(lens):
+    r, acc = [], 0
+    for n in lens:
+        r.append(acc)
+        acc += int(n)
+    return r
+
+
+def decode_batch_workspace_bytes(lens, num_q_heads: int, num_kv_heads: int, head_dim: int = 128, row0=None,
+                                 q_to_kv=None, cache_rows: Optional[int] = None) -> int:
+    lens = [int(n) for n in lens]
+    row0 = _packed_rows(lens) if row0 is None else [int(r) for r in row0]
+    rows = max([r + n for r, n in zip(row0, lens)] + [0]) if cache_rows is None else int(cache_rows)
+    n = ctypes.c_size_t(0)
+    _check(lib().jl_bifocal_decode_batch(None, None, None, rows, _i64_array(row0), _i64_array(lens), len(lens),
+                                         None, None, num_q_heads, num_kv_heads, _i32_array(q_to_kv), head_dim,
+                                         BF16, 0, 1, 10000.0, 0.0, None, ctypes.byref(n), None))
+    return int(n.value)
+
+
+def decode_batch(q, k_cache, v_cache, lens, *, w0: int, w_pretrained: int, rope_base: float, row0=None,
+                 scale: Optional[float] = None, q_to_kv=None, out=None, lse=None, return_lse=True,
+                 workspace=None):
+    """One generation step for each of B ragged sequences.  q [B, Hq, d] bf16
+    (q[b] base-rotated at lens[b] - 1); caches [R, Hkv, d] bf16 holding
+    base-rotated keys, sequence b's keys at rows row0[b] .. row0[b] + lens[b] - 1
+    (default: packed one after the other).  Returns (o [B, Hq, d], lse [B, Hq]
+    or None); sequences with lens[b] == 0 leave their rows of o and lse
+    unwritten."""
+    import torch
+    B, Hq, d = q.shape
+    lens = [int(n) for n in lens]
+    if len(lens) != B:
+        raise ValueError("one length per query row")
+    row0 = _packed_rows(lens) if row0 is None else [int(r) for r in row0]
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()) or k_cache.shape != v_cache.shape:
+        raise ValueError("caches must be contiguous and of one shape")
+    R, Hkv = k_cache.shape[0], k_cache.shape[1]
+    q = q.contiguous()
+    o = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    kvmap = _i32_array(q_to_kv)
+    r0, ln = _i64_array(row0), _i64_array(lens)
+    dt = _dtype_code(q)
+    n = ctypes.c_size_t(0)
+    _check(lib().jl_bifocal_decode_batch(None, None, None, R, r0, ln, B, None, None, Hq, Hkv, kvmap, d, dt,
+                                         int(w0), int(w_pretrained), float(rope_base), 0.0, None,
+                                         ctypes.byref(n), None))
+    if workspace is None or workspace.numel() < n.value:
+        workspace = torch.empty(max(int(n.value), 16), dtype=torch.uint8, device=q.device)
+    n = ctypes.c_size_t(workspace.numel())
+    _check(lib().jl_bifocal_decode_batch(_ptr(q), _ptr(k_cache), _ptr(v_cache), R, r0, ln, B, _ptr(o),
+                                         _ptr(lse) if return_lse else None, Hq, Hkv, kvmap, d, dt, int(w0),
+                                         int(w_pretrained), float(rope_base), 0.0 if scale is None else float(scale),
+                                         _ptr(workspace), ctypes.byref(n), _stream(q.device)))
     return o, (lse if return_lse else None)
 
 

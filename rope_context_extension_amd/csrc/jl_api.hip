@@ -240,13 +240,27 @@ JL_EXPORT int jl_bifocal_prefill_disjoint(const void* q, const void* k, const vo
                       hip_stream, true);
 }
 
-JL_EXPORT int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_cache, int64_t L,
-                                void* o, float* lse, int32_t num_q_heads, int32_t num_kv_heads,
-                                const int32_t* q_to_kv, int32_t head_dim, jl_dtype dtype, int64_t w0,
-                                int64_t w_pretrained, double rope_base, float softmax_scale,
-                                void* workspace, size_t* workspace_bytes, void* hip_stream) {
+// One or more sequences: lens[b] keys at cache rows row0[b] .. row0[b] + lens[b] - 1.
+// cache_rows < 0: the caller gave no cache size (single-sequence call).
+static int decode_impl(const void* q, const void* k_cache, const void* v_cache, int64_t cache_rows,
+                       const int64_t* row0, const int64_t* lens, int32_t num_seqs, void* o, float* lse,
+                       int32_t num_q_heads, int32_t num_kv_heads, const int32_t* q_to_kv, int32_t head_dim,
+                       jl_dtype dtype, int64_t w0, int64_t w_pretrained, double rope_base, float softmax_scale,
+                       void* workspace, size_t* workspace_bytes, void* hip_stream) {
   if (workspace_bytes == nullptr) return fail(JL_EINVAL, "workspace_bytes is NULL");
-  if (L < 0) return fail(JL_EINVAL, "L < 0");
+  if (num_seqs < 1) return fail(JL_EINVAL, "num_seqs must be >= 1");
+  if (num_seqs > JL_MAX_SEQS) return fail(JL_EUNSUPPORTED, "num_seqs > %d", JL_MAX_SEQS);
+  if (lens == nullptr || row0 == nullptr) return fail(JL_EINVAL, "lens and row0 must be host arrays");
+  int64_t total = 0;
+  for (int b = 0; b < num_seqs; ++b) {
+    if (lens[b] < 0) return fail(JL_EINVAL, "L < 0 (sequence %d)", b);
+    if (lens[b] > (int64_t)INT32_MAX) return fail(JL_EUNSUPPORTED, "L >= 2^31 (sequence %d)", b);
+    if (row0[b] < 0) return fail(JL_EINVAL, "row0 < 0 (sequence %d)", b);
+    if (cache_rows >= 0 && row0[b] + lens[b] > cache_rows)
+      return fail(JL_EINVAL, "sequence %d: rows %lld + %lld exceed the cache's %lld rows", b, (long long)row0[b],
+                  (long long)lens[b], (long long)cache_rows);
+    total += lens[b];
+  }
   if (dtype != JL_BF16 && dtype != JL_FP32) return fail(JL_EINVAL, "unknown dtype %d", (int)dtype);
   int rc = check_common(w0, w_pretrained, rope_base);
   if (rc) return rc;
@@ -266,14 +280,16 @@ JL_EXPORT int jl_bifocal_decode(const void* q, const void* k_cache, const void* 
     for (int g = 0; g < num_kv_heads; ++g)
       if (cnt[g] != NG) return fail(JL_EUNSUPPORTED, "decode needs the same number of q heads per kv head");
   }
-  if (L > (int64_t)INT32_MAX) return fail(JL_EUNSUPPORTED, "L >= 2^31");
-  const size_t need = L == 0 ? 0 : jl_decode_workspace_bytes(L, num_q_heads, head_dim);
+  if (total > (int64_t)INT32_MAX * 16) return fail(JL_EUNSUPPORTED, "too many keys in one call");
+  JlDecSeqs ds;
+  jl_decode_plan(lens, row0, num_seqs, w0, w_pretrained, &ds);
+  const size_t need = total == 0 ? 0 : jl_decode_workspace_bytes(ds, num_q_heads);
   if (workspace == nullptr) {
     *workspace_bytes = need;
     return JL_OK;
   }
   if (*workspace_bytes < need) return fail(JL_ENOSPC, "workspace has %zu bytes, %zu needed", *workspace_bytes, need);
-  if (L == 0) return JL_OK;
+  if (total == 0) return JL_OK;
   if (!q || !k_cache || !v_cache || !o) return fail(JL_EINVAL, "q, caches and o must be device pointers");
   if (((uintptr_t)workspace & 15) || (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15))
     return fail(JL_EINVAL, "q, caches and workspace must be 16-byte aligned");
@@ -281,13 +297,34 @@ JL_EXPORT int jl_bifocal_decode(const void* q, const void* k_cache, const void* 
   JlFreqs fr;
   build_freqs(&fr, head_dim, rope_base);
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
-  const int32_t G = (int32_t)jl_group_size_i64(L, w_pretrained);
   if (g_ev_before) (void)hipEventRecord(g_ev_before, (hipStream_t)hip_stream);
-  hipError_t e = jl_launch_decode_bf16(q, k_cache, v_cache, L, o, lse, num_q_heads, num_kv_heads, hm, w0,
-                                       G, scale, fr, workspace, (hipStream_t)hip_stream);
+  hipError_t e = jl_launch_decode_bf16(q, k_cache, v_cache, ds, o, lse, num_q_heads, num_kv_heads, hm, scale, fr,
+                                       workspace, (hipStream_t)hip_stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (g_ev_after) (void)hipEventRecord(g_ev_after, (hipStream_t)hip_stream);
   return JL_OK;
+}
+
+JL_EXPORT int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_cache, int64_t L,
+                                void* o, float* lse, int32_t num_q_heads, int32_t num_kv_heads,
+                                const int32_t* q_to_kv, int32_t head_dim, jl_dtype dtype, int64_t w0,
+                                int64_t w_pretrained, double rope_base, float softmax_scale,
+                                void* workspace, size_t* workspace_bytes, void* hip_stream) {
+  const int64_t row0 = 0;
+  return decode_impl(q, k_cache, v_cache, -1, &row0, &L, 1, o, lse, num_q_heads, num_kv_heads, q_to_kv, head_dim,
+                     dtype, w0, w_pretrained, rope_base, softmax_scale, workspace, workspace_bytes, hip_stream);
+}
+
+JL_EXPORT int jl_bifocal_decode_batch(const void* q, const void* k_cache, const void* v_cache, int64_t cache_rows,
+                                      const int64_t* row0, const int64_t* lens, int32_t num_seqs, void* o,
+                                      float* lse, int32_t num_q_heads, int32_t num_kv_heads,
+                                      const int32_t* q_to_kv, int32_t head_dim, jl_dtype dtype, int64_t w0,
+                                      int64_t w_pretrained, double rope_base, float softmax_scale,
+                                      void* workspace, size_t* workspace_bytes, void* hip_stream) {
+  if (cache_rows < 0) return fail(JL_EINVAL, "cache_rows < 0");
+  return decode_impl(q, k_cache, v_cache, cache_rows, row0, lens, num_seqs, o, lse, num_q_heads, num_kv_heads,
+                     q_to_kv, head_dim, dtype, w0, w_pretrained, rope_base, softmax_scale, workspace,
+                     workspace_bytes, hip_stream);
 }
 
 JL_EXPORT int jl_rope_rows(const void* x, void* y, int64_t n_rows, int32_t num_heads, int32_t head_dim,

@@ -1,4 +1,5 @@
-// jl_decode.hip - single-batch bifocal decode against a base-RoPE KV cache.
+// jl_decode.hip - bifocal decode against a base-RoPE KV cache, one query
+// token for each of one or more sequences.
 //
 // The cache holds keys rotated at their absolute positions and is never
 // written.  For a key at distance >= w0 from the query, the correction
@@ -9,9 +10,11 @@
 // gives the vector rotated at the aliased position).  G is recomputed from L
 // at every step, so crossing a G boundary needs no cache work.
 //
-// Split-K: workgroup w covers keys [w C, (w+1) C) for every head and writes
-// unnormalised partial statistics (max, sum, accumulator) per head; a second
-// kernel merges them through their LogSumExp values.
+// Split-K: workgroup w covers keys [w C, (w+1) C) of its sequence for every
+// head and writes unnormalised partial statistics (max, sum, accumulator) per
+// head; a second kernel merges each sequence's partials through their
+// LogSumExp values.  Sequences are independent: each has its own length, G,
+// cache rows and query, and its own range of workgroups.
 //
 // A workgroup has one wave per kv head (8 waves) and walks its keys in
 // 64-key sub-chunks:
@@ -38,8 +41,8 @@
 // of the scores, V per 32-key half of PV), so every wave keeps about a
 // sub-chunk of loads in flight while it computes, issued a few at a time.
 // The angle table has three buffers, filled two sub-chunks ahead; the waves
-// synchronise only through a workgroup counter of finished sub-chunks, so a
-// wave may run up to a sub-chunk ahead of the slowest one.
+// synchronise only through per-wave counts of finished sub-chunks in LDS,
+// so a wave may run up to a sub-chunk ahead of the slowest one.
 #include "jl_internal.h"
 
 namespace {
@@ -150,14 +153,19 @@ __device__ inline f32x4 remote_block(const u32x4 (&kw)[4], const uint2* trow, co
   return sr;
 }
 
-// Waits until the workgroup counter reaches `target`.  Every wave adds one
-// per sub-chunk whatever it computes, so the count always arrives; the bound
-// only keeps a broken invariant from hanging the device (the caller then
-// poisons its results).
-__device__ inline bool wait_count(const int* counter, int target) {
+// Waits until every wave of the workgroup has finished `target` sub-chunks
+// (done[w] counts wave w's; lane w < NWAVES polls entry w).  A per-wave
+// count, not one shared total: a total can reach NWAVES * k while fast waves
+// are several sub-chunks ahead and slow ones have not finished sub-chunk
+// k - 1.  Every wave counts every sub-chunk whatever it computes, so the
+// counts always arrive; the bound only keeps a broken invariant from hanging
+// the device (the caller then poisons its results).
+__device__ inline bool wait_all(const int* done, int target) {
+  const int l = lane_now();
   for (int it = 0; it < (1 << 22); ++it) {
-    const int v = __hip_atomic_load(counter, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    if (__builtin_amdgcn_readfirstlane(v) >= target) return true;
+    const int v = l < NWAVES ? __hip_atomic_load(&done[l], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)
+                             : target;
+    if (__all(v >= target)) return true;
     __builtin_amdgcn_s_sleep(1);
   }
   return false;
@@ -184,14 +192,14 @@ __device__ inline void fill_trig(uint2 (*tb)[TPITCH], float4* chain, float4 st, 
   chain[tid] = make_float4(c, s, __int_as_float(rem), 0.f);
 }
 
-// Partial records, laid out for the merge:
+// Partial records, laid out for the merge (nwg: workgroups of the call):
 //   part_ml [Hq][nwg][2]    (max in log2 units, sum)
 //   part_o  [Hq][nwg][128]  unnormalised accumulator
 template <int NG>
 __global__ void __launch_bounds__(NT) decode_split_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kc, const __bf16* __restrict__ vc,
-    float* __restrict__ part_ml, float* __restrict__ part_o, int L, int Hq, int Hkv, JlHeadMap hm,
-    int w0, int G, int nsub, int nwg, float scale_log2, JlFreqs fr) {
+    float* __restrict__ part_ml, float* __restrict__ part_o, int Hq, int Hkv, JlHeadMap hm,
+    JlDecSeqs ds, float scale_log2, JlFreqs fr) {
   // Row pitches carry 16 bytes of padding: the 16 lanes of an LDS read pass
   // fetch the same columns of different rows, which then fall on distinct
   // banks.
@@ -208,12 +216,19 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
   // in order, and waiting on anything else would wait on the prefetches too.
   __shared__ float4 steps[64];
   __shared__ float4 chain[NT];
-  __shared__ int tables_done;            // angle-table fills finished, one per wave and sub-chunk
+  __shared__ int done[NWAVES];           // sub-chunks finished (angle-table fills included) per wave
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // the workgroup's sequence (uniform)
+  int b = 0;
+  while (b + 1 < ds.nseq && (int)blockIdx.x >= ds.wg_begin[b + 1]) ++b;
+  const int L = ds.L[b], G = ds.G[b], w0 = ds.w0[b], nsub = ds.nsub;
+  const int nwg = ds.wg_begin[ds.nseq];
+  q += (int64_t)b * Hq * D;
+  const int64_t row0 = ds.row0[b];
   const int i = L - 1;
-  const int c_begin = blockIdx.x * nsub * SUB;
+  const int c_begin = ((int)blockIdx.x - ds.wg_begin[b]) * nsub * SUB;
   const int nsc = min(nsub, (L - c_begin + SUB - 1) / SUB);     // sub-chunks holding keys: >= 1
 
   if (tid < Hq) {
@@ -237,9 +252,9 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
   const int row_bytes = Hkv * D * 2;
   const int nrows = min(L - c_begin, nsub * SUB);
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const char*)kc + (int64_t)c_begin * row_bytes), 0, nrows * row_bytes, BUF_RSRC_WORD3);
+      (void*)((const char*)kc + (row0 + c_begin) * row_bytes), 0, nrows * row_bytes, BUF_RSRC_WORD3);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const char*)vc + (int64_t)c_begin * row_bytes), 0, nrows * row_bytes, BUF_RSRC_WORD3);
+      (void*)((const char*)vc + (row0 + c_begin) * row_bytes), 0, nrows * row_bytes, BUF_RSRC_WORD3);
   const int koff = kl * row_bytes + 256 * kvh + 32 * gq;       // key kl, channels 16 gq ..
   const int voff = 8 * gq * row_bytes + 256 * kvh + 16 * kl;   // key 8 gq, channels 8 kl ..
   KTile kt;
@@ -252,13 +267,15 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
   }
   __syncthreads();
   {
-    // the query in both variants, scaled by scale * log2 e: as given (base)
-    // and rotated by Delta_q
+    // the query in both variants: as given (base; bf16 input, so the base
+    // scores carry no rounding of q at all) and rotated by Delta_q.  The
+    // softmax scale is applied to the fp32 scores (folded into the exp2
+    // argument), not to the bf16 query.
     const int dq = jl_remote_pos(i, G) - i;
     for (int e = tid; e < Hq * 64; e += NT) {
       const int slot = e >> 6, m = e & 63;
       const __bf16* qr = q + heads[slot] * D;
-      const float x1 = (float)qr[m] * scale_log2, x2 = (float)qr[m + 64] * scale_log2;
+      const float x1 = (float)qr[m], x2 = (float)qr[m + 64];
       float c, s;
       jl_rope_sincos(dq, fr.turn_frac[m], &s, &c);
       qlds[0][slot * QPITCH + m] = (__bf16)x1;
@@ -297,22 +314,21 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   float run_m = -INFINITY, run_l = 0.f;              // column kl (lanes kl + 16 gq)
-  if (tid == 0) tables_done = 0;
+  if (tid < NWAVES) done[tid] = 0;
   __syncthreads();
   bool in_time = true;
 
   for (int sc = 0; sc < nsc; ++sc) {
     const int c0 = c_begin + sc * SUB;
-    // sub-chunk sc's table was filled two sub-chunks ago (or before the
-    // loop): every wave has counted that
-    if (sc >= 2) in_time &= wait_count(&tables_done, NWAVES * (sc - 1));
+    // sub-chunk sc's table was filled in sub-chunk sc - 2 (or before the
+    // loop): every wave has finished that
+    if (sc >= 2) in_time &= wait_all(done, sc - 1);
     const uint2 (*tb)[TPITCH] = trig[sc % NTRIG];
     float alpha = 1.f;
     if (active) {
 
     // ---------------- scores: 4 blocks of 16 keys ----------------
-    // lane holds S^T[key blk*16 + 4 gq + e][column kl], in log2 units (the
-    // query carries scale * log2 e)
+    // lane holds S^T[key blk*16 + 4 gq + e][column kl] = q.k, unscaled
     f32x4 sco[4];
     {
 #pragma unroll
@@ -348,7 +364,8 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
       for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sco[blk][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(run_m, mx);            // finite: every sub-chunk has a valid key
+    // scores are raw q.k: the stabiliser is in log2 units (scale * log2 e folded in)
+    const float mn = fmaxf(run_m, mx * scale_log2);   // finite: every sub-chunk has a valid key
     alpha = __builtin_amdgcn_exp2f(run_m - mn);
     float sum = 0.f;
 #pragma unroll
@@ -356,7 +373,7 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
       float pr[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pr[e] = __builtin_amdgcn_exp2f(sco[blk][e] - mn);
+        pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sco[blk][e], scale_log2, -mn));
         sum += pr[e];
       }
       if (kl < NG)
@@ -401,15 +418,15 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
     }   // active
 
     // sub-chunk sc + 2's table goes to the buffer of sub-chunk sc - 1, whose
-    // readers are done once every wave has counted sub-chunk sc - 1
+    // readers are done once every wave has finished sub-chunk sc - 1
     if (sc + 2 < nsc && (i - (c0 + 2 * SUB)) >= w0) {
-      if (sc >= 1) in_time &= wait_count(&tables_done, NWAVES * sc);
+      if (sc >= 1) in_time &= wait_all(done, sc);
       fill_trig(trig[(sc + 2) % NTRIG], chain, steps[tm], tid, tm, tk, thr, dlo_g);
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);              // lgkmcnt(0): table rows written
-    if (lane == 0) __hip_atomic_fetch_add(&tables_done, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (lane == 0) __hip_atomic_store(&done[wave], sc + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
-  if (!in_time) run_l = NAN;                   // a count that never came: fail loudly
+  if (!in_time) run_l = NAN;                   // a count that never arrived: fail loudly
   // ---------------- partial records ----------------
   if (!active || kl >= NG) return;
   // output row 4 gq + e of MFMA c is channel 8 (4 gq + e) + c
@@ -433,18 +450,22 @@ constexpr int RED_GROUPS = 64;
 constexpr int RED_DEPTH = 8;
 
 __global__ void __launch_bounds__(256) decode_reduce_kernel(const float* __restrict__ part_ml,
-                                                            const float* __restrict__ part_o, int nwg,
+                                                            const float* __restrict__ part_o, JlDecSeqs ds,
                                                             int Hq, int NG, JlHeadMap hm,
                                                             __bf16* __restrict__ o,
                                                             float* __restrict__ lse) {
   __shared__ float red_m[RED_GROUPS];
   __shared__ float red_l[4];
   __shared__ float4 red_a[4][4];
-  const int slot = blockIdx.x, part = blockIdx.y, tid = threadIdx.x;
+  const int slot = blockIdx.x, part = blockIdx.y, sq = blockIdx.z, tid = threadIdx.x;
+  const int w_first = ds.wg_begin[sq];
+  const int nwg = ds.wg_begin[sq + 1] - w_first;     // this sequence's partials
+  if (nwg == 0) return;                               // L = 0: nothing to write
+  const int stride = ds.wg_begin[ds.nseq];
   const int lane = tid & 63, wave = tid >> 6;
   const int c4 = tid & 3, grp = tid >> 2;
-  const float2* ml = (const float2*)part_ml + (int64_t)slot * nwg;
-  const float* po = part_o + (int64_t)slot * nwg * D + part * 16 + c4 * 4;
+  const float2* ml = (const float2*)part_ml + (int64_t)slot * stride + w_first;
+  const float* po = part_o + ((int64_t)slot * stride + w_first) * D + part * 16 + c4 * 4;
   float m = -INFINITY, l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int wb = grp; wb < nwg; wb += RED_GROUPS * RED_DEPTH) {
@@ -505,50 +526,78 @@ __global__ void __launch_bounds__(256) decode_reduce_kernel(const float* __restr
         if (cnt == n) head = h;
         ++cnt;
       }
-    o[head * D + part * 16 + tid] = (__bf16)(A / Lt);
-    if (lse != nullptr && part == 0 && tid == 0) lse[head] = (M + __log2f(Lt)) * LN2;
+    o[((int64_t)sq * Hq + head) * D + part * 16 + tid] = (__bf16)(A / Lt);
+    if (lse != nullptr && part == 0 && tid == 0) lse[(int64_t)sq * Hq + head] = (M + __log2f(Lt)) * LN2;
   }
 }
 
 }  // namespace
 
-static int decode_nsub(int64_t L) {
-  // about one workgroup per compute unit at long L, at least one 64-key
-  // sub-chunk each
-  int64_t n = L / (SUB * 256);
-  if (n < 1) n = 1;
-  if (n > 32) n = 32;
-  return (int)n;
+// Compute units of an MI355X; one split workgroup fits per compute unit (its
+// LDS use is above half of the 160 KB).
+constexpr int64_t DEC_CUS = 256;
+constexpr int64_t DEC_MAX_NSUB = 1024;   // 65536 keys per workgroup: byte offsets stay in 32 bits
+
+static int64_t decode_wgs(const int64_t* lens, int nseq, int64_t nsub) {
+  int64_t w = 0;
+  for (int b = 0; b < nseq; ++b) w += (lens[b] + nsub * SUB - 1) / (nsub * SUB);
+  return w;
 }
 
-static int64_t decode_nwg(int64_t L) {
-  const int nsub = decode_nsub(L);
-  return (L + (int64_t)nsub * SUB - 1) / ((int64_t)nsub * SUB);
+// The smallest sub-chunk count per workgroup whose workgroups all fit one
+// round on the compute units: a second, partly filled round would cost a
+// whole workgroup's time for a few keys.
+static int decode_nsub(const int64_t* lens, int nseq) {
+  if (decode_wgs(lens, nseq, DEC_MAX_NSUB) > DEC_CUS) return (int)DEC_MAX_NSUB;
+  int64_t lo = 1, hi = DEC_MAX_NSUB;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) / 2;
+    if (decode_wgs(lens, nseq, mid) <= DEC_CUS) hi = mid;
+    else lo = mid + 1;
+  }
+  return (int)lo;
 }
 
-size_t jl_decode_workspace_bytes(int64_t L, int32_t Hq, int32_t d) {
-  (void)d;
-  const int64_t nwg = decode_nwg(L);
-  return (size_t)(nwg * Hq * (2 + D) * sizeof(float));
+void jl_decode_plan(const int64_t* lens, const int64_t* row0, int32_t nseq, int64_t w0, int64_t w_pretrained,
+                    JlDecSeqs* ds) {
+  ds->nseq = nseq;
+  ds->nsub = decode_nsub(lens, nseq);
+  const int64_t chunk = (int64_t)ds->nsub * SUB;
+  int wg = 0;
+  for (int b = 0; b < JL_MAX_SEQS; ++b) {
+    const bool real = b < nseq;
+    const int64_t L = real ? lens[b] : 0;
+    const int32_t G = (int32_t)jl_group_size_i64(L, w_pretrained);
+    ds->wg_begin[b] = wg;
+    ds->L[b] = (int32_t)L;
+    ds->G[b] = G;
+    // With G = 1 the aliased positions are the absolute ones (Delta = 0):
+    // every key takes the base path, and the angle table is never built.
+    ds->w0[b] = (w0 > L || G == 1) ? (int32_t)L : (int32_t)w0;
+    ds->row0[b] = real ? row0[b] : 0;
+    wg += (int)((L + chunk - 1) / chunk);
+  }
+  ds->wg_begin[JL_MAX_SEQS] = wg;
+  for (int b = nseq; b <= JL_MAX_SEQS; ++b) ds->wg_begin[b] = wg;
 }
 
-hipError_t jl_launch_decode_bf16(const void* q, const void* k_cache, const void* v_cache, int64_t L,
-                                 void* o, float* lse, int32_t Hq, int32_t Hkv,
-                                 const JlHeadMap& hm, int64_t w0, int32_t G, float scale,
+size_t jl_decode_workspace_bytes(const JlDecSeqs& ds, int32_t Hq) {
+  return (size_t)ds.wg_begin[ds.nseq] * Hq * (2 + D) * sizeof(float);
+}
+
+hipError_t jl_launch_decode_bf16(const void* q, const void* k_cache, const void* v_cache, const JlDecSeqs& ds,
+                                 void* o, float* lse, int32_t Hq, int32_t Hkv, const JlHeadMap& hm, float scale,
                                  const JlFreqs& fr, void* workspace, hipStream_t st) {
-  const int nsub = decode_nsub(L);
-  const int nwg = (int)decode_nwg(L);
+  const int nwg = ds.wg_begin[ds.nseq];
+  if (nwg == 0) return hipSuccess;
   const int NG = Hq / Hkv;
-  // With G = 1 the aliased positions are the absolute ones (Delta = 0): every
-  // key takes the base path, and the angle table is never built.
-  const int w0c = (w0 > L || G == 1) ? (int)L : (int)w0;
   float* part_ml = (float*)workspace;
   float* part_o = part_ml + (int64_t)nwg * Hq * 2;
   const float sl2 = scale * LOG2E;
 #define JL_DEC(NGV)                                                                          \
   decode_split_kernel<NGV><<<nwg, NT, 0, st>>>((const __bf16*)q, (const __bf16*)k_cache,   \
                                                (const __bf16*)v_cache, part_ml, part_o,     \
-                                               (int)L, Hq, Hkv, hm, w0c, G, nsub, nwg, sl2, fr)
+                                               Hq, Hkv, hm, ds, sl2, fr)
   switch (NG) {
     case 1: JL_DEC(1); break;
     case 2: JL_DEC(2); break;
@@ -560,6 +609,6 @@ hipError_t jl_launch_decode_bf16(const void* q, const void* k_cache, const void*
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (hipEvent_t mid = jl_profile_mid_event()) (void)hipEventRecord(mid, st);
-  decode_reduce_kernel<<<dim3(Hq, 8), 256, 0, st>>>(part_ml, part_o, nwg, Hq, NG, hm, (__bf16*)o, lse);
+  decode_reduce_kernel<<<dim3(Hq, 8, ds.nseq), 256, 0, st>>>(part_ml, part_o, ds, Hq, NG, hm, (__bf16*)o, lse);
   return hipGetLastError();
 }

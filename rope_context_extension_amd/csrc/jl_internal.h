@@ -100,12 +100,26 @@ hipError_t jl_launch_prefill_bf16(const JlPrefillWs& ws, void* o, float* lse, in
                                   int32_t Hq, int32_t Hkv, const JlHeadMap& hm, const JlSeqs& seqs,
                                   int64_t w0, float scale, int32_t max_len, bool disjoint, hipStream_t st);
 
-// decode
-size_t jl_decode_workspace_bytes(int64_t L, int32_t Hq, int32_t d);
-hipError_t jl_launch_decode_bf16(const void* q, const void* k_cache, const void* v_cache, int64_t L,
-                                 void* o, float* lse, int32_t Hq, int32_t Hkv,
-                                 const JlHeadMap& hm, int64_t w0, int32_t G, float scale,
-                                 const JlFreqs& fr, void* workspace, hipStream_t st);
+// decode: the sequences of one call, each with its own length, group size
+// and cache rows; workgroup w serves sequence b for wg_begin[b] <= w <
+// wg_begin[b + 1], keys [(w - wg_begin[b]) nsub 64, + nsub 64) of it
+struct JlDecSeqs {
+  int32_t nseq;
+  int32_t nsub;                        // 64-key sub-chunks per workgroup (one value per call)
+  int32_t wg_begin[JL_MAX_SEQS + 1];   // prefix sums of the workgroups per sequence
+  int32_t L[JL_MAX_SEQS];              // cached keys, the query at L - 1
+  int32_t G[JL_MAX_SEQS];
+  int32_t w0[JL_MAX_SEQS];             // window, L when every key is base (w0 >= L or G = 1)
+  int64_t row0[JL_MAX_SEQS];           // first cache row of the sequence
+};
+// plan of a call (host): nsub from the total key count, workgroups per sequence
+void jl_decode_plan(const int64_t* lens, const int64_t* row0, int32_t nseq, int64_t w0,
+                    int64_t w_pretrained, JlDecSeqs* ds);
+size_t jl_decode_workspace_bytes(const JlDecSeqs& ds, int32_t Hq);
+hipError_t jl_launch_decode_bf16(const void* q, const void* k_cache, const void* v_cache,
+                                 const JlDecSeqs& ds, void* o, float* lse, int32_t Hq, int32_t Hkv,
+                                 const JlHeadMap& hm, float scale, const JlFreqs& fr, void* workspace,
+                                 hipStream_t st);
 
 // instrumentation: event to record after the dominant kernel, or nullptr
 hipEvent_t jl_profile_mid_event();

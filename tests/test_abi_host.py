@@ -147,6 +147,56 @@ def test_decode_workspace_too_small_is_enospc():
     assert rc == JL_ENOSPC
 
 
+def _decb(lens, row0=None, rows=None, **kw):
+    a = dict(Hq=32, Hkv=8, kvmap=None, d=128, dt=jl.BF16, w0=16, wpt=64, base=1e6, ws=None, nbytes=0)
+    a.update(kw)
+    if row0 is None:
+        row0 = [sum(lens[:b]) for b in range(len(lens))]
+    if rows is None:
+        rows = max([r + n for r, n in zip(row0, lens)] + [0])
+    n = ctypes.c_size_t(a["nbytes"])
+    arr = lambda v: (ctypes.c_int64 * max(1, len(v)))(*v)
+    rc = L.jl_bifocal_decode_batch(None, None, None, rows, arr(row0), arr(lens), len(lens), None, None, a["Hq"],
+                                   a["Hkv"], a["kvmap"], a["d"], a["dt"], a["w0"], a["wpt"], a["base"], 0.0,
+                                   a["ws"], ctypes.byref(n), None)
+    return rc, n.value
+
+
+def test_decode_batch_size_query():
+    # one sequence: the same workspace as the single-sequence call
+    assert _decb([1000]) == _dec(L=1000)
+    assert _decb([131072]) == _dec(L=131072)
+    rc, n = _decb([5000, 0, 70000, 1])
+    assert rc == JL_OK and n > 0
+    assert _decb([0, 0]) == (JL_OK, 0)
+
+
+@pytest.mark.parametrize("args,kw,code", [
+    (([5, -1],), {}, JL_EINVAL),                         # negative length
+    (([5, 2**31],), {}, JL_EUNSUPPORTED),
+    (([5, 6], [0, -2]), {}, JL_EINVAL),                  # negative row0
+    (([5, 6], [0, 5], 10), {}, JL_EINVAL),               # 5 + 6 rows past a cache of 10
+    (([],), {}, JL_EINVAL),                              # no sequences
+    (([1] * 65,), {}, JL_EUNSUPPORTED),                  # more than JL_MAX_SEQS
+    (([5],), dict(dt=jl.FP32), JL_EUNSUPPORTED),
+    (([5],), dict(Hq=12, Hkv=4), JL_EUNSUPPORTED),
+    (([5],), dict(w0=-1), JL_EINVAL),
+])
+def test_decode_batch_rejects(args, kw, code):
+    rc, _ = _decb(*args, **kw)
+    assert rc == code, L.jl_last_error()
+    assert L.jl_last_error()
+
+
+def test_decode_batch_overlapping_rows_and_null_pointers():
+    rc, n = _decb([100, 100], row0=[0, 50], rows=150)    # shared cache rows are allowed
+    assert rc == JL_OK and n > 0
+    assert _decb([100, 100], row0=[0, 50], rows=150, ws=0x1000, nbytes=n)[0] == JL_EINVAL
+    assert _decb([100, 100], row0=[0, 50], rows=150, ws=0x1000, nbytes=n - 1)[0] == JL_ENOSPC
+    assert L.jl_bifocal_decode_batch(None, None, None, -1, None, None, 1, None, None, 32, 8, None, 128, jl.BF16,
+                                     16, 64, 1e6, 0.0, None, ctypes.byref(ctypes.c_size_t(0)), None) == JL_EINVAL
+
+
 def test_rope_rows_rejects_before_launch():
     f = L.jl_rope_rows
     assert f(None, None, 0, 2, 128, jl.BF16, 0, 1e4, None) == JL_OK            # empty: no-op

@@ -96,3 +96,22 @@ def test_empty_cache_is_noop():
     o, lse = jl.decode(q, kc, kc, 0, w0=4, w_pretrained=8, rope_base=1e4)
     torch.cuda.synchronize()
     assert o.shape == (4, 128)
+
+
+@pytest.mark.parametrize("L", [65537, 131072])
+def test_repeated_calls_are_bitwise_identical(L):
+    """A wave reads a sub-chunk's angle table only after every wave of the
+    workgroup has written its share, so identical calls give identical bits
+    (regression: a shared-total progress counter once let fast waves read a
+    table that slow waves were still filling)."""
+    jl, torch = gpu_or_skip()
+    cfg = W.decode_8b(L)
+    q, kc, vc = W.make_decode_inputs(cfg)
+    qd, kd, vd = q.cuda(), kc.cuda(), vc.cuda()
+    kw = dict(w0=cfg.w0, w_pretrained=cfg.w_pretrained, rope_base=cfg.rope_base)
+    o0, l0 = jl.decode(qd, kd, vd, L, **kw)
+    for _ in range(4):
+        o, l = jl.decode(qd, kd, vd, L, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o0.view(torch.int16))
+        assert torch.equal(l, l0)

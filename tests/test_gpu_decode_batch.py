@@ -1,0 +1,119 @@
+"""Ragged multi-sequence decode (one call, B sequences with their own L, G,
+query and cache rows) against the fp64 oracle's single-sequence decode of
+every sequence, and against the library's own single-sequence decode.  Every
+sequence follows the technical summary, Methodology item 2 on its own: its
+cache holds base keys at their absolute positions and its correction
+rotation depends on its own length."""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from jl_testutil import BF16_LSE_RTOL, BF16_O_ATOL, gpu_or_skip, lse_rel_err, max_abs
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _check_against_oracle(q, kc, vc, row0, lens, o, lse, seqs, w0, wpt, base, q_to_kv=None):
+    worst_o = worst_l = 0.0
+    for b in seqs:
+        L, r = lens[b], row0[b]
+        oo, ll = oracle.decode(q[b].double().numpy(), kc[r:r + L].double().numpy(), vc[r:r + L].double().numpy(),
+                               L, w0=w0, w_pretrained=wpt, rope_base=base, q_to_kv=q_to_kv)
+        e_o, e_l = max_abs(o[b], oo), lse_rel_err(lse[b], ll)
+        _say(f"[decode-batch] seq {b} L={L} G={oracle.group_size(L, wpt)}: max|do|={e_o:.3e} lse rel={e_l:.3e}")
+        worst_o, worst_l = max(worst_o, e_o), max(worst_l, e_l)
+    assert worst_o <= BF16_O_ATOL
+    assert worst_l <= BF16_LSE_RTOL
+
+
+def test_ragged_batch_matches_oracle():
+    """Qwen3-8B heads; lengths on both sides of the G boundary at 32768, one
+    empty sequence (its outputs stay untouched), spare rows between the
+    sequences' cache ranges."""
+    jl, torch = gpu_or_skip()
+    lens = [1, 63, 65, 4097, 0, 32768, 32769, 20000]
+    Hq, Hkv, w0, wpt, base = 32, 8, 4096, 32768, 1e6
+    q, kc, vc, row0 = W.make_decode_batch_inputs(Hq, Hkv, 128, lens, seed=41, gap=37)
+    _say(f"[decode-batch] lens={lens} rows={kc.shape[0]}")
+    qd, kd, vd = q.cuda(), kc.cuda(), vc.cuda()
+    k_sum = kd.view(torch.int16).sum(dtype=torch.int64).item()
+    o = torch.full_like(qd, 7.0)
+    lse = torch.full((len(lens), Hq), 7.0, device="cuda")
+    jl.decode_batch(qd, kd, vd, lens, row0=row0, w0=w0, w_pretrained=wpt, rope_base=base, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert kd.view(torch.int16).sum(dtype=torch.int64).item() == k_sum        # caches untouched
+    og, lg = o.float().cpu().numpy(), lse.cpu().numpy()
+    assert np.all(og[4] == 7.0) and np.all(lg[4] == 7.0)                    # L = 0: not written
+    _check_against_oracle(q, kc, vc, row0, lens, og, lg, [b for b in range(len(lens)) if lens[b]], w0, wpt, base)
+
+
+def test_small_heads_shared_rows_and_head_map():
+    """8 q / 2 kv heads with an explicit head map, G from 1 to 4, and two
+    sequences that read the same cache rows (the first a prefix of the
+    second)."""
+    jl, torch = gpu_or_skip()
+    lens = [3, 300, 1000, 129, 500, 700]
+    Hq, Hkv, w0, wpt, base = 8, 2, 100, 256, 1e4
+    kvmap = [1, 0, 1, 0, 0, 1, 1, 0]
+    q, kc, vc, row0 = W.make_decode_batch_inputs(Hq, Hkv, 128, lens, seed=43, gap=5)
+    row0[5] = row0[4]                       # sequence 5 extends sequence 4's rows
+    kc, vc = kc[:row0[4] + 700 + 5], vc[:row0[4] + 700 + 5]
+    o, lse = jl.decode_batch(q.cuda(), kc.cuda(), vc.cuda(), lens, row0=row0, w0=w0, w_pretrained=wpt,
+                             rope_base=base, q_to_kv=kvmap)
+    torch.cuda.synchronize()
+    _check_against_oracle(q, kc, vc, row0, lens, o.float().cpu().numpy(), lse.cpu().numpy(), range(len(lens)),
+                          w0, wpt, base, q_to_kv=kvmap)
+
+
+def test_one_sequence_is_the_single_call():
+    """A batch of one runs the same plan as jl_bifocal_decode: same bits."""
+    jl, torch = gpu_or_skip()
+    cfg = W.decode_8b(65537)
+    q, kc, vc = W.make_decode_inputs(cfg)
+    qd, kd, vd = q.cuda(), kc.cuda(), vc.cuda()
+    kw = dict(w0=cfg.w0, w_pretrained=cfg.w_pretrained, rope_base=cfg.rope_base)
+    o1, l1 = jl.decode(qd, kd, vd, cfg.L, **kw)
+    ob, lb = jl.decode_batch(qd[None], kd, vd, [cfg.L], **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), ob[0].view(torch.int16))
+    assert torch.equal(l1, lb[0])
+
+
+def test_varlen_8_sequences_8k_to_128k():
+    """Eight sequences with the Qwen3-4B varlen lengths (8K .. 128K, seeded),
+    32 q / 8 kv heads: every sequence against the library's single-sequence
+    decode, the shortest and the longest against the oracle."""
+    jl, torch = gpu_or_skip()
+    lens = list(W.varlen_4b(4096).seqlens)
+    Hq, Hkv, w0, wpt, base = 32, 8, 4096, 32768, 1e6
+    q, kc, vc, row0 = W.make_decode_batch_inputs(Hq, Hkv, 128, lens, seed=47, device="cuda")
+    _say(f"[decode-batch] lens={lens} rows={kc.shape[0]}")
+    kw = dict(w0=w0, w_pretrained=wpt, rope_base=base)
+    o, lse = jl.decode_batch(q, kc, vc, lens, row0=row0, **kw)
+    torch.cuda.synchronize()
+    worst_o = worst_l = 0.0
+    for b, L in enumerate(lens):
+        r = row0[b]
+        os_, ls_ = jl.decode(q[b], kc[r:r + L], vc[r:r + L], L, **kw)
+        torch.cuda.synchronize()
+        worst_o = max(worst_o, (o[b].float() - os_.float()).abs().max().item())
+        worst_l = max(worst_l, lse_rel_err(lse[b].cpu().numpy(), ls_.cpu().numpy()))
+    _say(f"[decode-batch] vs single-sequence calls: max|do|={worst_o:.3e} lse rel={worst_l:.3e}")
+    assert worst_o <= BF16_O_ATOL and worst_l <= BF16_LSE_RTOL
+    check = [lens.index(min(lens)), lens.index(max(lens))]
+    qc, og, lg = q.cpu(), o.float().cpu().numpy(), lse.cpu().numpy()
+    for b in check:
+        r, L = row0[b], lens[b]
+        oo, ll = oracle.decode(qc[b].double().numpy(), kc[r:r + L].cpu().double().numpy(),
+                               vc[r:r + L].cpu().double().numpy(), L, **kw)
+        e_o, e_l = max_abs(og[b], oo), lse_rel_err(lg[b], ll)
+        _say(f"[decode-batch] seq {b} L={L}: max|do|={e_o:.3e} lse rel={e_l:.3e}")
+        assert e_o <= BF16_O_ATOL and e_l <= BF16_LSE_RTOL

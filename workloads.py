@@ -116,6 +116,26 @@ def make_decode_inputs(cfg: DecodeConfig, L_cap: Optional[int] = None, seed: Opt
     return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
 
 
+def make_decode_batch_inputs(num_q_heads: int, num_kv_heads: int, head_dim: int, lens, seed: int,
+                             gap: int = 0, device: str = "cpu"):
+    """Returns (q [B, Hq, d], k_cache [R, Hkv, d], v_cache, row0) in bf16.
+
+    Sequence b's keys occupy cache rows row0[b] .. row0[b] + lens[b] - 1; the
+    sequences follow one another with ``gap`` spare rows after each (drawn
+    too, so reads outside a sequence's rows would see finite values).  With
+    device="cuda" the draws come from a generator on the GPU (large caches)."""
+    g = torch.Generator(device).manual_seed(seed)
+    row0, r = [], 0
+    for n in lens:
+        row0.append(r)
+        r += int(n) + gap
+    B = len(lens)
+    q = torch.randn((B, num_q_heads, head_dim), dtype=torch.float32, generator=g, device=device)
+    k = torch.randn((r, num_kv_heads, head_dim), dtype=torch.float32, generator=g, device=device)
+    v = torch.randn((r, num_kv_heads, head_dim), dtype=torch.float32, generator=g, device=device)
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16), row0
+
+
 def cu_seqlens_of(seqlens) -> List[int]:
     out = [0]
     for n in seqlens:
