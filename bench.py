@@ -24,6 +24,8 @@ Prints ONE JSON line:
             window pass on the base grid plus a far-only pass on the remote
             grid, merged with two positive weights): exactly the causal pair
             count, so its actual FLOPs are 4 d Hq L(L+1)/2;
+  decode_batch  one decode step for each of 8 ragged sequences (the Qwen3-4B
+            varlen lengths, 8K .. 128K) in one call, KV bytes over time;
   overhead  the bifocal calls over plain attention at the same shapes (the same
             library with w_pretrained = L, i.e. G = 1: plain causal RoPE prefill
             and Delta-free decode);
@@ -31,7 +33,7 @@ Prints ONE JSON line:
 
     python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--no-cpu-baseline] [--headline-only]
 
---headline-only skips the disjoint-merge, plain-attention and G-boundary runs, so
+--headline-only skips the disjoint-merge, plain-attention, G-boundary and batched-decode runs, so
 that in a profiler run every dispatch of a kernel has the headline shape.
 """
 
@@ -365,7 +367,36 @@ def main():
             f"disjoint merge {dj_ms:.2f} ms (far pass {dj_far_ms:.2f} ms)")
         return dj, ov
 
+    def run_decode_batch():
+        """Ragged batched decode: one step for each of the 8 sequences of the
+        Qwen3-4B varlen lengths (8K .. 128K), 32 q / 8 kv heads, caches packed."""
+        lens = list(W.varlen_4b(cfg.w0).seqlens)
+        qb, kb_, vb, row0 = W.make_decode_batch_inputs(Hq, Hkv, d, lens, seed=dcfg.seed, device="cuda")
+        ob = torch.empty_like(qb)
+        lb = torch.empty((len(lens), Hq), dtype=torch.float32, device=dev)
+        wsb = torch.empty(max(16, jl.decode_batch_workspace_bytes(lens, Hq, Hkv)), dtype=torch.uint8, device=dev)
+
+        def step():
+            jl.decode_batch(qb, kb_, vb, lens, row0=row0, w0=dcfg.w0, w_pretrained=dcfg.w_pretrained,
+                            rope_base=dcfg.rope_base, out=ob, lse=lb, workspace=wsb)
+
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+        n = 50
+        ev.record(e0, stream)
+        for _ in range(n):
+            step()
+        ev.record(e1, stream)
+        us = ev.elapsed_ms(e0, e1) * 1e3 / n
+        torch.cuda.synchronize()
+        kvb = 2 * sum(lens) * Hkv * d * 2
+        log(f"[bench] batched decode of {len(lens)} sequences: {us:.1f} us per step ({kvb / us / 1e3:.0f} GB/s)")
+        return {"lens": lens, "us_per_step": round(us, 2), "kv_bytes": kvb,
+                "GB/s": round(kvb / (us * 1e-6) / 1e9, 1), "frac_hbm": round(kvb / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+
     dj_obj, ov_obj = (None, None) if args.headline_only else run_extras()
+    db_obj = None if args.headline_only else run_decode_batch()
 
     tflops = F3 / (call_ms * 1e-3) / 1e12
     pass2_tflops = Fc / (pass2_ms * 1e-3) / 1e12
@@ -411,6 +442,7 @@ def main():
                    "step_frac_hbm": round(dec_gbs / PEAK_HBM_GBS, 4)},
         "disjoint_merge": dj_obj,
         "overhead": ov_obj,
+        "decode_batch": db_obj,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
