@@ -56,6 +56,16 @@ int build_head_map(JlHeadMap* hm, int Hq, int Hkv, const int32_t* q_to_kv) {
     }
   }
   for (int h = Hq; h < JL_MAX_HEADS; ++h) hm->kv_of[h] = 0;
+  for (int h = 0; h < JL_MAX_HEADS; ++h) hm->head_of_slot[h] = 0;
+  if (Hq % Hkv == 0) {
+    const int NG = Hq / Hkv;
+    int cnt[JL_MAX_HEADS] = {0};
+    for (int h = 0; h < Hq; ++h) {
+      const int kv = hm->kv_of[h];
+      if (cnt[kv] < NG) hm->head_of_slot[kv * NG + cnt[kv]] = (uint8_t)h;
+      ++cnt[kv];
+    }
+  }
   return JL_OK;
 }
 

@@ -231,17 +231,8 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
   const int c_begin = ((int)blockIdx.x - ds.wg_begin[b]) * nsub * SUB;
   const int nsc = min(nsub, (L - c_begin + SUB - 1) / SUB);     // sub-chunks holding keys: >= 1
 
-  if (tid < Hq) {
-    // slot s = kvh * NG + n  <->  the n-th q head (in head order) of kv head kvh
-    const int kvh = tid / NG, n = tid % NG;
-    int cnt = 0, hh = 0;
-    for (int h = 0; h < Hq; ++h)
-      if (hm.kv_of[h] == kvh) {
-        if (cnt == n) hh = h;
-        ++cnt;
-      }
-    heads[tid] = hh;
-  }
+  // slot s = kvh * NG + n  <->  the n-th q head (in head order) of kv head kvh
+  if (tid < Hq) heads[tid] = hm.head_of_slot[tid];
 
   const int kl = lane & 15, gq = lane >> 4;        // column / row index, lane group
   const int kvh = wave;                              // this wave's kv head
@@ -451,7 +442,7 @@ constexpr int RED_DEPTH = 8;
 
 __global__ void __launch_bounds__(256) decode_reduce_kernel(const float* __restrict__ part_ml,
                                                             const float* __restrict__ part_o, JlDecSeqs ds,
-                                                            int Hq, int NG, JlHeadMap hm,
+                                                            int Hq, JlHeadMap hm,
                                                             __bf16* __restrict__ o,
                                                             float* __restrict__ lse) {
   __shared__ float red_m[RED_GROUPS];
@@ -519,13 +510,7 @@ __global__ void __launch_bounds__(256) decode_reduce_kernel(const float* __restr
       A += e == 0 ? a.x : e == 1 ? a.y : e == 2 ? a.z : a.w;
       Lt += red_l[w];
     }
-    const int kvh = slot / NG, n = slot % NG;
-    int cnt = 0, head = 0;
-    for (int h = 0; h < Hq; ++h)
-      if (hm.kv_of[h] == kvh) {
-        if (cnt == n) head = h;
-        ++cnt;
-      }
+    const int head = hm.head_of_slot[slot];
     o[((int64_t)sq * Hq + head) * D + part * 16 + tid] = (__bf16)(A / Lt);
     if (lse != nullptr && part == 0 && tid == 0) lse[(int64_t)sq * Hq + head] = (M + __log2f(Lt)) * LN2;
   }
@@ -609,6 +594,6 @@ hipError_t jl_launch_decode_bf16(const void* q, const void* k_cache, const void*
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (hipEvent_t mid = jl_profile_mid_event()) (void)hipEventRecord(mid, st);
-  decode_reduce_kernel<<<dim3(Hq, 8, ds.nseq), 256, 0, st>>>(part_ml, part_o, ds, Hq, NG, hm, (__bf16*)o, lse);
+  decode_reduce_kernel<<<dim3(Hq, 8, ds.nseq), 256, 0, st>>>(part_ml, part_o, ds, Hq, hm, (__bf16*)o, lse);
   return hipGetLastError();
 }

@@ -42,6 +42,9 @@ struct JlFreqs {
 
 struct JlHeadMap {
   uint8_t kv_of[JL_MAX_HEADS];
+  // with NG = Hq / Hkv q heads on every kv head: slot kvh * NG + n holds the
+  // n-th q head (in head order) of kv head kvh (decode's head slots)
+  uint8_t head_of_slot[JL_MAX_HEADS];
 };
 
 // Workspace of the prefill path: rotated operands, head-major.
