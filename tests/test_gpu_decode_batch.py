@@ -73,6 +73,21 @@ def test_small_heads_shared_rows_and_head_map():
                           w0, wpt, base, q_to_kv=kvmap)
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 2), (3, 3)])
+def test_batch_group_sizes(Hq, Hkv):
+    """1, 8 and 1 (with three kv heads: a wave without a kv head) q heads per
+    kv head; ragged lengths with G from 1 to 5."""
+    jl, torch = gpu_or_skip()
+    lens = [700, 1, 2049, 333, 1500]
+    w0, wpt, base = 128, 400, 1e4
+    q, kc, vc, row0 = W.make_decode_batch_inputs(Hq, Hkv, 128, lens, seed=Hq * 10 + Hkv, gap=3)
+    o, lse = jl.decode_batch(q.cuda(), kc.cuda(), vc.cuda(), lens, row0=row0, w0=w0, w_pretrained=wpt,
+                             rope_base=base)
+    torch.cuda.synchronize()
+    _check_against_oracle(q, kc, vc, row0, lens, o.float().cpu().numpy(), lse.cpu().numpy(), range(len(lens)),
+                          w0, wpt, base)
+
+
 def test_one_sequence_is_the_single_call():
     """A batch of one runs the same plan as jl_bifocal_decode: same bits."""
     jl, torch = gpu_or_skip()

@@ -263,9 +263,11 @@ def test_disjoint_rejects_fp32():
         jl.prefill(x, x, x, w0=2, w_pretrained=4, rope_base=1e4, disjoint=True)
 
 
-def test_qwen3_4b_varlen():
+@pytest.mark.parametrize("w0", [1024, 4096, 8192])
+def test_qwen3_4b_varlen(w0):
+    """The Qwen3-4B varlen layer at each window of the sweep."""
     jl, torch = gpu_or_skip()
-    cfg = W.varlen_4b(1024)
+    cfg = W.varlen_4b(w0)
     # check the shortest and the longest sequence
     lens = list(cfg.seqlens)
     _check_sampled(jl, torch, cfg, n_random=4, seqs_to_check=[lens.index(min(lens)), lens.index(max(lens))])
