@@ -925,6 +925,16 @@ __device__ inline void pp_run(const PpTiles& T, const bf16x8* qf, PpState& st, f
 // output's own rounding.
 constexpr int O1_BYTES = PP_NT * 128;
 
+// The lane's 64 channels of an fp32 output row (channels db*32 + 8*q4 + 4*g
+// + 0..3 in slot 4*db + q4), all loads issued before any use: the merge
+// stores bf16 rows in between, and with the loads next to their uses the
+// compiler kept each behind the previous store (it cannot prove the two
+// arrays apart), one memory round trip per 16 bytes.
+__device__ inline void pp_load_row(float4* v, const float* row, int g) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = *(const float4*)(row + (i >> 2) * 32 + 8 * (i & 3) + 4 * g);
+}
+
 // ROLE 0: pass 2 (full causal, remote q/k).  ROLE 3: passes 1 and 3 of the
 // tile one after the other (window, base q/k, then window, remote q/k) and
 // the inclusion-exclusion merge with pass 2's output; sequences with
@@ -1045,12 +1055,14 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
     const float inv = 1.f / Z;
     const float* ofrow = A.o2 + ridx * D;
     __bf16* orow = A.out + ((s0 + wr.myrow) * A.Hq + h) * D;
+    float4 vfs[16];
+    pp_load_row(vfs, ofrow, g);
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d0 = db * 32 + 8 * q4 + 4 * g;
-        const float4 vf = *(const float4*)(ofrow + d0);
+        const float4 vf = vfs[4 * db + q4];
         const float ofv[4] = {vf.x, vf.y, vf.z, vf.w};
         bf16x4 w;
 #pragma unroll
@@ -1093,6 +1105,8 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
     const float Z = z1 + fmaxf(far, 0.f);
     const float inv = 1.f / Z;
     const float* o2row = A.o2 + ridx * D;
+    float4 v2s[16];
+    pp_load_row(v2s, o2row, g);
     const __attribute__((address_space(3))) bf16x8* o1s =
         (const __attribute__((address_space(3))) bf16x8*)(lds + 2 * (KT_BYTES + VT_BYTES)) + tid;
     __bf16* orow = A.out + ((s0 + wr.myrow) * A.Hq + h) * D;
@@ -1103,7 +1117,7 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
       for (int hq = 0; hq < 2; ++hq) {
         const int db = c >> 1, q4 = 2 * (c & 1) + hq;
         const int d0 = db * 32 + 8 * q4 + 4 * g;
-        const float4 v2 = *(const float4*)(o2row + d0);
+        const float4 v2 = v2s[4 * db + q4];
         const float o2v[4] = {v2.x, v2.y, v2.z, v2.w};
         bf16x4 w;
 #pragma unroll
