@@ -132,3 +132,16 @@ def test_varlen_8_sequences_8k_to_128k():
         e_o, e_l = max_abs(og[b], oo), lse_rel_err(lg[b], ll)
         _say(f"[decode-batch] seq {b} L={L}: max|do|={e_o:.3e} lse rel={e_l:.3e}")
         assert e_o <= BF16_O_ATOL and e_l <= BF16_LSE_RTOL
+
+
+def test_batch_repeated_calls_are_bitwise_identical():
+    jl, torch = gpu_or_skip()
+    lens = list(W.varlen_4b(4096).seqlens)[:4]
+    q, kc, vc, row0 = W.make_decode_batch_inputs(32, 8, 128, lens, seed=53, device="cuda")
+    kw = dict(row0=row0, w0=4096, w_pretrained=32768, rope_base=1e6)
+    o0, l0 = jl.decode_batch(q, kc, vc, lens, **kw)
+    for _ in range(3):
+        o, l = jl.decode_batch(q, kc, vc, lens, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o0.view(torch.int16))
+        assert torch.equal(l, l0)
