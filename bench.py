@@ -171,7 +171,7 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=320)
+    ap.add_argument("--cpu-rows", type=int, default=420)
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the disjoint-merge, plain-attention and G-boundary runs (profiling runs: every "
