@@ -145,3 +145,20 @@ def test_batch_repeated_calls_are_bitwise_identical():
         torch.cuda.synchronize()
         assert torch.equal(o.view(torch.int16), o0.view(torch.int16))
         assert torch.equal(l, l0)
+
+
+def test_batch_max_sequences():
+    """JL_MAX_SEQS (64) sequences of seeded lengths 0 .. 3000 in one call."""
+    jl, torch = gpu_or_skip()
+    g = torch.Generator("cpu").manual_seed(73)
+    lens = [int(x) for x in torch.randint(0, 3001, (64,), generator=g)]
+    lens[3] = 0
+    lens[4] = 1
+    Hq, Hkv, w0, wpt, base = 8, 2, 200, 700, 1e4
+    q, kc, vc, row0 = W.make_decode_batch_inputs(Hq, Hkv, 128, lens, seed=74, gap=1)
+    o = torch.zeros((64, Hq, 128), dtype=torch.bfloat16, device="cuda")
+    o, lse = jl.decode_batch(q.cuda(), kc.cuda(), vc.cuda(), lens, row0=row0, w0=w0, w_pretrained=wpt,
+                             rope_base=base, out=o)
+    torch.cuda.synchronize()
+    _check_against_oracle(q, kc, vc, row0, lens, o.float().cpu().numpy(), lse.cpu().numpy(),
+                          [b for b in range(64) if lens[b]], w0, wpt, base)

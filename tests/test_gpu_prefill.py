@@ -286,3 +286,23 @@ def test_repeated_calls_are_bitwise_identical(disjoint):
         torch.cuda.synchronize()
         assert torch.equal(o.view(torch.int16), o0.view(torch.int16))
         assert torch.equal(l, l0)
+
+
+def test_bf16_max_sequences_and_heads():
+    """JL_MAX_SEQS (64) packed sequences of seeded lengths 0 .. 300, each with
+    its own G, and 64 q heads on 8 kv heads."""
+    jl, torch = gpu_or_skip()
+    g = torch.Generator("cpu").manual_seed(71)
+    lens = [int(x) for x in torch.randint(0, 301, (64,), generator=g)]
+    lens[5] = 0
+    lens[9] = 1
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    _check_full(jl, torch, None, 64, 8, 128, "bf16", 40, 90, 1e6, seed=72, cu=cu)
+
+
+def test_bf16_max_q_heads():
+    """128 q heads (the most a call takes) on 16 kv heads, G = 3."""
+    jl, torch = gpu_or_skip()
+    _check_full(jl, torch, 700, 128, 16, 128, "bf16", 90, 256, 1e6, seed=75)
