@@ -35,12 +35,14 @@ int jl_test_remote_pos_device(int64_t x0, int64_t n, int64_t G, int32_t* f_out, 
 int jl_test_rope_angles_device(const int32_t* pos, int64_t n, int32_t m, int32_t head_dim,
                                double rope_base, float* cos_out, float* sin_out, void* hip_stream);
 
-/* Instrumentation for benchmarks: while set, every jl_bifocal_prefill and
-   jl_bifocal_decode call made on the calling thread records hipEvent_t
+/* Instrumentation for benchmarks: while set, every prefill and decode call
+   (jl_bifocal_prefill, jl_bifocal_prefill_disjoint, jl_bifocal_decode,
+   jl_bifocal_decode_batch) made on the calling thread records hipEvent_t
    `before` on its stream immediately before launching its attention
    kernels, `mid` (optional, may be NULL) right after its dominant kernel
-   (prefill: the full-causal pass-2 launches; decode: the split-K launch),
-   and `after` after the last of them.  The RoPE pre-pass of prefill stays
+   (prefill: the full-causal pass-2 launches, or the far pass of the
+   disjoint form; decode: the split-K launch), and `after` after the last of
+   them.  The RoPE pre-pass of prefill stays
    outside.  Pass NULL for all three to stop.  The events are the caller's;
    the library never creates or destroys them.  Returns JL_EINVAL if exactly
    one of `before` and `after` is NULL. */
