@@ -334,22 +334,24 @@ def main():
         dec_plain_us = ev.elapsed_ms(e0, e1) * 1e3 / args.decode_steps
         torch.cuda.synchronize()
 
-        # decode step time on both sides of the G boundaries (the cache is the same; only L moves)
-        def decode_at(Lx, i):
+        # decode step time on both sides of the G boundaries (the cache is the same; only L moves),
+        # bifocal and plain (w_pretrained = L: G = 1) at each length
+        def decode_at(Lx, i, wpt):
             kc, vc = caches[i % n_caches]
-            jl.decode(qd, kc, vc, Lx, w0=dcfg.w0, w_pretrained=dcfg.w_pretrained, rope_base=dcfg.rope_base,
+            jl.decode(qd, kc, vc, Lx, w0=dcfg.w0, w_pretrained=wpt, rope_base=dcfg.rope_base,
                       out=od, lse=lsed, workspace=wsd)
 
-        boundary = {}
+        boundary, boundary_plain = {}, {}
         for Lx in (32768, 32769, 65536, 65537):
-            for i in range(4):
-                decode_at(Lx, i)
-            torch.cuda.synchronize()
-            ev.record(e0, stream)
-            for i in range(100):
-                decode_at(Lx, i)
-            ev.record(e1, stream)
-            boundary[str(Lx)] = round(ev.elapsed_ms(e0, e1) * 1e3 / 100, 2)
+            for key, wpt in ((boundary, dcfg.w_pretrained), (boundary_plain, Lx)):
+                for i in range(4):
+                    decode_at(Lx, i, wpt)
+                torch.cuda.synchronize()
+                ev.record(e0, stream)
+                for i in range(100):
+                    decode_at(Lx, i, wpt)
+                ev.record(e1, stream)
+                key[str(Lx)] = round(ev.elapsed_ms(e0, e1) * 1e3 / 100, 2)
         torch.cuda.synchronize()
         dj = {"call_ms": round(dj_ms, 3), "tflops_actual": round(Fc / (dj_ms * 1e-3) / 1e12, 2),
               "frac_actual": round(Fc / (dj_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -362,7 +364,8 @@ def main():
               "prefill_bifocal_over_plain": round(call_ms / plain_ms, 4),
               "decode_plain_us_per_step": round(dec_plain_us, 2),
               "decode_bifocal_over_plain": round(dec_us / dec_plain_us, 4),
-              "decode_us_per_step_across_g_boundaries": boundary}
+              "decode_us_per_step_across_g_boundaries": boundary,
+              "decode_plain_us_per_step_at_those_lengths": boundary_plain}
         log(f"[bench] plain causal prefill {plain_ms:.2f} ms, Delta-free decode {dec_plain_us:.1f} us; "
             f"disjoint merge {dj_ms:.2f} ms (far pass {dj_far_ms:.2f} ms)")
         return dj, ov
