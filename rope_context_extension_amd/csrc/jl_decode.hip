@@ -63,6 +63,10 @@ constexpr int MAX_HKV = 8;
 constexpr int QPITCH = D + 8;      // bf16 elements per query row in LDS
 constexpr int TPITCH = 64 + 2;     // float2 entries per angle-table row
 constexpr int BUF_RSRC_WORD3 = 0x00020000;   // raw buffer, 32-bit data format
+// Cache-policy operands of the tile loads.  Every cache row is read once per
+// step.  V rows are loaded non-temporal (nt), K rows with the default policy.
+constexpr int K_LOAD_AUX = 0;
+constexpr int V_LOAD_AUX = 2;
 
 __device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -112,17 +116,17 @@ __device__ inline void load_k_blk(KTile& t, int blk, __amdgpu_buffer_rsrc_t rk, 
                                   int lane_off) {
   const int off = (row0 + blk * 16) * row_bytes + lane_off;
   // MFMA steps kb: channels (kb >> 1) * 64 + 8 (kb & 1) + 16 gq .. + 8
-  t.w[blk][0] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
-  t.w[blk][1] = __builtin_amdgcn_raw_buffer_load_b128(rk, off + 16, 0, 0);
-  t.w[blk][2] = __builtin_amdgcn_raw_buffer_load_b128(rk, off + 128, 0, 0);
-  t.w[blk][3] = __builtin_amdgcn_raw_buffer_load_b128(rk, off + 144, 0, 0);
+  t.w[blk][0] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, K_LOAD_AUX);
+  t.w[blk][1] = __builtin_amdgcn_raw_buffer_load_b128(rk, off + 16, 0, K_LOAD_AUX);
+  t.w[blk][2] = __builtin_amdgcn_raw_buffer_load_b128(rk, off + 128, 0, K_LOAD_AUX);
+  t.w[blk][3] = __builtin_amdgcn_raw_buffer_load_b128(rk, off + 144, 0, K_LOAD_AUX);
 }
 
 __device__ inline void load_v_half(VTile& t, int kh, __amdgpu_buffer_rsrc_t rv, int row0, int row_bytes,
                                    int lane_off) {
 #pragma unroll
   for (int x = 0; x < 8; ++x)
-    t.w[kh][x] = __builtin_amdgcn_raw_buffer_load_b128(rv, (row0 + 32 * kh + x) * row_bytes + lane_off, 0, 0);
+    t.w[kh][x] = __builtin_amdgcn_raw_buffer_load_b128(rv, (row0 + 32 * kh + x) * row_bytes + lane_off, 0, V_LOAD_AUX);
 }
 
 // Scores of one 16-key block against the rotated query columns: the lane's
