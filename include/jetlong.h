@@ -57,6 +57,10 @@ typedef enum { JL_BF16 = 0, JL_FP32 = 1 } jl_dtype;
 /* Largest number of sequences one jl_bifocal_prefill or jl_bifocal_decode_batch call accepts. */
 #define JL_MAX_SEQS 64
 
+/* Longest sequence the bf16 prefill accepts, 2^23 - 64 tokens: its tile copies address a sequence's
+   K and V rows (256 bytes per key) with 31-bit byte offsets. */
+#define JL_BF16_MAX_SEQ_LEN 8388544
+
 /*
  * Group size G = max(1, ceil(L / w_pretrained)) (technical summary,
  * Methodology item 1, group-size equation).  Host integer function, exact
@@ -86,7 +90,8 @@ int64_t jl_group_size(int64_t L, int64_t w_pretrained);
  *   dtype      JL_BF16: bf16 MFMA passes with fp32 accumulation, bf16 o.
  *              JL_FP32: fp32 vector-ALU passes (exactness reference path).
  *   w0         >= 0 local window; w_pretrained >= 1; rope_base > 0.
- *   Sequences longer than 2^31 - 1 tokens are JL_EUNSUPPORTED.
+ *   With JL_BF16, sequences longer than JL_BF16_MAX_SEQ_LEN tokens are
+ *   JL_EUNSUPPORTED (JL_FP32: longer than 2^31 - 513 in total).
  */
 int jl_bifocal_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
                        const int64_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,

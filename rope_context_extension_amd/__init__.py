@@ -23,6 +23,7 @@ __all__ = ["group_size", "prefill", "prefill_workspace_bytes", "decode", "decode
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjetlong.so")
 BF16, FP32 = 0, 1
+BF16_MAX_SEQ_LEN = 8388544   # JL_BF16_MAX_SEQ_LEN: longest sequence of the bf16 prefill
 _STATUS = {0: "JL_OK", -1: "JL_EINVAL", -2: "JL_EUNSUPPORTED", -3: "JL_ENOSPC", -4: "JL_EHIP"}
 
 _lib = None

@@ -123,6 +123,11 @@ static int prefill_impl(const void* q, const void* k, const void* v, void* o, fl
     int64_t s1 = cu_seqlens ? cu_seqlens[b + 1] : total_tokens;
     if (b == 0 && s0 != 0) return fail(JL_EINVAL, "cu_seqlens[0] != 0");
     if (s1 < s0) return fail(JL_EINVAL, "cu_seqlens decreases at %d", b);
+    // the bf16 pass kernels copy a sequence's K and V tiles through buffer
+    // resources with 31-bit byte offsets: 256 bytes per key, tiles of 64 keys
+    if (dtype == JL_BF16 && s1 - s0 > JL_BF16_MAX_SEQ_LEN)
+      return fail(JL_EUNSUPPORTED, "bf16 prefill supports sequences of up to %lld tokens (sequence %d has %lld)",
+                  (long long)JL_BF16_MAX_SEQ_LEN, b, (long long)(s1 - s0));
     pl.seqs.start[b] = (int32_t)s0;
     pl.seqs.len[b] = (int32_t)(s1 - s0);
     pl.seqs.G[b] = (int32_t)jl_group_size_i64(s1 - s0, w_pretrained);

@@ -82,6 +82,23 @@ def test_prefill_rejects(kw, code):
     assert L.jl_last_error()
 
 
+def test_bf16_prefill_sequence_length_limit():
+    # the bf16 pass kernels address one sequence's K/V rows with 31-bit byte
+    # offsets: up to 2^23 - 64 tokens per sequence, checked on the host
+    assert jl.BF16_MAX_SEQ_LEN == 2**23 - 64
+    rc, n = _pf(T=jl.BF16_MAX_SEQ_LEN)
+    assert rc == JL_OK and n > 0, L.jl_last_error()
+    rc, _ = _pf(T=jl.BF16_MAX_SEQ_LEN + 1)
+    assert rc == JL_EUNSUPPORTED and b"up to 8388544" in L.jl_last_error()
+    T = jl.BF16_MAX_SEQ_LEN + 100
+    rc, _ = _pf(T=T, nseq=2, cu=(ctypes.c_int64 * 3)(0, 100, T))
+    assert rc == JL_OK, L.jl_last_error()              # both sequences within the limit
+    rc, _ = _pf(T=T, nseq=2, cu=(ctypes.c_int64 * 3)(0, 99, T))
+    assert rc == JL_EUNSUPPORTED and b"sequence 1" in L.jl_last_error()
+    rc, _ = _pf(T=jl.BF16_MAX_SEQ_LEN + 1, dt=jl.FP32, d=64)
+    assert rc == JL_OK, L.jl_last_error()              # the fp32 path has no such limit
+
+
 def test_prefill_workspace_too_small_is_enospc():
     rc, n = _pf()
     # a non-NULL workspace that is too small is refused before any device access
