@@ -61,6 +61,10 @@ typedef enum { JL_BF16 = 0, JL_FP32 = 1 } jl_dtype;
    K and V rows (256 bytes per key) with 31-bit byte offsets. */
 #define JL_BF16_MAX_SEQ_LEN 8388544
 
+/* Longest sequence the fp32 prefill accepts, 2^24 tokens: it runs one 64-lane workgroup per query row,
+   and one dispatch holds fewer than 2^32 work-items. */
+#define JL_FP32_MAX_SEQ_LEN 16777216
+
 /*
  * Group size G = max(1, ceil(L / w_pretrained)) (technical summary,
  * Methodology item 1, group-size equation).  Host integer function, exact
@@ -74,8 +78,21 @@ int64_t jl_group_size(int64_t L, int64_t w_pretrained);
  * inclusion-exclusion merge of three flash passes combined through their
  * LogSumExp statistics (technical summary, Methodology item 2, "Inference
  * efficiency mechanisms": local window with base q/k, full causal with
- * remote q/k, local window with remote q/k; no mask matrix):
- *   out = (z1 o1 + z2 o2 - z3 o3) / (z1 + z2 - z3),  z_k = exp(lse_k - M).
+ * remote q/k, local window with remote q/k; no mask matrix).  With
+ * lse_k = log sum of pass k's weights, M = max(lse_1, lse_2) and
+ * z_k = exp(lse_k - M), the far mass z2 - z3 is clamped at zero:
+ *   far = max(z2 - z3, 0),
+ *   out = (z1 o1 + [far > 0] (z2 o2 - z3 o3)) / (z1 + far),
+ *   lse = M + log(z1 + far).
+ * In exact arithmetic z2 >= z3 and the clamp changes nothing; it keeps the
+ * result finite when rounding makes the difference negative.  Precision: the
+ * far mass is formed as the difference of two window-dominated terms, so a
+ * row whose far mass is small against its window mass under the remote grid
+ * loses relative precision in that term (rounding of passes 2 and 3 times
+ * z2 / (z1 + far)).  On inputs with large score spreads (q, k ~ N(0, 9) and
+ * more) this can move the output outside the range of V.
+ * jl_bifocal_prefill_disjoint computes the same attention with two positive
+ * weights and no cancelling term; prefer it for such inputs.
  *
  *   q          [total_tokens, num_q_heads, head_dim]  raw (pre-RoPE), dtype
  *   k, v       [total_tokens, num_kv_heads, head_dim] raw (pre-RoPE), dtype
@@ -91,7 +108,10 @@ int64_t jl_group_size(int64_t L, int64_t w_pretrained);
  *              JL_FP32: fp32 vector-ALU passes (exactness reference path).
  *   w0         >= 0 local window; w_pretrained >= 1; rope_base > 0.
  *   With JL_BF16, sequences longer than JL_BF16_MAX_SEQ_LEN tokens are
- *   JL_EUNSUPPORTED (JL_FP32: longer than 2^31 - 513 in total).
+ *   JL_EUNSUPPORTED; with JL_FP32, longer than JL_FP32_MAX_SEQ_LEN.  Either
+ *   way total_tokens is at most 2^31 - 513.
+ *   The work order follows the current device's XCD count (it must be the
+ *   device of hip_stream); results do not depend on it.
  */
 int jl_bifocal_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
                        const int64_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
@@ -141,6 +161,9 @@ int jl_bifocal_prefill_disjoint(const void* q, const void* k, const void* v, voi
  *   o        [num_q_heads, head_dim] bf16 (written)
  *   lse      [num_q_heads] fp32, or NULL
  *   head_dim 128; dtype must be JL_BF16.
+ *   The split of the keys over workgroups (and so the workspace size) follows
+ *   the compute-unit count of the current device, which must be the device
+ *   of hip_stream: query the size and call with the same device current.
  */
 int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_cache, int64_t L,
                       void* o, float* lse, int32_t num_q_heads, int32_t num_kv_heads,
@@ -188,7 +211,8 @@ int jl_bifocal_decode_batch(const void* q, const void* k_cache, const void* v_ca
  *
  *   x, y       [n_rows, num_heads, head_dim] dtype, device; y may equal x
  *              (in place), otherwise the ranges must not overlap
- *   pos0       position of row 0, >= 0; pos0 + n_rows - 1 < 2^31
+ *   pos0       position of row 0, >= 0; pos0 + n_rows - 1 < 2^31 (so any
+ *              n_rows up to 2^31 is launched, in a grid-stride loop)
  *   head_dim   even, <= 128
  *   n_rows == 0 does nothing.
  */

@@ -48,6 +48,20 @@ int jl_test_rope_angles_device(const int32_t* pos, int64_t n, int32_t m, int32_t
    one of `before` and `after` is NULL. */
 int jl_set_profile_events(void* before, void* mid, void* after);
 
+/* The device shape the library plans with: compute units and XCDs of the
+   current device, read once per device (hipDeviceAttributeMultiprocessorCount
+   and hipDeviceAttributeNumberOfXccs).  A host without a device reports the
+   full MI355X shape, 256 and 8.  Host function. */
+int jl_test_device_shape(int32_t* cus, int32_t* xcds);
+
+/* The decode plan (host function, nothing launched) for num_seqs sequences
+   of lens[b] keys on a device with `cus` compute units: *nsub = 64-key
+   sub-chunks per split workgroup, *nwg = split workgroups.  The plan takes
+   the smallest nsub whose workgroups fit one round (one per compute unit).
+   JL_EINVAL on a NULL pointer, cus < 1, num_seqs outside 1 .. JL_MAX_SEQS or
+   a length outside 0 .. 2^31 - 1. */
+int jl_test_decode_plan(const int64_t* lens, int32_t num_seqs, int32_t cus, int32_t* nsub, int32_t* nwg);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,6 +24,7 @@ __all__ = ["group_size", "prefill", "prefill_workspace_bytes", "decode", "decode
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjetlong.so")
 BF16, FP32 = 0, 1
 BF16_MAX_SEQ_LEN = 8388544   # JL_BF16_MAX_SEQ_LEN: longest sequence of the bf16 prefill
+FP32_MAX_SEQ_LEN = 16777216  # JL_FP32_MAX_SEQ_LEN: longest sequence of the fp32 prefill
 _STATUS = {0: "JL_OK", -1: "JL_EINVAL", -2: "JL_EUNSUPPORTED", -3: "JL_ENOSPC", -4: "JL_EHIP"}
 
 _lib = None
@@ -83,6 +84,11 @@ def lib() -> ctypes.CDLL:
                                                  c.c_void_p, c.c_void_p, c.c_void_p]
         L.jl_set_profile_events.restype = c.c_int
         L.jl_set_profile_events.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p]
+        L.jl_test_device_shape.restype = c.c_int
+        L.jl_test_device_shape.argtypes = [c.POINTER(c.c_int32), c.POINTER(c.c_int32)]
+        L.jl_test_decode_plan.restype = c.c_int
+        L.jl_test_decode_plan.argtypes = [c.POINTER(c.c_int64), c.c_int32, c.c_int32, c.POINTER(c.c_int32),
+                                          c.POINTER(c.c_int32)]
         _lib = L
     return _lib
 
@@ -121,6 +127,48 @@ def _i64_array(seq: Optional[Sequence[int]]):
     return (ctypes.c_int64 * len(seq))(*[int(x) for x in seq])
 
 
+def _need(cond: bool, msg: str, exc=ValueError) -> None:
+    if not cond:
+        raise exc(msg)
+
+
+def _check_tensor(name: str, t, shape, dtype) -> None:
+    """Structure of a tensor the C side will read or write through a raw
+    pointer: exact shape, dtype and a contiguous layout.  Checked for every
+    tensor before any device check and before any library call."""
+    import torch
+    _need(isinstance(t, torch.Tensor), f"{name} must be a torch.Tensor", TypeError)
+    _need(tuple(t.shape) == tuple(shape), f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    _need(t.dtype == dtype, f"{name} has dtype {t.dtype}, expected {dtype}", TypeError)
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def _check_devices(device, **tensors) -> None:
+    """Every tensor lives on the same GPU as the first one."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        _need(t.is_cuda, f"{name} must be a GPU tensor")
+        _need(t.device == device, f"{name} is on {t.device}, expected {device}")
+
+
+def _check_head_map(q_to_kv, Hq: int) -> None:
+    if q_to_kv is not None:
+        _need(len(q_to_kv) == Hq, f"q_to_kv has {len(q_to_kv)} entries, expected one per q head ({Hq})")
+
+
+def _workspace(workspace, need: int, device):
+    """The caller's workspace (uint8, contiguous, on the call's GPU) or a new one."""
+    import torch
+    if workspace is None:
+        return torch.empty(max(int(need), 16), dtype=torch.uint8, device=device)
+    _need(isinstance(workspace, torch.Tensor) and workspace.dim() == 1, "workspace must be a 1-D tensor")
+    _check_tensor("workspace", workspace, (workspace.numel(),), torch.uint8)
+    _check_devices(device, workspace=workspace)
+    _need(workspace.numel() >= need, f"workspace has {workspace.numel()} bytes, {need} needed")
+    return workspace
+
+
 def _dtype_code(t) -> int:
     import torch
     if t.dtype == torch.bfloat16:
@@ -157,30 +205,40 @@ def prefill(q, k, v, *, w0: int, w_pretrained: int, rope_base: float, cu_seqlens
     merge the window pass with a far-only pass instead of the three-pass
     inclusion-exclusion (bf16 only)."""
     import torch
-    if not (q.is_cuda and k.is_cuda and v.is_cuda):
-        raise ValueError("q, k, v must be GPU tensors")
-    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-    T, Hq, d = q.shape
-    Hkv = k.shape[1]
+    _need(isinstance(q, torch.Tensor) and q.dim() == 3, "q must be a [T, Hq, d] tensor")
     dt = _dtype_code(q)
-    if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise TypeError("q, k, v must share a dtype")
-    nseq = 1 if cu_seqlens is None else len(cu_seqlens) - 1
-    cu = _i64_array(cu_seqlens)
-    kvmap = _i32_array(q_to_kv)
-    o = torch.empty_like(q) if out is None else out
-    if return_lse and lse is None:
-        lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
-    n = ctypes.c_size_t(0)
-    _check(_prefill_call(None, None, None, None, None, cu, nseq, T, Hq, Hkv, kvmap, d, dt, w0,
-                         w_pretrained, rope_base, 0.0, None, n, None))
-    if workspace is None or workspace.numel() < n.value:
-        workspace = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=q.device)
-    n = ctypes.c_size_t(workspace.numel())
-    _check(_prefill_call(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse) if return_lse else None,
-                         cu, nseq, T, Hq, Hkv, kvmap, d, dt, w0, w_pretrained, rope_base,
-                         0.0 if scale is None else scale, _ptr(workspace), n, _stream(q.device),
-                         disjoint))
+    T, Hq, d = q.shape
+    _need(isinstance(k, torch.Tensor) and k.dim() == 3, "k must be a [T, Hkv, d] tensor")
+    Hkv = k.shape[1]
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    _check_tensor("k", k, (T, Hkv, d), q.dtype)
+    _check_tensor("v", v, (T, Hkv, d), q.dtype)
+    if out is not None:
+        _check_tensor("out", out, (T, Hq, d), q.dtype)
+    if return_lse and lse is not None:
+        _check_tensor("lse", lse, (Hq, T), torch.float32)
+    _check_head_map(q_to_kv, Hq)
+    if cu_seqlens is not None:
+        _need(len(cu_seqlens) >= 2 and int(cu_seqlens[0]) == 0 and int(cu_seqlens[-1]) == T,
+              "cu_seqlens must start at 0 and end at the token count")
+    _check_devices(q.device, q=q, k=k, v=v, out=out, lse=lse if return_lse else None, workspace=workspace)
+    # the plan follows the shape of the current device: make it the tensors' device
+    with torch.cuda.device(q.device):
+        nseq = 1 if cu_seqlens is None else len(cu_seqlens) - 1
+        cu = _i64_array(cu_seqlens)
+        kvmap = _i32_array(q_to_kv)
+        n = ctypes.c_size_t(0)
+        _check(_prefill_call(None, None, None, None, None, cu, nseq, T, Hq, Hkv, kvmap, d, dt, w0,
+                             w_pretrained, rope_base, 0.0, None, n, None, disjoint))
+        workspace = _workspace(workspace, int(n.value), q.device)
+        o = torch.empty_like(q) if out is None else out
+        if return_lse and lse is None:
+            lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+        n = ctypes.c_size_t(workspace.numel())
+        _check(_prefill_call(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse) if return_lse else None,
+                             cu, nseq, T, Hq, Hkv, kvmap, d, dt, w0, w_pretrained, rope_base,
+                             0.0 if scale is None else scale, _ptr(workspace), n, _stream(q.device),
+                             disjoint))
     return o, (lse if return_lse else None)
 
 
@@ -200,30 +258,40 @@ def decode(q, k_cache, v_cache, L: int, *, w0: int, w_pretrained: int, rope_base
     [L_cap, Hkv, d] bf16 holding base-rotated keys.  Returns (o [Hq, d], lse
     [Hq] or None)."""
     import torch
+    _need(isinstance(q, torch.Tensor) and q.dim() == 2, "q must be a [Hq, d] tensor")
+    _need(isinstance(k_cache, torch.Tensor) and k_cache.dim() == 3, "k_cache must be a [L_cap, Hkv, d] tensor")
     Hq, d = q.shape
     Hkv = k_cache.shape[1]
-    if k_cache.shape[0] < L or v_cache.shape[0] < L:
-        raise ValueError("cache shorter than L")
     q = q.contiguous()
-    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
-        raise ValueError("caches must be contiguous")
-    o = torch.empty_like(q) if out is None else out
-    if return_lse and lse is None:
-        lse = torch.empty((Hq,), dtype=torch.float32, device=q.device)
-    kvmap = _i32_array(q_to_kv)
-    dt = _dtype_code(q)
-    n = ctypes.c_size_t(0)
-    _check(lib().jl_bifocal_decode(None, None, None, int(L), None, None, Hq, Hkv, kvmap, d, dt,
-                                   int(w0), int(w_pretrained), float(rope_base), 0.0, None,
-                                   ctypes.byref(n), None))
-    if workspace is None or workspace.numel() < n.value:
-        workspace = torch.empty(max(int(n.value), 16), dtype=torch.uint8, device=q.device)
-    n = ctypes.c_size_t(workspace.numel())
-    _check(lib().jl_bifocal_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), int(L), _ptr(o),
-                                   _ptr(lse) if return_lse else None, Hq, Hkv, kvmap, d, dt,
-                                   int(w0), int(w_pretrained), float(rope_base),
-                                   0.0 if scale is None else float(scale), _ptr(workspace),
-                                   ctypes.byref(n), _stream(q.device)))
+    _check_tensor("q", q, (Hq, d), torch.bfloat16)
+    _check_tensor("k_cache", k_cache, (k_cache.shape[0], Hkv, d), torch.bfloat16)
+    _check_tensor("v_cache", v_cache, tuple(k_cache.shape), torch.bfloat16)
+    _need(0 <= int(L) <= k_cache.shape[0], f"L = {L} outside the cache's {k_cache.shape[0]} rows")
+    if out is not None:
+        _check_tensor("out", out, (Hq, d), torch.bfloat16)
+    if return_lse and lse is not None:
+        _check_tensor("lse", lse, (Hq,), torch.float32)
+    _check_head_map(q_to_kv, Hq)
+    _check_devices(q.device, q=q, k_cache=k_cache, v_cache=v_cache, out=out,
+                   lse=lse if return_lse else None, workspace=workspace)
+    # the plan follows the shape of the current device: make it the tensors' device
+    with torch.cuda.device(q.device):
+        kvmap = _i32_array(q_to_kv)
+        dt = _dtype_code(q)
+        n = ctypes.c_size_t(0)
+        _check(lib().jl_bifocal_decode(None, None, None, int(L), None, None, Hq, Hkv, kvmap, d, dt,
+                                       int(w0), int(w_pretrained), float(rope_base), 0.0, None,
+                                       ctypes.byref(n), None))
+        workspace = _workspace(workspace, int(n.value), q.device)
+        o = torch.empty_like(q) if out is None else out
+        if return_lse and lse is None:
+            lse = torch.empty((Hq,), dtype=torch.float32, device=q.device)
+        n = ctypes.c_size_t(workspace.numel())
+        _check(lib().jl_bifocal_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), int(L), _ptr(o),
+                                       _ptr(lse) if return_lse else None, Hq, Hkv, kvmap, d, dt,
+                                       int(w0), int(w_pretrained), float(rope_base),
+                                       0.0 if scale is None else float(scale), _ptr(workspace),
+                                       ctypes.byref(n), _stream(q.device)))
     return o, (lse if return_lse else None)
 
 
@@ -257,32 +325,43 @@ def decode_batch(q, k_cache, v_cache, lens, *, w0: int, w_pretrained: int, rope_
     or None); sequences with lens[b] == 0 leave their rows of o and lse
     unwritten."""
     import torch
+    _need(isinstance(q, torch.Tensor) and q.dim() == 3, "q must be a [B, Hq, d] tensor")
+    _need(isinstance(k_cache, torch.Tensor) and k_cache.dim() == 3, "k_cache must be a [R, Hkv, d] tensor")
     B, Hq, d = q.shape
     lens = [int(n) for n in lens]
-    if len(lens) != B:
-        raise ValueError("one length per query row")
+    _need(len(lens) == B, f"{len(lens)} lengths for {B} query rows")
     row0 = _packed_rows(lens) if row0 is None else [int(r) for r in row0]
-    if not (k_cache.is_contiguous() and v_cache.is_contiguous()) or k_cache.shape != v_cache.shape:
-        raise ValueError("caches must be contiguous and of one shape")
+    _need(len(row0) == B, f"{len(row0)} first rows for {B} query rows")
     R, Hkv = k_cache.shape[0], k_cache.shape[1]
     q = q.contiguous()
-    o = torch.empty_like(q) if out is None else out
-    if return_lse and lse is None:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    kvmap = _i32_array(q_to_kv)
-    r0, ln = _i64_array(row0), _i64_array(lens)
-    dt = _dtype_code(q)
-    n = ctypes.c_size_t(0)
-    _check(lib().jl_bifocal_decode_batch(None, None, None, R, r0, ln, B, None, None, Hq, Hkv, kvmap, d, dt,
-                                         int(w0), int(w_pretrained), float(rope_base), 0.0, None,
-                                         ctypes.byref(n), None))
-    if workspace is None or workspace.numel() < n.value:
-        workspace = torch.empty(max(int(n.value), 16), dtype=torch.uint8, device=q.device)
-    n = ctypes.c_size_t(workspace.numel())
-    _check(lib().jl_bifocal_decode_batch(_ptr(q), _ptr(k_cache), _ptr(v_cache), R, r0, ln, B, _ptr(o),
-                                         _ptr(lse) if return_lse else None, Hq, Hkv, kvmap, d, dt, int(w0),
-                                         int(w_pretrained), float(rope_base), 0.0 if scale is None else float(scale),
-                                         _ptr(workspace), ctypes.byref(n), _stream(q.device)))
+    _check_tensor("q", q, (B, Hq, d), torch.bfloat16)
+    _check_tensor("k_cache", k_cache, (R, Hkv, d), torch.bfloat16)
+    _check_tensor("v_cache", v_cache, (R, Hkv, d), torch.bfloat16)
+    if out is not None:
+        _check_tensor("out", out, (B, Hq, d), torch.bfloat16)
+    if return_lse and lse is not None:
+        _check_tensor("lse", lse, (B, Hq), torch.float32)
+    _check_head_map(q_to_kv, Hq)
+    _check_devices(q.device, q=q, k_cache=k_cache, v_cache=v_cache, out=out,
+                   lse=lse if return_lse else None, workspace=workspace)
+    # the plan follows the shape of the current device: make it the tensors' device
+    with torch.cuda.device(q.device):
+        kvmap = _i32_array(q_to_kv)
+        r0, ln = _i64_array(row0), _i64_array(lens)
+        dt = _dtype_code(q)
+        n = ctypes.c_size_t(0)
+        _check(lib().jl_bifocal_decode_batch(None, None, None, R, r0, ln, B, None, None, Hq, Hkv, kvmap, d, dt,
+                                             int(w0), int(w_pretrained), float(rope_base), 0.0, None,
+                                             ctypes.byref(n), None))
+        workspace = _workspace(workspace, int(n.value), q.device)
+        o = torch.empty_like(q) if out is None else out
+        if return_lse and lse is None:
+            lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        n = ctypes.c_size_t(workspace.numel())
+        _check(lib().jl_bifocal_decode_batch(_ptr(q), _ptr(k_cache), _ptr(v_cache), R, r0, ln, B, _ptr(o),
+                                             _ptr(lse) if return_lse else None, Hq, Hkv, kvmap, d, dt, int(w0),
+                                             int(w_pretrained), float(rope_base), 0.0 if scale is None else float(scale),
+                                             _ptr(workspace), ctypes.byref(n), _stream(q.device)))
     return o, (lse if return_lse else None)
 
 
@@ -290,12 +369,14 @@ def rope_rows(x, pos0: int, *, rope_base: float, out=None):
     """Base RoPE of the rows of x [n, H, d] (bf16 or fp32) at positions pos0,
     pos0 + 1, ...; out may be x itself.  Returns out."""
     import torch
-    if x.dim() != 3 or not x.is_contiguous():
-        raise ValueError("x must be a contiguous [n, H, d] tensor")
+    _need(isinstance(x, torch.Tensor) and x.dim() == 3, "x must be an [n, H, d] tensor")
+    _check_tensor("x", x, tuple(x.shape), x.dtype)
+    dt = _dtype_code(x)
+    if out is not None:
+        _check_tensor("out", out, tuple(x.shape), x.dtype)
+    _check_devices(x.device, x=x, out=out)
     o = torch.empty_like(x) if out is None else out
-    if o.shape != x.shape or o.dtype != x.dtype or not o.is_contiguous():
-        raise ValueError("out must match x")
     n, H, d = x.shape
-    _check(lib().jl_rope_rows(_ptr(x), _ptr(o), n, H, d, _dtype_code(x), int(pos0), float(rope_base),
+    _check(lib().jl_rope_rows(_ptr(x), _ptr(o), n, H, d, dt, int(pos0), float(rope_base),
                               _stream(x.device)))
     return o

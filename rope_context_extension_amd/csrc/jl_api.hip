@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/jetlong_testing.h"
 #include "jl_internal.h"
 
@@ -76,6 +78,27 @@ int check_common(int64_t w0, int64_t w_pretrained, double rope_base) {
   return JL_OK;
 }
 
+// The device-shape cache: one entry per device, filled once under its flag.
+constexpr int JL_MAX_DEVICES = 64;
+std::once_flag g_shape_once[JL_MAX_DEVICES];
+JlDevShape g_shape[JL_MAX_DEVICES];
+const JlDevShape kDefaultShape{256, 8};   // a full MI355X: 256 CUs in 8 XCDs of 32
+
+JlDevShape read_device_shape(int dev) {
+  JlDevShape s = kDefaultShape;
+  int cus = 0, xccs = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return s;
+  s.cus = cus;
+  // XCD count as the runtime reports it; gfx950 has 32 CUs per XCD in every
+  // partition mode, which serves when the attribute is missing
+  if (hipDeviceGetAttribute(&xccs, hipDeviceAttributeNumberOfXccs, dev) == hipSuccess && xccs >= 1)
+    s.xcds = xccs;
+  else
+    s.xcds = cus >= 32 ? cus / 32 : 1;
+  return s;
+}
+
 struct PrefillPlan {
   JlSeqs seqs;
   int32_t max_len;
@@ -84,6 +107,16 @@ struct PrefillPlan {
 };
 
 }  // namespace
+
+JlDevShape jl_device_shape() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= JL_MAX_DEVICES) {
+    (void)hipGetLastError();   // no device on this host: clear the sticky error
+    return kDefaultShape;
+  }
+  std::call_once(g_shape_once[dev], [dev] { g_shape[dev] = read_device_shape(dev); });
+  return g_shape[dev];
+}
 
 JL_EXPORT int64_t jl_group_size(int64_t L, int64_t w_pretrained) {
   if (L < 0 || w_pretrained < 1) return fail(JL_EINVAL, "jl_group_size needs L >= 0 and w_pretrained >= 1");
@@ -128,6 +161,10 @@ static int prefill_impl(const void* q, const void* k, const void* v, void* o, fl
     if (dtype == JL_BF16 && s1 - s0 > JL_BF16_MAX_SEQ_LEN)
       return fail(JL_EUNSUPPORTED, "bf16 prefill supports sequences of up to %lld tokens (sequence %d has %lld)",
                   (long long)JL_BF16_MAX_SEQ_LEN, b, (long long)(s1 - s0));
+    // the fp32 kernel runs one 64-lane workgroup per row of a sequence
+    if (dtype == JL_FP32 && s1 - s0 > JL_FP32_MAX_SEQ_LEN)
+      return fail(JL_EUNSUPPORTED, "fp32 prefill supports sequences of up to %lld tokens (sequence %d has %lld)",
+                  (long long)JL_FP32_MAX_SEQ_LEN, b, (long long)(s1 - s0));
     pl.seqs.start[b] = (int32_t)s0;
     pl.seqs.len[b] = (int32_t)(s1 - s0);
     pl.seqs.G[b] = (int32_t)jl_group_size_i64(s1 - s0, w_pretrained);
@@ -297,7 +334,7 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache, 
   }
   if (total > (int64_t)INT32_MAX * 16) return fail(JL_EUNSUPPORTED, "too many keys in one call");
   JlDecSeqs ds;
-  jl_decode_plan(lens, row0, num_seqs, w0, w_pretrained, &ds);
+  jl_decode_plan(lens, row0, num_seqs, w0, w_pretrained, jl_device_shape().cus, &ds);
   const size_t need = total == 0 ? 0 : jl_decode_workspace_bytes(ds, num_q_heads);
   if (workspace == nullptr) {
     *workspace_bytes = need;
@@ -373,6 +410,28 @@ JL_EXPORT int jl_set_profile_events(void* before, void* mid, void* after) {
 }
 
 hipEvent_t jl_profile_mid_event() { return g_ev_mid; }
+
+JL_EXPORT int jl_test_device_shape(int32_t* cus, int32_t* xcds) {
+  if (!cus || !xcds) return fail(JL_EINVAL, "bad arguments");
+  const JlDevShape s = jl_device_shape();
+  *cus = s.cus;
+  *xcds = s.xcds;
+  return JL_OK;
+}
+
+JL_EXPORT int jl_test_decode_plan(const int64_t* lens, int32_t num_seqs, int32_t cus, int32_t* nsub,
+                                  int32_t* nwg) {
+  if (!lens || !nsub || !nwg || num_seqs < 1 || num_seqs > JL_MAX_SEQS || cus < 1)
+    return fail(JL_EINVAL, "bad arguments");
+  int64_t row0[JL_MAX_SEQS] = {0};
+  for (int b = 0; b < num_seqs; ++b)
+    if (lens[b] < 0 || lens[b] > (int64_t)INT32_MAX) return fail(JL_EINVAL, "bad length");
+  JlDecSeqs ds;
+  jl_decode_plan(lens, row0, num_seqs, 0, 1, cus, &ds);
+  *nsub = ds.nsub;
+  *nwg = ds.wg_begin[num_seqs];
+  return JL_OK;
+}
 
 JL_EXPORT int jl_test_group_size_device(const int64_t* L, int64_t n, int64_t w_pretrained, int64_t* G_out,
                                         void* hip_stream) {

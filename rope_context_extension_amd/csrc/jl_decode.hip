@@ -522,9 +522,8 @@ __global__ void __launch_bounds__(256) decode_reduce_kernel(const float* __restr
 
 }  // namespace
 
-// Compute units of an MI355X; one split workgroup fits per compute unit (its
-// LDS use is above half of the 160 KB).
-constexpr int64_t DEC_CUS = 256;
+// One split workgroup fits per compute unit (its LDS use is above half of the
+// 160 KB), so a round of the split launch is one workgroup per compute unit.
 constexpr int64_t DEC_MAX_NSUB = 1024;   // 65536 keys per workgroup: byte offsets stay in 32 bits
 
 static int64_t decode_wgs(const int64_t* lens, int nseq, int64_t nsub) {
@@ -536,21 +535,21 @@ static int64_t decode_wgs(const int64_t* lens, int nseq, int64_t nsub) {
 // The smallest sub-chunk count per workgroup whose workgroups all fit one
 // round on the compute units: a second, partly filled round would cost a
 // whole workgroup's time for a few keys.
-static int decode_nsub(const int64_t* lens, int nseq) {
-  if (decode_wgs(lens, nseq, DEC_MAX_NSUB) > DEC_CUS) return (int)DEC_MAX_NSUB;
+static int decode_nsub(const int64_t* lens, int nseq, int64_t cus) {
+  if (decode_wgs(lens, nseq, DEC_MAX_NSUB) > cus) return (int)DEC_MAX_NSUB;
   int64_t lo = 1, hi = DEC_MAX_NSUB;
   while (lo < hi) {
     const int64_t mid = (lo + hi) / 2;
-    if (decode_wgs(lens, nseq, mid) <= DEC_CUS) hi = mid;
+    if (decode_wgs(lens, nseq, mid) <= cus) hi = mid;
     else lo = mid + 1;
   }
   return (int)lo;
 }
 
 void jl_decode_plan(const int64_t* lens, const int64_t* row0, int32_t nseq, int64_t w0, int64_t w_pretrained,
-                    JlDecSeqs* ds) {
+                    int32_t cus, JlDecSeqs* ds) {
   ds->nseq = nseq;
-  ds->nsub = decode_nsub(lens, nseq);
+  ds->nsub = decode_nsub(lens, nseq, cus < 1 ? 1 : cus);
   const int64_t chunk = (int64_t)ds->nsub * SUB;
   int wg = 0;
   for (int b = 0; b < JL_MAX_SEQS; ++b) {

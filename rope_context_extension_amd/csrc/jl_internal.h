@@ -28,7 +28,8 @@ struct JlSeqs {
 struct JlSched {
   int32_t nlev;
   int32_t total_units;
-  int32_t xcd_heads;           // Hq / 8 when Hq % 8 == 0, else 0
+  int32_t nxcd;                // XCDs of the device (workgroup n runs on XCD n % nxcd)
+  int32_t xcd_heads;           // Hq / nxcd when Hq % nxcd == 0, else 0
   int32_t c[JL_MAX_SEQS];
   int32_t perm[JL_MAX_SEQS];
   uint8_t head_order[JL_MAX_HEADS];   // q heads grouped by kv head
@@ -80,6 +81,16 @@ struct JlPrefillWs {
 // sequence, whose rows see at most this many keys.
 #define JL_LO_ROWS 128
 
+// Shape of the device the calls launch on: compute units and XCDs (each XCD
+// has its own L2; workgroup n of a dispatch runs on XCD n % xcds).  Read once
+// per device (the library's only global state) from the current device; a
+// host without a device gets the full MI355X shape, 256 CUs in 8 XCDs.
+struct JlDevShape {
+  int32_t cus;
+  int32_t xcds;
+};
+JlDevShape jl_device_shape();
+
 int64_t jl_prefill_t_pad(int64_t total_tokens);
 
 // rope pre-pass: writes qb, qr, kb, kr (elem = 2 for bf16, 4 for fp32); q is scaled by qscale
@@ -116,8 +127,9 @@ struct JlDecSeqs {
   int64_t row0[JL_MAX_SEQS];           // first cache row of the sequence
 };
 // plan of a call (host): nsub from the total key count, workgroups per sequence
+// cus: compute units of the device (one split workgroup per compute unit)
 void jl_decode_plan(const int64_t* lens, const int64_t* row0, int32_t nseq, int64_t w0,
-                    int64_t w_pretrained, JlDecSeqs* ds);
+                    int64_t w_pretrained, int32_t cus, JlDecSeqs* ds);
 size_t jl_decode_workspace_bytes(const JlDecSeqs& ds, int32_t Hq);
 hipError_t jl_launch_decode_bf16(const void* q, const void* k_cache, const void* v_cache,
                                  const JlDecSeqs& ds, void* o, float* lse, int32_t Hq, int32_t Hkv,

@@ -34,8 +34,9 @@
 //   the 8 P values a lane feeds to one PV MFMA belong to 8 consecutive keys,
 //   i.e. one contiguous 16-byte read of a V^T row.
 //
-// Work order: block n -> (xcd stream n % 8, slot n / 8).  With Hq % 8 == 0
-// each stream owns Hq / 8 heads that share kv heads, so the K/V tiles a head
+// Work order: block n -> (xcd stream n % X, slot n / X) for the X XCDs of the
+// device (the dispatcher deals workgroups to the XCDs round robin).  With
+// Hq % X == 0 each stream owns Hq / X heads that share kv heads, so the K/V tiles a head
 // group streams stay in that XCD's L2; within a stream the (sequence, q tile)
 // units come heaviest first (descending q tile index) for load balance.
 #include "jl_internal.h"
@@ -373,7 +374,7 @@ __device__ inline bool block_item(const JlSched& sc, int Hq, int* h, int* b, int
   }
   int u;
   if (sc.xcd_heads > 0) {
-    const int s = n & 7, slot = n >> 3;
+    const int slot = n / sc.nxcd, s = n - slot * sc.nxcd;
     u = slot / sc.xcd_heads;
     *h = sc.head_order[s * sc.xcd_heads + slot % sc.xcd_heads];
   } else {
@@ -1134,7 +1135,7 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
 
 }  // namespace
 
-void jl_build_sched(const JlSeqs& seqs, const JlHeadMap& hm, int Hq, JlSched* sc) {
+void jl_build_sched(const JlSeqs& seqs, const JlHeadMap& hm, int Hq, int nxcd, JlSched* sc) {
   // 256-row units of rows >= 128 of every sequence, grouped into levels of
   // equal count
   int c[JL_MAX_SEQS], perm[JL_MAX_SEQS], n = 0;
@@ -1164,7 +1165,8 @@ void jl_build_sched(const JlSeqs& seqs, const JlHeadMap& hm, int Hq, JlSched* sc
     for (int h = 0; h < Hq; ++h)
       if (hm.kv_of[h] == kv) sc->head_order[o++] = (uint8_t)h;
   for (int h = Hq; h < JL_MAX_HEADS; ++h) sc->head_order[h] = 0;
-  sc->xcd_heads = (Hq % 8 == 0) ? Hq / 8 : 0;
+  sc->nxcd = nxcd < 1 ? 1 : nxcd;
+  sc->xcd_heads = (Hq % sc->nxcd == 0) ? Hq / sc->nxcd : 0;
 }
 
 hipError_t jl_launch_prefill_bf16(const JlPrefillWs& ws, void* o, float* lse, int64_t total_tokens,
@@ -1173,7 +1175,7 @@ hipError_t jl_launch_prefill_bf16(const JlPrefillWs& ws, void* o, float* lse, in
   (void)Hkv;
   (void)max_len;
   JlSched sc;
-  jl_build_sched(seqs, hm, Hq, &sc);
+  jl_build_sched(seqs, hm, Hq, jl_device_shape().xcds, &sc);
   PrefillArgs A;
   A.qb = (const __bf16*)ws.qb;
   A.qr = (const __bf16*)ws.qr;

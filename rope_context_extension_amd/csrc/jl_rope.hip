@@ -127,22 +127,26 @@ __global__ void __launch_bounds__(256) rope_prepass_kernel(
 // that build or extend a decode cache of base-rotated keys, or rotate the
 // newest query (technical summary on gist.science, Methodology item 2: the
 // cache holds keys rotated at their absolute positions).  y may alias x.
+// Grid-stride over the n * d/2 (row, m) items, so any row count fits one
+// dispatch.
 template <typename T>
 __global__ void __launch_bounds__(256) rope_rows_kernel(const T* x, T* y, int64_t n, int H, int d,
                                                         int64_t pos0, JlFreqs fr) {
   const int half = d >> 1;
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= n * half) return;
-  const int64_t r = e / half;
-  const int m = (int)(e - r * half);
-  float c, s;
-  jl_rope_sincos((int32_t)(pos0 + r), fr.turn_frac[m], &s, &c);
-  for (int h = 0; h < H; ++h) {
-    const T* xr = x + (r * H + h) * d;
-    T* yr = y + (r * H + h) * d;
-    const float x1 = ld_f(xr + m), x2 = ld_f(xr + m + half);
-    st_f(yr + m, x1 * c - x2 * s);
-    st_f(yr + m + half, x2 * c + x1 * s);
+  const int64_t items = n * half;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < items; e += stride) {
+    const int64_t r = e / half;
+    const int m = (int)(e - r * half);
+    float c, s;
+    jl_rope_sincos((int32_t)(pos0 + r), fr.turn_frac[m], &s, &c);
+    for (int h = 0; h < H; ++h) {
+      const T* xr = x + (r * H + h) * d;
+      T* yr = y + (r * H + h) * d;
+      const float x1 = ld_f(xr + m), x2 = ld_f(xr + m + half);
+      st_f(yr + m, x1 * c - x2 * s);
+      st_f(yr + m + half, x2 * c + x1 * s);
+    }
   }
 }
 
@@ -223,7 +227,8 @@ hipError_t jl_launch_transpose_v(const void* v, const JlPrefillWs& ws, const JlS
 hipError_t jl_launch_rope_rows(const void* x, void* y, int elem_bytes, int64_t n, int32_t H, int32_t d,
                                int64_t pos0, const JlFreqs& fr, hipStream_t st) {
   const int64_t work = n * (d / 2);
-  const unsigned blocks = (unsigned)((work + 255) / 256);
+  const int64_t need = (work + 255) / 256;
+  const unsigned blocks = (unsigned)(need < (1 << 20) ? need : (1 << 20));   // then grid-stride
   if (elem_bytes == 2)
     rope_rows_kernel<__bf16><<<blocks, 256, 0, st>>>((const __bf16*)x, (__bf16*)y, n, H, d, pos0, fr);
   else

@@ -96,7 +96,20 @@ def test_bf16_prefill_sequence_length_limit():
     rc, _ = _pf(T=T, nseq=2, cu=(ctypes.c_int64 * 3)(0, 99, T))
     assert rc == JL_EUNSUPPORTED and b"sequence 1" in L.jl_last_error()
     rc, _ = _pf(T=jl.BF16_MAX_SEQ_LEN + 1, dt=jl.FP32, d=64)
-    assert rc == JL_OK, L.jl_last_error()              # the fp32 path has no such limit
+    assert rc == JL_OK, L.jl_last_error()              # the fp32 path has its own, larger limit
+
+
+def test_fp32_prefill_sequence_length_limit():
+    # one 64-lane workgroup per row: a sequence past 2^24 rows would exceed a
+    # dispatch's 2^32 work-items, so the host refuses it before any launch
+    assert jl.FP32_MAX_SEQ_LEN == 2**24
+    rc, n = _pf(T=jl.FP32_MAX_SEQ_LEN, dt=jl.FP32, d=64)
+    assert rc == JL_OK and n > 0, L.jl_last_error()
+    rc, _ = _pf(T=jl.FP32_MAX_SEQ_LEN + 1, dt=jl.FP32, d=64)
+    assert rc == JL_EUNSUPPORTED and b"fp32 prefill supports" in L.jl_last_error()
+    T = jl.FP32_MAX_SEQ_LEN + 10
+    rc, _ = _pf(T=T, nseq=2, cu=(ctypes.c_int64 * 3)(0, 10, T), dt=jl.FP32, d=64)
+    assert rc == JL_OK, L.jl_last_error()
 
 
 def test_prefill_workspace_too_small_is_enospc():
@@ -227,3 +240,46 @@ def test_rope_rows_rejects_before_launch():
     assert f(None, None, 4, 2, 128, 7, 0, 1e4, None) == JL_EINVAL
     assert f(None, None, 4, 2, 128, jl.BF16, 0, 1e4, None) == JL_EINVAL       # null pointers
     assert b"device pointers" in L.jl_last_error()
+
+
+def _plan(lens, cus):
+    nsub, nwg = ctypes.c_int32(), ctypes.c_int32()
+    arr = (ctypes.c_int64 * len(lens))(*lens)
+    rc = L.jl_test_decode_plan(arr, len(lens), cus, ctypes.byref(nsub), ctypes.byref(nwg))
+    assert rc == JL_OK, L.jl_last_error()
+    return nsub.value, nwg.value
+
+
+def test_decode_plan_follows_the_compute_unit_count():
+    """The split plan fills one round of the device's compute units: the
+    smallest 64-key sub-chunk count whose workgroups fit one per CU.  A full
+    MI355X (256 CUs) and its partition modes (128, 64, 32 CUs) each get
+    their own plan."""
+    for cus, nsub in ((256, 8), (128, 16), (64, 32), (32, 64)):
+        assert _plan([131072], cus) == (nsub, cus), cus
+    # 32769 keys = 513 sub-chunks: 171 workgroups of 3 on 256 CUs, 65 of 8 on 80 CUs
+    assert _plan([32769], 256) == (3, 171)
+    assert _plan([32769], 80) == (7, 74)
+    # one key per CU at most: small caches take one sub-chunk per workgroup
+    assert _plan([100], 256) == (1, 2)
+    # a batch shares one plan across its sequences
+    nsub, nwg = _plan([131072, 65536, 1], 256)
+    assert nwg <= 256 and _plan([131072, 65536, 1], 128)[1] <= 128
+    for cus in (7, 100, 304):
+        nsub, nwg = _plan([131072, 12345], cus)
+        assert nwg <= cus
+        assert nsub == 1 or sum(-(-n // (64 * (nsub - 1))) for n in (131072, 12345)) > cus
+    bad = ctypes.c_int32()
+    assert L.jl_test_decode_plan((ctypes.c_int64 * 1)(5), 1, 0, ctypes.byref(bad), ctypes.byref(bad)) == JL_EINVAL
+
+
+def test_device_shape_default_without_a_device():
+    """On a host without a GPU the library plans for the full MI355X shape;
+    on a GPU the shape is read from the device (checked by the GPU tests)."""
+    import torch
+    cus, xcds = ctypes.c_int32(), ctypes.c_int32()
+    assert L.jl_test_device_shape(ctypes.byref(cus), ctypes.byref(xcds)) == JL_OK
+    if not torch.cuda.is_available():
+        assert (cus.value, xcds.value) == (256, 8)
+    else:
+        assert cus.value >= 1 and 1 <= xcds.value <= cus.value

@@ -3,6 +3,7 @@
 (technical summary, Methodology item 1: group-size equation and remote map)."""
 
 import math
+import sys
 
 import numpy as np
 import pytest
@@ -60,3 +61,16 @@ def test_device_angles_accurate_at_long_positions():
             err = max(np.abs(c.cpu().numpy() - np.cos(ang)).max(), np.abs(s.cpu().numpy() - np.sin(ang)).max())
             worst = max(worst, err)
     assert worst < 2e-6, worst
+
+
+def test_device_shape_matches_the_runtime():
+    """The library plans with the device's own compute-unit count (decode's
+    one-round split) and XCD count (prefill's per-XCD head groups)."""
+    import ctypes
+    jl, torch = gpu_or_skip()
+    cus, xcds = ctypes.c_int32(), ctypes.c_int32()
+    assert jl.lib().jl_test_device_shape(ctypes.byref(cus), ctypes.byref(xcds)) == 0
+    props = torch.cuda.get_device_properties(0)
+    print(f"[shape] {props.name}: {cus.value} CUs, {xcds.value} XCDs", file=sys.stderr, flush=True)
+    assert cus.value == props.multi_processor_count
+    assert 1 <= xcds.value <= cus.value and cus.value % xcds.value == 0

@@ -178,6 +178,10 @@ def test_bf16_disjoint_small_far_mass():
         errs[dj] = (max_abs(o, oo), lse_rel_err(lse, ll))
     _say(f"[prefill] small far mass: three-pass max|do|={errs[False][0]:.3e} lse rel={errs[False][1]:.3e}; "
          f"disjoint max|do|={errs[True][0]:.3e} lse rel={errs[True][1]:.3e}")
+    # both merges meet the bf16 bar on this input: the three-pass form loses
+    # more (its far mass is a difference of window-dominated terms), but it
+    # stays inside the bar
+    assert errs[False][0] <= BF16_O_ATOL and errs[False][1] <= BF16_LSE_RTOL
     assert errs[True][0] <= BF16_O_ATOL and errs[True][1] <= BF16_LSE_RTOL
 
 
@@ -233,8 +237,10 @@ def _check_sampled(jl, torch, cfg, n_random, seqs_to_check=None, disjoint=False)
         idx = [s0 + r for r in rows]
         og = o[idx].float().cpu().numpy()
         lg = lse[:, idx].cpu().numpy()
-        worst_o = max(worst_o, max_abs(og, oo))
-        worst_l = max(worst_l, lse_rel_err(lg, ll))
+        e_o, e_l = max_abs(og, oo), lse_rel_err(lg, ll)
+        _say(f"[prefill]   seq {b}: L={L} G={G} rows={len(rows)} max|do|={e_o:.3e} lse rel={e_l:.3e}")
+        worst_o = max(worst_o, e_o)
+        worst_l = max(worst_l, e_l)
     _say(f"[prefill] {cfg.name}: max|do|={worst_o:.3e} lse rel={worst_l:.3e}")
     assert worst_o <= BF16_O_ATOL
     assert worst_l <= BF16_LSE_RTOL
@@ -273,13 +279,15 @@ def test_qwen3_1p7b_64k_g2():
 
 
 def test_qwen3_8b_128k_g4():
+    """The headline layer: the structural rows plus 64 seeded random rows,
+    all 32 heads."""
     jl, torch = gpu_or_skip()
-    _check_sampled(jl, torch, W.QWEN3_8B_128K, n_random=8)
+    _check_sampled(jl, torch, W.QWEN3_8B_128K, n_random=64)
 
 
 def test_qwen3_8b_128k_g4_disjoint():
     jl, torch = gpu_or_skip()
-    _check_sampled(jl, torch, W.QWEN3_8B_128K, n_random=8, disjoint=True)
+    _check_sampled(jl, torch, W.QWEN3_8B_128K, n_random=16, disjoint=True)
 
 
 def test_disjoint_rejects_fp32():
@@ -294,9 +302,9 @@ def test_qwen3_4b_varlen(w0):
     """The Qwen3-4B varlen layer at each window of the sweep."""
     jl, torch = gpu_or_skip()
     cfg = W.varlen_4b(w0)
-    # check the shortest and the longest sequence
-    lens = list(cfg.seqlens)
-    _check_sampled(jl, torch, cfg, n_random=4, seqs_to_check=[lens.index(min(lens)), lens.index(max(lens))])
+    # every packed sequence (seed 4: G = 4, 4, 4, 1, 3, 4, 2, 1), structural
+    # rows plus 2 seeded random rows each
+    _check_sampled(jl, torch, cfg, n_random=2)
 
 
 @pytest.mark.parametrize("disjoint", [False, True])
