@@ -3,8 +3,9 @@
 One step = one bifocal prefill of a Qwen3-8B-shaped attention layer (32 q / 8
 kv heads, head_dim 128, bf16, RoPE base 1e6, w_pretrained 32768, w0 4096) at
 L = 131072 (G = 4), followed by one single-batch decode step against a bf16
-base-RoPE KV cache of L = 131072 keys.  Four decode caches (2 GiB) are
-rotated so the 256 MB last-level cache cannot hold the one being read.
+base-RoPE KV cache of L = 131072 keys.  Decode rotates through 2 GiB of
+distinct cache rows, so the 256 MB last-level cache cannot hold the rows a
+step reads.
 
 Prints ONE JSON line:
   value     prefill throughput on the three-pass FLOP basis,
@@ -14,12 +15,18 @@ Prints ONE JSON line:
   roofline  the dominant kernel (the full-causal pass-2 launches): its
             algorithmic FLOPs 4 d Hq L(L+1)/2 over its own duration, taken
             from events the library records right around it, against the
-            MI355X dense bf16 MFMA peak; traffic comes from the committed
-            counter summary when it was measured on the current kernel source;
-  decode    sustained decode steps (KV bytes 2 L Hkv d 2 per step; both
-            kernels of a step, timed over back-to-back steps, since a HIP
-            event pair around one ~100 us kernel adds several us of its own)
-            against the HBM peak;
+            MI355X dense bf16 MFMA peak (and against the measured MFMA-only
+            ceiling); traffic comes from the committed counter summary when it
+            was measured on the current kernel source;
+  decode    sustained decode steps at 128K (KV bytes 2 L Hkv d 2 per step; both
+            kernels of a step, timed over back-to-back steps) against the HBM
+            peak; decode_lengths: the same at 16K, 32K, 32769, 64K, 65537 and
+            128K keys, bifocal and Delta-free (plain) side by side;
+  prefill_configs  the other prefill workloads: Qwen3-1.7B heads at 32K (G=1)
+            and 64K (G=2), and the Qwen3-4B varlen layer (8 sequences of
+            8K..128K) at w0 = 1024, 4096, 8192, each on both FLOP bases;
+  ceilings  what the chip achieves on its own: dense bf16 MFMA issue only, and
+            a streaming read (default and non-temporal cache policy);
   disjoint_merge  the same prefill with the far pairs computed directly (a
             window pass on the base grid plus a far-only pass on the remote
             grid, merged with two positive weights): exactly the causal pair
@@ -29,12 +36,16 @@ Prints ONE JSON line:
   overhead  the bifocal calls over plain attention at the same shapes (the same
             library with w_pretrained = L, i.e. G = 1: plain causal RoPE prefill
             and Delta-free decode);
-  cpu_baseline  the fp64 oracle on a sample of query rows of the same layer.
+  cpu_baseline  the fp64 oracle on the host cores: a sample of query rows of
+            the same layer (the value), the whole tiny fp32 config and whole
+            decode steps (median of 3), and the full layer extrapolated from
+            the sample (labelled as such).
 
     python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--no-cpu-baseline] [--headline-only]
+    python bench.py --mfma-peak | --read-peak | --copy-calibration
 
---headline-only skips the disjoint-merge, plain-attention, G-boundary and batched-decode runs, so
-that in a profiler run every dispatch of a kernel has the headline shape.
+--headline-only skips every run but the headline prefill and decode, so that in a profiler run every
+dispatch of a kernel has the headline shape.
 """
 
 from __future__ import annotations
@@ -44,6 +55,8 @@ import ctypes
 import hashlib
 import json
 import os
+import platform
+import statistics
 import sys
 import time
 
@@ -60,10 +73,16 @@ PASS2_TRAFFIC = (os.path.join(ROOT, "profiles", "prefill_pass2_traffic_qwen3_8b_
                  os.path.join(CSRC, "jl_prefill_mfma.hip"))
 DECODE_TRAFFIC = (os.path.join(ROOT, "profiles", "decode_split_traffic_qwen3_8b_L131072.txt"),
                   os.path.join(CSRC, "jl_decode.hip"))
+CACHE_POOL_ROWS = 131072      # rows of each of the 4 decode cache pools (4 x 2 x 256 MiB = 2 GiB)
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def window_pairs(L: int, w0: int) -> int:
+    """W(L, w0) = sum_{i<L} min(i+1, w0)."""
+    return w0 * L - w0 * (w0 - 1) // 2 if L >= w0 else L * (L + 1) // 2
 
 
 def far_flops(L: int, Hq: int, d: int, w0: int, first_rows: int = 128):
@@ -77,8 +96,16 @@ def far_flops(L: int, Hq: int, d: int, w0: int, first_rows: int = 128):
 def prefill_flops(L: int, Hq: int, d: int, w0: int):
     """(F_3pass, F_causal): FLOPs of the three passes and of causal attention."""
     P = L * (L + 1) // 2                                   # causal pairs
-    W = w0 * L - w0 * (w0 - 1) // 2 if L >= w0 else P      # window pairs, sum_i min(i+1, w0)
-    return 4 * d * Hq * (P + 2 * W), 4 * d * Hq * P
+    return 4 * d * Hq * (P + 2 * window_pairs(L, w0)), 4 * d * Hq * P
+
+
+def prefill_flops_varlen(lens, Hq: int, d: int, w0: int):
+    f3 = fc = 0
+    for L in lens:
+        a, b = prefill_flops(int(L), Hq, d, w0)
+        f3 += a
+        fc += b
+    return f3, fc
 
 
 class HipEvents:
@@ -134,18 +161,37 @@ def read_traffic(which):
         return None
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def blas_threads() -> int:
+    try:
+        import threadpoolctl
+        return sum(p.get("num_threads", 0) for p in threadpoolctl.threadpool_info()) or os.cpu_count()
+    except Exception:
+        return os.cpu_count()
+
+
 def cpu_baseline(cfg, n_rows: int, seed: int = 1234):
-    """fp64 oracle on n_rows random query rows (all heads) of the prefill layer;
-    throughput on the same F_3pass-per-row basis as the GPU value."""
+    """The fp64 oracle on the host cores.
+
+    value: n_rows random query rows (all heads) of the prefill layer, on the
+    same F_3pass-per-row basis as the GPU value; beside it the whole tiny fp32
+    config and whole decode steps (median of 3 each), and the full layer's
+    time extrapolated from the sampled rate."""
     import torch
     import oracle
     import workloads as W
-    try:
-        import threadpoolctl
-        threads = sum(p.get("num_threads", 0) for p in threadpoolctl.threadpool_info()) or os.cpu_count()
-    except Exception:
-        threads = os.cpu_count()
+    threads = blas_threads()
     L = cfg.seqlens[0]
+    d, Hq = cfg.head_dim, cfg.num_q_heads
     q, k, v = W.make_prefill_inputs(cfg)
     g = torch.Generator("cpu").manual_seed(seed)
     rows = sorted(set(torch.randint(L // 2, L, (n_rows,), generator=g).tolist()))
@@ -153,16 +199,99 @@ def cpu_baseline(cfg, n_rows: int, seed: int = 1234):
     qn[rows] = q[torch.tensor(rows)].double().numpy()
     kn = k.double().numpy()
     vn = v.double().numpy()
+    del q, k, v
     t0 = time.perf_counter()
-    oracle.prefill(qn, kn, vn, w0=cfg.w0, w_pretrained=cfg.w_pretrained, rope_base=cfg.rope_base,
-                   rows=rows)
+    oracle.prefill(qn, kn, vn, w0=cfg.w0, w_pretrained=cfg.w_pretrained, rope_base=cfg.rope_base, rows=rows)
     dt = time.perf_counter() - t0
-    d, Hq = cfg.head_dim, cfg.num_q_heads
+    del qn, kn, vn
     flops = sum(4 * d * Hq * ((i + 1) + 2 * min(i + 1, cfg.w0)) for i in rows)
-    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
+    rate = flops / dt
+    F3, _ = prefill_flops(L, Hq, d, cfg.w0)
+
+    # the tiny fp32 config, whole (every row), median of 3
+    tq, tk, tv = (t.double().numpy() for t in W.make_prefill_inputs(W.TINY))
+    tiny_s = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.prefill(tq, tk, tv, w0=W.TINY.w0, w_pretrained=W.TINY.w_pretrained, rope_base=W.TINY.rope_base)
+        tiny_s.append(time.perf_counter() - t0)
+    tiny_F3, _ = prefill_flops(W.TINY.seqlens[0], W.TINY.num_q_heads, W.TINY.head_dim, W.TINY.w0)
+
+    # whole decode steps (one query row against every cached key), median of 3
+    dec = {}
+    for Ld in (16384, 131072):
+        dcfg = W.decode_8b(Ld)
+        dq, dk, dv = W.make_decode_inputs(dcfg)
+        dq, dk, dv = dq.double().numpy(), dk.double().numpy(), dv.double().numpy()
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.decode(dq, dk, dv, Ld, w0=dcfg.w0, w_pretrained=dcfg.w_pretrained, rope_base=dcfg.rope_base)
+            ts.append(time.perf_counter() - t0)
+        s = statistics.median(ts)
+        dec[str(Ld)] = {"s_per_step": round(s, 4), "kv_GB/s": round(2 * Ld * 8 * 128 * 2 / s / 1e9, 3)}
+        del dq, dk, dv
+    return {"value": round(rate / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
+            "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count(),
             "sample": f"{len(rows)} random query rows in [L/2, L) x {Hq} heads of the L={L} layer "
-                      f"(keys rotated up to the last sampled row), {dt:.1f} s, F_3pass-per-row basis"}
+                      f"(keys rotated up to the last sampled row), {dt:.1f} s, F_3pass-per-row basis",
+            "sample_rows_x_heads_per_s": round(len(rows) * Hq / dt, 2),
+            "full_layer_s_extrapolated": round(F3 / rate, 1),
+            "tiny_fp32_config_full": {"s_median_of_3": round(statistics.median(tiny_s), 5),
+                                      "tflops_3pass": round(tiny_F3 / statistics.median(tiny_s) / 1e12, 6)},
+            "decode_full_median_of_3": dec}
+
+
+def measure_ceilings(jl, torch, dev, ev, stream):
+    """MFMA-only issue rate and streaming-read bandwidth on this GPU."""
+    lib = jl.lib()
+    sink = torch.zeros(4, dtype=torch.float32, device=dev)
+    flops = ctypes.c_int64()
+    out = {}
+    iters = 20000
+    for _ in range(2):   # warm: the clock ramps on the first launch
+        jl._check(lib.jl_bench_mfma_peak(iters, ctypes.c_void_p(sink.data_ptr()), ctypes.byref(flops),
+                                         ctypes.c_void_p(stream)))
+    a, b = ev.create(), ev.create()
+    ev.record(a, stream)
+    jl._check(lib.jl_bench_mfma_peak(iters, ctypes.c_void_p(sink.data_ptr()), ctypes.byref(flops),
+                                     ctypes.c_void_p(stream)))
+    ev.record(b, stream)
+    ms = ev.elapsed_ms(a, b)
+    out["mfma_bf16_tflops"] = round(flops.value / (ms * 1e-3) / 1e12, 1)
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    for nt, key in ((0, "read_GB/s"), (1, "read_nt_GB/s")):
+        for _ in range(2):
+            jl._check(lib.jl_bench_read_peak(ctypes.c_void_p(buf.data_ptr()), nbytes, nt,
+                                             ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream)))
+        ts = []
+        for _ in range(5):
+            ev.record(a, stream)
+            jl._check(lib.jl_bench_read_peak(ctypes.c_void_p(buf.data_ptr()), nbytes, nt,
+                                             ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream)))
+            ev.record(b, stream)
+            ts.append(ev.elapsed_ms(a, b))
+        out[key] = round(nbytes / (statistics.median(ts) * 1e-3) / 1e9, 1)
+    del buf
+    torch.cuda.synchronize()
+    out["method"] = ("mfma: one 8-wave workgroup per CU, four independent v_mfma_f32_32x32x16_bf16 chains per "
+                     f"wave, {iters} x 32 MFMAs per wave; read: 4 GiB streamed with 16-byte loads, median of 5")
+    return out
+
+
+def time_calls(ev, stream, fn, n, warm=2):
+    """Mean ms per call of fn() over n back-to-back calls (events around the batch)."""
+    for _ in range(warm):
+        fn()
+    a, b = ev.create(), ev.create()
+    ev.record(a, stream)
+    for _ in range(n):
+        fn()
+    ev.record(b, stream)
+    return ev.elapsed_ms(a, b) / n
 
 
 def main():
@@ -174,11 +303,18 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=420)
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--headline-only", action="store_true",
-                    help="skip the disjoint-merge, plain-attention and G-boundary runs (profiling runs: every "
-                         "dispatch of a kernel then has the headline shape)")
+                    help="run the headline prefill and decode only (profiling runs: every dispatch of a kernel "
+                         "then has the headline shape)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer three times (counter calibration run)")
+    ap.add_argument("--mfma-peak", action="store_true", help="only measure the MFMA-only ceiling")
+    ap.add_argument("--read-peak", action="store_true", help="only measure the streaming-read ceiling")
     args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the path shards by "
+              f"kv head or by sequence with no exchange, so the one-GPU figure is the per-GPU figure.",
+              file=sys.stderr)
+        sys.exit(2)
     if args.copy_calibration:
         import torch
         src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
@@ -188,11 +324,6 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": src.numel(), "copies": 3}), flush=True)
         return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the path shards by "
-              f"kv head or by sequence with no exchange, so the one-GPU figure is the per-GPU figure.",
-              file=sys.stderr)
-        sys.exit(2)
 
     import torch
     import rope_context_extension_amd as jl
@@ -200,6 +331,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    ev = HipEvents()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    lib = jl.lib()
+    if args.mfma_peak or args.read_peak:
+        c = measure_ceilings(jl, torch, dev, ev, stream)
+        c["device"] = torch.cuda.get_device_properties(dev).name
+        print(json.dumps(c), flush=True)
+        return
+
     cfg = W.QWEN3_8B_128K
     L, Hq, Hkv, d = cfg.seqlens[0], cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
     F3, Fc = prefill_flops(L, Hq, d, cfg.w0)
@@ -210,37 +350,42 @@ def main():
     ws = torch.empty(jl.prefill_workspace_bytes(L, Hq, Hkv, d, jl.BF16, w_pretrained=cfg.w_pretrained),
                      dtype=torch.uint8, device=dev)
 
+    # decode cache pools: 4 x (K, V) of 131072 rows, 2 GiB in all; a step of L keys reads one
+    # L-row window of one pool, and consecutive steps take distinct windows
     dcfg = W.decode_8b(L)
-    n_caches = 4
     gen = torch.Generator(device=dev).manual_seed(dcfg.seed)
-    caches = []
-    for _ in range(n_caches):
-        kc = torch.randn((L, Hkv, d), generator=gen, device=dev).bfloat16()
-        vc = torch.randn((L, Hkv, d), generator=gen, device=dev).bfloat16()
-        caches.append((kc, vc))
+    pools = []
+    for _ in range(4):
+        kc = torch.randn((CACHE_POOL_ROWS, Hkv, d), generator=gen, device=dev).bfloat16()
+        vc = torch.randn((CACHE_POOL_ROWS, Hkv, d), generator=gen, device=dev).bfloat16()
+        pools.append((kc, vc))
     qd = torch.randn((Hq, d), generator=gen, device=dev).bfloat16()
     od = torch.empty_like(qd)
     lsed = torch.empty((Hq,), dtype=torch.float32, device=dev)
-    wsd = torch.empty(max(16, jl.decode_workspace_bytes(L, Hq, Hkv)), dtype=torch.uint8, device=dev)
-    kv_bytes = 2 * L * Hkv * d * 2
+    wsd = torch.empty(max(16, jl.decode_workspace_bytes(CACHE_POOL_ROWS, Hq, Hkv)), dtype=torch.uint8, device=dev)
 
-    ev = HipEvents()
-    stream = torch.cuda.current_stream(dev).cuda_stream
-    lib = jl.lib()
+    def decode_steps(Lx: int, wpt: int):
+        """Prepared decode calls of Lx keys over distinct cache windows (2 GiB in all)."""
+        calls = []
+        per_pool = CACHE_POOL_ROWS // Lx
+        for kc, vc in pools:
+            for w in range(per_pool):
+                calls.append(jl.decode(qd, kc[w * Lx:(w + 1) * Lx], vc[w * Lx:(w + 1) * Lx], Lx, w0=dcfg.w0,
+                                       w_pretrained=wpt, rope_base=dcfg.rope_base, out=od, lse=lsed,
+                                       workspace=wsd, prepare=True))
+        return calls
+
+    head_calls = decode_steps(L, dcfg.w_pretrained)
+    kv_bytes = 2 * L * Hkv * d * 2
 
     def prefill():
         jl.prefill(q, k, v, w0=cfg.w0, w_pretrained=cfg.w_pretrained, rope_base=cfg.rope_base, out=o,
                    lse=lse, workspace=ws)
 
-    def decode(i):
-        kc, vc = caches[i % n_caches]
-        jl.decode(qd, kc, vc, L, w0=dcfg.w0, w_pretrained=dcfg.w_pretrained, rope_base=dcfg.rope_base,
-                  out=od, lse=lsed, workspace=wsd)
-
     log(f"[bench] warmup {args.warmup}")
     for i in range(args.warmup):
         prefill()
-        decode(i)
+        head_calls[i % len(head_calls)]()
     torch.cuda.synchronize()
 
     # per step: [call start, attention start, after pass 2, attention end, call end] for
@@ -257,7 +402,7 @@ def main():
         lib.jl_set_profile_events(None, None, None)
         ev.record(r[4], stream)
         lib.jl_set_profile_events(r[5], r[6], r[7])
-        decode(i)
+        head_calls[i % len(head_calls)]()
         lib.jl_set_profile_events(None, None, None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -267,20 +412,35 @@ def main():
     attn_ms = float(np.mean([ev.elapsed_ms(r[1], r[3]) for r in recs]))
     dec_in_step_us = float(np.mean([ev.elapsed_ms(r[5], r[7]) for r in recs])) * 1e3
 
-    # sustained decode: back-to-back steps over the rotated caches
-    e0, e1 = ev.create(), ev.create()
-    torch.cuda.synchronize()
-    ev.record(e0, stream)
-    for i in range(args.decode_steps):
-        decode(i)
-    ev.record(e1, stream)
-    dec_us = ev.elapsed_ms(e0, e1) * 1e3 / args.decode_steps
+    # sustained decode: back-to-back steps over the rotated cache windows
+    dec_us = 1e3 * time_calls(ev, stream, lambda it=iter(range(10**9)): head_calls[next(it) % len(head_calls)](),
+                              args.decode_steps, warm=4)
     torch.cuda.synchronize()
 
+    def run_decode_lengths():
+        """Decode steps at the decode config's lengths, bifocal and plain (w_pretrained = L: G = 1)."""
+        outd = {}
+        for Lx in W.DECODE_LENGTHS:
+            row = {}
+            for key, wpt in (("bifocal", dcfg.w_pretrained), ("plain", Lx)):
+                calls = decode_steps(Lx, wpt)
+                n = max(100, len(calls) * 4)
+                us = 1e3 * time_calls(ev, stream, lambda it=iter(range(10**9)): calls[next(it) % len(calls)](), n,
+                                      warm=len(calls))
+                b = 2 * Lx * Hkv * d * 2
+                row[key] = {"us_per_step": round(us, 2), "GB/s": round(b / (us * 1e-6) / 1e9, 1),
+                            "frac_hbm": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+            row["G"] = jl.group_size(Lx, dcfg.w_pretrained)
+            row["kv_bytes"] = 2 * Lx * Hkv * d * 2
+            row["bifocal_over_plain"] = round(row["bifocal"]["us_per_step"] / row["plain"]["us_per_step"], 4)
+            outd[str(Lx)] = row
+            log(f"[bench] decode L={Lx}: {row['bifocal']['us_per_step']} us ({row['bifocal']['frac_hbm']:.3f} of "
+                f"peak), plain {row['plain']['us_per_step']} us")
+        torch.cuda.synchronize()
+        return outd
+
     def run_extras():
-        """The disjoint-merge variant, plain attention at the same shapes and decode steps on both
-        sides of the G boundaries, on the inputs above."""
-        # the disjoint merge variant on the same inputs (own output buffers)
+        """The disjoint-merge variant and plain attention at the same shapes, on the inputs above."""
         od_ = torch.empty_like(o)
         lsed_ = torch.empty_like(lse)
 
@@ -304,54 +464,17 @@ def main():
         dj_do = float((od_.float() - o.float()).abs().max().item())
         del od_, lsed_
 
-        # overhead against plain attention at the same shapes: G = 1 (w_pretrained = L) makes every
-        # aliased position the absolute one, so the same library runs plain causal RoPE attention
-        # (prefill: one full-causal pass) and Delta-free decode (every key on the base path)
+        # plain attention at the same shapes: G = 1 (w_pretrained = L) makes every aliased position the
+        # absolute one, so the same library runs plain causal RoPE attention (one full-causal pass)
         def prefill_plain():
             jl.prefill(q, k, v, w0=cfg.w0, w_pretrained=L, rope_base=cfg.rope_base, out=o, lse=lse,
                        workspace=ws)
 
-        def decode_plain(i):
-            kc, vc = caches[i % n_caches]
-            jl.decode(qd, kc, vc, L, w0=dcfg.w0, w_pretrained=L, rope_base=dcfg.rope_base, out=od, lse=lsed,
-                      workspace=wsd)
-
-        prefill_plain()
-        torch.cuda.synchronize()
-        pe = [(ev.create(), ev.create()) for _ in range(3)]
-        for a_, b_ in pe:
-            ev.record(a_, stream)
-            prefill_plain()
-            ev.record(b_, stream)
-        plain_ms = float(np.mean([ev.elapsed_ms(a_, b_) for a_, b_ in pe]))
-        for i in range(8):
-            decode_plain(i)
-        torch.cuda.synchronize()
-        ev.record(e0, stream)
-        for i in range(args.decode_steps):
-            decode_plain(i)
-        ev.record(e1, stream)
-        dec_plain_us = ev.elapsed_ms(e0, e1) * 1e3 / args.decode_steps
-        torch.cuda.synchronize()
-
-        # decode step time on both sides of the G boundaries (the cache is the same; only L moves),
-        # bifocal and plain (w_pretrained = L: G = 1) at each length
-        def decode_at(Lx, i, wpt):
-            kc, vc = caches[i % n_caches]
-            jl.decode(qd, kc, vc, Lx, w0=dcfg.w0, w_pretrained=wpt, rope_base=dcfg.rope_base,
-                      out=od, lse=lsed, workspace=wsd)
-
-        boundary, boundary_plain = {}, {}
-        for Lx in (32768, 32769, 65536, 65537):
-            for key, wpt in ((boundary, dcfg.w_pretrained), (boundary_plain, Lx)):
-                for i in range(4):
-                    decode_at(Lx, i, wpt)
-                torch.cuda.synchronize()
-                ev.record(e0, stream)
-                for i in range(100):
-                    decode_at(Lx, i, wpt)
-                ev.record(e1, stream)
-                key[str(Lx)] = round(ev.elapsed_ms(e0, e1) * 1e3 / 100, 2)
+        plain_ms = time_calls(ev, stream, prefill_plain, 3, warm=1)
+        plain_calls = decode_steps(L, L)
+        dec_plain_us = 1e3 * time_calls(ev, stream,
+                                        lambda it=iter(range(10**9)): plain_calls[next(it) % len(plain_calls)](),
+                                        args.decode_steps, warm=8)
         torch.cuda.synchronize()
         dj = {"call_ms": round(dj_ms, 3), "tflops_actual": round(Fc / (dj_ms * 1e-3) / 1e12, 2),
               "frac_actual": round(Fc / (dj_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -363,9 +486,7 @@ def main():
         ov = {"prefill_plain_causal_ms": round(plain_ms, 3),
               "prefill_bifocal_over_plain": round(call_ms / plain_ms, 4),
               "decode_plain_us_per_step": round(dec_plain_us, 2),
-              "decode_bifocal_over_plain": round(dec_us / dec_plain_us, 4),
-              "decode_us_per_step_across_g_boundaries": boundary,
-              "decode_plain_us_per_step_at_those_lengths": boundary_plain}
+              "decode_bifocal_over_plain": round(dec_us / dec_plain_us, 4)}
         log(f"[bench] plain causal prefill {plain_ms:.2f} ms, Delta-free decode {dec_plain_us:.1f} us; "
             f"disjoint merge {dj_ms:.2f} ms (far pass {dj_far_ms:.2f} ms)")
         return dj, ov
@@ -377,29 +498,60 @@ def main():
         qb, kb_, vb, row0 = W.make_decode_batch_inputs(Hq, Hkv, d, lens, seed=dcfg.seed, device="cuda")
         ob = torch.empty_like(qb)
         lb = torch.empty((len(lens), Hq), dtype=torch.float32, device=dev)
-        wsb = torch.empty(max(16, jl.decode_batch_workspace_bytes(lens, Hq, Hkv)), dtype=torch.uint8, device=dev)
-
-        def step():
-            jl.decode_batch(qb, kb_, vb, lens, row0=row0, w0=dcfg.w0, w_pretrained=dcfg.w_pretrained,
-                            rope_base=dcfg.rope_base, out=ob, lse=lb, workspace=wsb)
-
-        for _ in range(4):
-            step()
-        torch.cuda.synchronize()
-        n = 50
-        ev.record(e0, stream)
-        for _ in range(n):
-            step()
-        ev.record(e1, stream)
-        us = ev.elapsed_ms(e0, e1) * 1e3 / n
+        step = jl.decode_batch(qb, kb_, vb, lens, row0=row0, w0=dcfg.w0, w_pretrained=dcfg.w_pretrained,
+                               rope_base=dcfg.rope_base, out=ob, lse=lb, prepare=True)
+        us = 1e3 * time_calls(ev, stream, step, 50, warm=4)
         torch.cuda.synchronize()
         kvb = 2 * sum(lens) * Hkv * d * 2
         log(f"[bench] batched decode of {len(lens)} sequences: {us:.1f} us per step ({kvb / us / 1e3:.0f} GB/s)")
         return {"lens": lens, "us_per_step": round(us, 2), "kv_bytes": kvb,
                 "GB/s": round(kvb / (us * 1e-6) / 1e9, 1), "frac_hbm": round(kvb / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
 
+    def run_prefill_configs():
+        """Prefill throughput of the other prefill workloads (inputs drawn on the GPU: the timing does
+        not depend on the values)."""
+        res = {}
+        cases = [(W.QWEN3_1P7B_32K, None), (W.QWEN3_1P7B_64K, None)] + \
+                [(W.varlen_4b(w), w) for w in (1024, 4096, 8192)]
+        for c, _ in cases:
+            T = c.total_tokens
+            g2 = torch.Generator(device=dev).manual_seed(c.seed)
+            qx = torch.randn((T, c.num_q_heads, c.head_dim), generator=g2, device=dev).bfloat16()
+            kx = torch.randn((T, c.num_kv_heads, c.head_dim), generator=g2, device=dev).bfloat16()
+            vx = torch.randn((T, c.num_kv_heads, c.head_dim), generator=g2, device=dev).bfloat16()
+            cu = W.cu_seqlens_of(c.seqlens) if len(c.seqlens) > 1 else None
+            ox = torch.empty_like(qx)
+            lx = torch.empty((c.num_q_heads, T), dtype=torch.float32, device=dev)
+            wsx = torch.empty(jl.prefill_workspace_bytes(T, c.num_q_heads, c.num_kv_heads, c.head_dim, jl.BF16,
+                                                         w_pretrained=c.w_pretrained, cu_seqlens=cu),
+                              dtype=torch.uint8, device=dev)
+
+            def call():
+                jl.prefill(qx, kx, vx, w0=c.w0, w_pretrained=c.w_pretrained, rope_base=c.rope_base, cu_seqlens=cu,
+                           out=ox, lse=lx, workspace=wsx)
+
+            ms = time_calls(ev, stream, call, 3, warm=1)
+            f3, fc = prefill_flops_varlen(c.seqlens, c.num_q_heads, c.head_dim, c.w0)
+            gs = [jl.group_size(n, c.w_pretrained) for n in c.seqlens]
+            res[c.name] = {"call_ms": round(ms, 3), "tflops_3pass": round(f3 / (ms * 1e-3) / 1e12, 2),
+                           "frac_3pass": round(f3 / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                           "tflops_causal_basis": round(fc / (ms * 1e-3) / 1e12, 2),
+                           "frac_causal": round(fc / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                           "flops_3pass": f3, "flops_causal": fc, "w0": c.w0, "G": gs,
+                           "seqlens": list(c.seqlens)}
+            log(f"[bench] prefill {c.name}: {ms:.2f} ms, {res[c.name]['tflops_3pass']} TFLOP/s (F_3pass), "
+                f"{res[c.name]['tflops_causal_basis']} (causal)")
+            del qx, kx, vx, ox, lx, wsx
+            torch.cuda.empty_cache()
+        return res
+
+    dl_obj = None if args.headline_only else run_decode_lengths()
     dj_obj, ov_obj = (None, None) if args.headline_only else run_extras()
     db_obj = None if args.headline_only else run_decode_batch()
+    del q, k, v, o, ws, pools, head_calls
+    torch.cuda.empty_cache()
+    pc_obj = None if args.headline_only else run_prefill_configs()
+    ceil = None if args.headline_only else measure_ceilings(jl, torch, dev, ev, stream)
 
     tflops = F3 / (call_ms * 1e-3) / 1e12
     pass2_tflops = Fc / (pass2_ms * 1e-3) / 1e12
@@ -408,6 +560,20 @@ def main():
         f"{attn_ms:.2f} ms; pass 2 {pass2_ms:.2f} ms -> {pass2_tflops:.1f} TFLOP/s; decode {dec_us:.1f} "
         f"us/step ({dec_gbs:.0f} GB/s)")
 
+    roof = {"bound": "mfma", "achieved": round(pass2_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(pass2_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": read_traffic(PASS2_TRAFFIC),
+            "kernel": "prefill_pp_kernel<0> + prefill_pass_kernel<0, true> (pass 2: remote "
+                      "q/k, full causal; the second kernel takes the first 128 rows)",
+            "flops_per_launch": Fc, "ms_per_launch": round(pass2_ms, 3)}
+    dec_roof = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                "traffic": read_traffic(DECODE_TRAFFIC),
+                "kernel": "decode_split_kernel + decode_reduce_kernel (one step, timed "
+                          "over back-to-back steps)", "us_per_launch": round(dec_us, 2)}
+    if ceil:
+        roof["frac_of_measured_mfma_ceiling"] = round(pass2_tflops / ceil["mfma_bf16_tflops"], 4)
+        dec_roof["frac_of_measured_nt_read_ceiling"] = round(dec_gbs / ceil["read_nt_GB/s"], 4)
     out = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -425,33 +591,28 @@ def main():
                                "+ one decode step at L=131072",
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "L": L, "w0": cfg.w0,
                    "w_pretrained": cfg.w_pretrained, "rope_base": cfg.rope_base, "batch": 1},
-        "roofline": {"bound": "mfma", "achieved": round(pass2_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(pass2_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": read_traffic(PASS2_TRAFFIC),
-                     "kernel": "prefill_pp_kernel<0> + prefill_pass_kernel<0, true> (pass 2: remote "
-                               "q/k, full causal; the second kernel takes the first 128 rows)",
-                     "flops_per_launch": Fc, "ms_per_launch": round(pass2_ms, 3)},
+        "roofline": roof,
         "prefill": {"call_ms": round(call_ms, 3), "attention_ms": round(attn_ms, 3),
                     "pass2_ms": round(pass2_ms, 3), "tflops_3pass": round(tflops, 2),
+                    "frac_3pass": round(tflops / PEAK_BF16_TFLOPS, 4),
                     "tflops_causal_basis": round(Fc / (call_ms * 1e-3) / 1e12, 2),
+                    "frac_causal": round(Fc / (call_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                     "flops_3pass": F3, "flops_causal": Fc},
         "decode": {"us_per_step": round(dec_us, 2), "us_in_step": round(dec_in_step_us, 2),
-                   "kv_bytes": kv_bytes, "GB/s": round(dec_gbs, 1),
-                   "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
-                                "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
-                                "traffic": read_traffic(DECODE_TRAFFIC),
-                                "kernel": "decode_split_kernel + decode_reduce_kernel (one step, timed "
-                                          "over back-to-back steps)", "us_per_launch": round(dec_us, 2)},
-                   "step_frac_hbm": round(dec_gbs / PEAK_HBM_GBS, 4)},
+                   "kv_bytes": kv_bytes, "GB/s": round(dec_gbs, 1), "roofline": dec_roof,
+                   "step_frac_hbm": round(dec_gbs / PEAK_HBM_GBS, 4),
+                   "caches": "4 pools of 131072 rows (2 GiB of K and V); each step reads its own window"},
+        "decode_lengths": dl_obj,
+        "prefill_configs": pc_obj,
+        "ceilings": ceil,
         "disjoint_merge": dj_obj,
         "overhead": ov_obj,
         "decode_batch": db_obj,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        del q, k, v, o, ws, caches
         torch.cuda.empty_cache()
-        log(f"[bench] cpu baseline ({args.cpu_rows} rows)")
+        log(f"[bench] cpu baseline ({args.cpu_rows} rows, tiny config, decode steps)")
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_rows)
     print(json.dumps(out), flush=True)
 

@@ -164,6 +164,8 @@ int jl_bifocal_prefill_disjoint(const void* q, const void* k, const void* v, voi
  *   The split of the keys over workgroups (and so the workspace size) follows
  *   the compute-unit count of the current device, which must be the device
  *   of hip_stream: query the size and call with the same device current.
+ *   The workspace size never decreases as L grows, so a workspace sized for
+ *   the longest step of a generation loop serves every shorter step.
  */
 int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_cache, int64_t L,
                       void* o, float* lse, int32_t num_q_heads, int32_t num_kv_heads,
@@ -191,8 +193,8 @@ int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_cache, i
  *   lse        [num_seqs, num_q_heads] fp32, or NULL
  *   Sequences with lens[b] == 0 are skipped: their o rows and lse entries
  *   are not written.  Workspace: two-call protocol as in jl_bifocal_decode;
- *   its size depends on lens.  The other arguments and errors are those of
- *   jl_bifocal_decode.
+ *   its size depends on lens and never decreases as any lens[b] grows.  The
+ *   other arguments and errors are those of jl_bifocal_decode.
  */
 int jl_bifocal_decode_batch(const void* q, const void* k_cache, const void* v_cache, int64_t cache_rows,
                             const int64_t* row0, const int64_t* lens, int32_t num_seqs, void* o,

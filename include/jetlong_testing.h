@@ -62,6 +62,19 @@ int jl_test_device_shape(int32_t* cus, int32_t* xcds);
    a length outside 0 .. 2^31 - 1. */
 int jl_test_decode_plan(const int64_t* lens, int32_t num_seqs, int32_t cus, int32_t* nsub, int32_t* nwg);
 
+/* Ceiling kernels for benchmarks: what the chip achieves on its own, the
+   denominators beside the published peaks.
+   jl_bench_mfma_peak: one workgroup of 8 waves per compute unit, each wave
+   issuing iters x 32 dense v_mfma_f32_32x32x16_bf16 in four independent
+   accumulator chains and nothing else; *flops receives the FLOPs of the
+   launch.  jl_bench_read_peak: a streaming read of `bytes` (a multiple of 16,
+   16-byte aligned device memory) with 16-byte loads, default or
+   non-temporal cache policy.  sink: one device float, written only under a
+   condition the kernels never meet.  Asynchronous on hip_stream; the caller
+   times them.  JL_EINVAL on bad arguments. */
+int jl_bench_mfma_peak(int64_t iters, float* sink, int64_t* flops, void* hip_stream);
+int jl_bench_read_peak(const void* buf, int64_t bytes, int32_t nontemporal, float* sink, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

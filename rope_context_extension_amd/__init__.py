@@ -18,7 +18,7 @@ import os
 from typing import Optional, Sequence
 
 __all__ = ["group_size", "prefill", "prefill_workspace_bytes", "decode", "decode_workspace_bytes",
-           "decode_batch", "decode_batch_workspace_bytes", "rope_rows",
+           "decode_batch", "decode_batch_workspace_bytes", "rope_rows", "PreparedCall",
            "lib", "JetLongError", "LIB_PATH", "BF16", "FP32"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjetlong.so")
@@ -86,6 +86,10 @@ def lib() -> ctypes.CDLL:
         L.jl_set_profile_events.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p]
         L.jl_test_device_shape.restype = c.c_int
         L.jl_test_device_shape.argtypes = [c.POINTER(c.c_int32), c.POINTER(c.c_int32)]
+        L.jl_bench_mfma_peak.restype = c.c_int
+        L.jl_bench_mfma_peak.argtypes = [c.c_int64, c.c_void_p, c.POINTER(c.c_int64), c.c_void_p]
+        L.jl_bench_read_peak.restype = c.c_int
+        L.jl_bench_read_peak.argtypes = [c.c_void_p, c.c_int64, c.c_int32, c.c_void_p, c.c_void_p]
         L.jl_test_decode_plan.restype = c.c_int
         L.jl_test_decode_plan.argtypes = [c.POINTER(c.c_int64), c.c_int32, c.c_int32, c.POINTER(c.c_int32),
                                           c.POINTER(c.c_int32)]
@@ -167,6 +171,25 @@ def _workspace(workspace, need: int, device):
     _check_devices(device, workspace=workspace)
     _need(workspace.numel() >= need, f"workspace has {workspace.numel()} bytes, {need} needed")
     return workspace
+
+
+class PreparedCall:
+    """One library call whose arguments were checked and marshalled once.
+
+    Calling the object repeats that call on the same tensors (whose contents
+    may change between calls) and the same stream, and returns the outputs.
+    It is for launch-bound loops such as decode steps, where the per-call
+    argument checks would take longer on the host than the step takes on the
+    GPU.  The object keeps every tensor and host array of the call alive."""
+
+    def __init__(self, fn, args, outputs, keep):
+        self._fn, self._args, self.outputs, self._keep = fn, args, outputs, keep
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc != 0:
+            _check(rc)
+        return self.outputs
 
 
 def _dtype_code(t) -> int:
@@ -253,10 +276,11 @@ def decode_workspace_bytes(L: int, num_q_heads: int, num_kv_heads: int, head_dim
 
 def decode(q, k_cache, v_cache, L: int, *, w0: int, w_pretrained: int, rope_base: float,
            scale: Optional[float] = None, q_to_kv=None, out=None, lse=None, return_lse=True,
-           workspace=None):
+           workspace=None, prepare: bool = False):
     """One generation step.  q [Hq, d] bf16 (base-rotated at L - 1); caches
     [L_cap, Hkv, d] bf16 holding base-rotated keys.  Returns (o [Hq, d], lse
-    [Hq] or None)."""
+    [Hq] or None).  prepare=True launches nothing and returns a PreparedCall
+    that runs this step (on the current stream) each time it is called."""
     import torch
     _need(isinstance(q, torch.Tensor) and q.dim() == 2, "q must be a [Hq, d] tensor")
     _need(isinstance(k_cache, torch.Tensor) and k_cache.dim() == 3, "k_cache must be a [L_cap, Hkv, d] tensor")
@@ -287,12 +311,14 @@ def decode(q, k_cache, v_cache, L: int, *, w0: int, w_pretrained: int, rope_base
         if return_lse and lse is None:
             lse = torch.empty((Hq,), dtype=torch.float32, device=q.device)
         n = ctypes.c_size_t(workspace.numel())
-        _check(lib().jl_bifocal_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), int(L), _ptr(o),
-                                       _ptr(lse) if return_lse else None, Hq, Hkv, kvmap, d, dt,
-                                       int(w0), int(w_pretrained), float(rope_base),
-                                       0.0 if scale is None else float(scale), _ptr(workspace),
-                                       ctypes.byref(n), _stream(q.device)))
-    return o, (lse if return_lse else None)
+        args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), int(L), _ptr(o), _ptr(lse) if return_lse else None,
+                Hq, Hkv, kvmap, d, dt, int(w0), int(w_pretrained), float(rope_base),
+                0.0 if scale is None else float(scale), _ptr(workspace), ctypes.byref(n), _stream(q.device))
+        outputs = (o, lse if return_lse else None)
+        call = PreparedCall(lib().jl_bifocal_decode, args, outputs, (q, k_cache, v_cache, workspace, kvmap, n))
+        if prepare:
+            return call
+        return call()
 
 
 def _packed_rows(lens):
@@ -317,13 +343,13 @@ def decode_batch_workspace_bytes(lens, num_q_heads: int, num_kv_heads: int, head
 
 def decode_batch(q, k_cache, v_cache, lens, *, w0: int, w_pretrained: int, rope_base: float, row0=None,
                  scale: Optional[float] = None, q_to_kv=None, out=None, lse=None, return_lse=True,
-                 workspace=None):
+                 workspace=None, prepare: bool = False):
     """One generation step for each of B ragged sequences.  q [B, Hq, d] bf16
     (q[b] base-rotated at lens[b] - 1); caches [R, Hkv, d] bf16 holding
     base-rotated keys, sequence b's keys at rows row0[b] .. row0[b] + lens[b] - 1
     (default: packed one after the other).  Returns (o [B, Hq, d], lse [B, Hq]
     or None); sequences with lens[b] == 0 leave their rows of o and lse
-    unwritten."""
+    unwritten.  prepare=True returns a PreparedCall instead of launching."""
     import torch
     _need(isinstance(q, torch.Tensor) and q.dim() == 3, "q must be a [B, Hq, d] tensor")
     _need(isinstance(k_cache, torch.Tensor) and k_cache.dim() == 3, "k_cache must be a [R, Hkv, d] tensor")
@@ -358,11 +384,15 @@ def decode_batch(q, k_cache, v_cache, lens, *, w0: int, w_pretrained: int, rope_
         if return_lse and lse is None:
             lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
         n = ctypes.c_size_t(workspace.numel())
-        _check(lib().jl_bifocal_decode_batch(_ptr(q), _ptr(k_cache), _ptr(v_cache), R, r0, ln, B, _ptr(o),
-                                             _ptr(lse) if return_lse else None, Hq, Hkv, kvmap, d, dt, int(w0),
-                                             int(w_pretrained), float(rope_base), 0.0 if scale is None else float(scale),
-                                             _ptr(workspace), ctypes.byref(n), _stream(q.device)))
-    return o, (lse if return_lse else None)
+        args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), R, r0, ln, B, _ptr(o), _ptr(lse) if return_lse else None,
+                Hq, Hkv, kvmap, d, dt, int(w0), int(w_pretrained), float(rope_base),
+                0.0 if scale is None else float(scale), _ptr(workspace), ctypes.byref(n), _stream(q.device))
+        outputs = (o, lse if return_lse else None)
+        call = PreparedCall(lib().jl_bifocal_decode_batch, args, outputs,
+                            (q, k_cache, v_cache, workspace, kvmap, r0, ln, n))
+        if prepare:
+            return call
+        return call()
 
 
 def rope_rows(x, pos0: int, *, rope_base: float, out=None):

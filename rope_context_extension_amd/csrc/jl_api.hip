@@ -460,3 +460,16 @@ JL_EXPORT int jl_test_rope_angles_device(const int32_t* pos, int64_t n, int32_t 
   hipError_t e = jl_launch_test_angles(pos, n, fr.turn_frac[m], cos_out, sin_out, (hipStream_t)hip_stream);
   return e == hipSuccess ? JL_OK : hip_fail(e, "test kernel");
 }
+
+JL_EXPORT int jl_bench_mfma_peak(int64_t iters, float* sink, int64_t* flops, void* hip_stream) {
+  if (iters < 1 || !sink || !flops) return fail(JL_EINVAL, "bad arguments");
+  *flops = (int64_t)jl_device_shape().cus * 8 * iters * 32 * (32 * 32 * 16 * 2);
+  hipError_t e = jl_launch_mfma_peak(iters, sink, (hipStream_t)hip_stream);
+  return e == hipSuccess ? JL_OK : hip_fail(e, "mfma peak kernel");
+}
+
+JL_EXPORT int jl_bench_read_peak(const void* buf, int64_t bytes, int32_t nontemporal, float* sink, void* hip_stream) {
+  if (!buf || !sink || bytes < 16 || (bytes & 15) || ((uintptr_t)buf & 15)) return fail(JL_EINVAL, "bad arguments");
+  hipError_t e = jl_launch_read_peak(buf, bytes, nontemporal, sink, (hipStream_t)hip_stream);
+  return e == hipSuccess ? JL_OK : hip_fail(e, "read peak kernel");
+}

@@ -567,10 +567,20 @@ void jl_decode_plan(const int64_t* lens, const int64_t* row0, int32_t nseq, int6
   }
   ds->wg_begin[JL_MAX_SEQS] = wg;
   for (int b = nseq; b <= JL_MAX_SEQS; ++b) ds->wg_begin[b] = wg;
+  // Workspace slots: the plan's workgroups, but never fewer than one round
+  // (or the sub-chunk count, when that is smaller).  The workgroup count of
+  // the plan falls when nsub steps up (32767 keys: 256 workgroups of 2
+  // sub-chunks; 32771 keys: 171 of 3), while this bound never decreases as
+  // any length grows, so a workspace sized for the longest step of a
+  // generation loop serves every shorter one.
+  int64_t subs = 0;
+  for (int b = 0; b < nseq; ++b) subs += (lens[b] + SUB - 1) / SUB;
+  const int64_t floor_wgs = subs < cus ? subs : cus;
+  ds->ws_wgs = wg > floor_wgs ? wg : floor_wgs;
 }
 
 size_t jl_decode_workspace_bytes(const JlDecSeqs& ds, int32_t Hq) {
-  return (size_t)ds.wg_begin[ds.nseq] * Hq * (2 + D) * sizeof(float);
+  return (size_t)ds.ws_wgs * Hq * (2 + D) * sizeof(float);
 }
 
 hipError_t jl_launch_decode_bf16(const void* q, const void* k_cache, const void* v_cache, const JlDecSeqs& ds,

@@ -125,6 +125,7 @@ struct JlDecSeqs {
   int32_t G[JL_MAX_SEQS];
   int32_t w0[JL_MAX_SEQS];             // window, L when every key is base (w0 >= L or G = 1)
   int64_t row0[JL_MAX_SEQS];           // first cache row of the sequence
+  int64_t ws_wgs;                      // partial-result slots the workspace holds (>= the workgroups)
 };
 // plan of a call (host): nsub from the total key count, workgroups per sequence
 // cus: compute units of the device (one split workgroup per compute unit)
@@ -145,3 +146,6 @@ hipError_t jl_launch_test_group_size(const int64_t* L, int64_t n, int64_t w, int
 hipError_t jl_launch_test_remote_pos(int64_t x0, int64_t n, int32_t G, int32_t* f, hipStream_t st);
 hipError_t jl_launch_test_angles(const int32_t* pos, int64_t n, uint64_t turn_frac, float* c,
                                  float* s, hipStream_t st);
+// ceiling kernels (measurement): dense MFMA issue on every CU, streaming read
+hipError_t jl_launch_mfma_peak(int64_t iters, float* sink, hipStream_t st);
+hipError_t jl_launch_read_peak(const void* buf, int64_t bytes, int nt, float* sink, hipStream_t st);

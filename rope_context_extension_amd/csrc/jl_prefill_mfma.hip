@@ -714,28 +714,30 @@ __device__ inline void pp_pv(const lds_char* vt, const bf16x8* p, int lane, f32x
 }
 
 // p = bf16(exp2(s + shift)) for the 32 scores of a lane (SHIFT false: shift
-// is 0 and not applied); returns the sum of the bf16 values (the weights the
-// PV product uses), accumulated in two independent chains.
+// is 0 and not applied); returns the sum of the fp32 values, accumulated in
+// four independent chains of plain adds.  The sum is not taken with
+// v_dot2c_f32_bf16 over the packed bf16 values: on gfx950 that instruction
+// waits for the matrix pipe, and issued beside the other wave's MFMAs it runs
+// about seven times slower than an add (measured: 38 cycles per dot2 against
+// 5.6 alone), which made this phase longer than the matrix phase it is meant
+// to hide behind.
 template <bool SHIFT>
 __device__ inline float pp_exp_tile(const f32x16* s, float shift, bf16x8* p) {
-  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
-  float sum[2] = {0.f, 0.f};
+  float sum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       bf16x8 v;
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        v[j] = (__bf16)__builtin_amdgcn_exp2f(SHIFT ? s[sb][8 * hh + j] + shift : s[sb][8 * hh + j]);
-      p[2 * sb + hh] = v;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x2 pr = {v[2 * j], v[2 * j + 1]};
-        sum[hh] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum[hh], false);
+      for (int j = 0; j < 8; ++j) {
+        const float e = __builtin_amdgcn_exp2f(SHIFT ? s[sb][8 * hh + j] + shift : s[sb][8 * hh + j]);
+        v[j] = (__bf16)e;
+        sum[j & 3] += e;
       }
+      p[2 * sb + hh] = v;
     }
-  return sum[0] + sum[1];
+  return (sum[0] + sum[1]) + (sum[2] + sum[3]);
 }
 
 // Largest probability a tile may produce before the stabiliser is moved.

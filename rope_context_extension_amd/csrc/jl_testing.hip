@@ -1,6 +1,8 @@
 // jl_testing.hip - kernels behind the test-only entry points: they run the
 // device build of the position mapper and of the angle formation
-// (jl_mapper.h) over caller-provided ranges.
+// (jl_mapper.h) over caller-provided ranges, and two ceiling kernels that
+// measure what the chip achieves on its own (dense bf16 MFMA issue, streaming
+// HBM reads), the denominators beside the published peaks.
 #include "jl_internal.h"
 
 namespace {
@@ -22,6 +24,67 @@ __global__ void angles_kernel(const int32_t* pos, int64_t n, uint64_t tf, float*
 
 unsigned blocks(int64_t n) { return (unsigned)((n + 255) / 256); }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Dense bf16 MFMA issue with nothing else: 8 waves (two per SIMD), each with
+// four independent 32x32x16 accumulator chains, iters x 32 MFMAs per wave.
+// The result goes to *sink only if it equals a value it never takes, which
+// keeps the work from being removed.
+__global__ void __launch_bounds__(512, 1) mfma_peak_kernel(int64_t iters, float* sink) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(lane * 0.01f + i);
+    b[i] = (__bf16)(i * 0.5f);
+  }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+    }
+  }
+  float r = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) r += c0[i] + c1[i] + c2[i] + c3[i];
+  if (r == -1.2345e-30f) sink[0] = r;
+}
+
+// Streaming read of n16 16-byte words: each thread keeps four loads in
+// flight per step of a grid-stride loop.  NT: non-temporal loads (the cache
+// policy decode uses for its V rows).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ inline u32x4 ld16(const u32x4* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <bool NT>
+__global__ void __launch_bounds__(256) read_peak_kernel(const u32x4* __restrict__ buf, int64_t n16, float* sink) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  uint32_t acc = 0;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = ld16<NT>(buf + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 v = ld16<NT>(buf + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9e3779b9u && n16 < 0) sink[0] = (float)acc;
+}
+
 }  // namespace
 
 hipError_t jl_launch_test_group_size(const int64_t* L, int64_t n, int64_t w, int64_t* G, hipStream_t st) {
@@ -37,5 +100,17 @@ hipError_t jl_launch_test_remote_pos(int64_t x0, int64_t n, int32_t G, int32_t* 
 hipError_t jl_launch_test_angles(const int32_t* pos, int64_t n, uint64_t turn_frac, float* c, float* s,
                                  hipStream_t st) {
   angles_kernel<<<blocks(n), 256, 0, st>>>(pos, n, turn_frac, c, s);
+  return hipGetLastError();
+}
+
+hipError_t jl_launch_mfma_peak(int64_t iters, float* sink, hipStream_t st) {
+  mfma_peak_kernel<<<(unsigned)jl_device_shape().cus, 512, 0, st>>>(iters, sink);
+  return hipGetLastError();
+}
+
+hipError_t jl_launch_read_peak(const void* buf, int64_t bytes, int nt, float* sink, hipStream_t st) {
+  const unsigned grid = (unsigned)jl_device_shape().cus * 8;
+  if (nt) read_peak_kernel<true><<<grid, 256, 0, st>>>((const u32x4*)buf, bytes / 16, sink);
+  else read_peak_kernel<false><<<grid, 256, 0, st>>>((const u32x4*)buf, bytes / 16, sink);
   return hipGetLastError();
 }

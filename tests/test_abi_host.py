@@ -283,3 +283,18 @@ def test_device_shape_default_without_a_device():
         assert (cus.value, xcds.value) == (256, 8)
     else:
         assert cus.value >= 1 and 1 <= xcds.value <= cus.value
+
+
+def test_decode_workspace_never_shrinks_as_L_grows():
+    """The plan's workgroup count falls where the sub-chunk count per
+    workgroup steps up (32767 keys: 256 workgroups of 2 sub-chunks, 32771
+    keys: 171 of 3), but the workspace size does not: a workspace sized for
+    the longest step of a generation loop serves every shorter one."""
+    sizes = [jl.decode_workspace_bytes(L, 32, 8) for L in range(32700, 32900)]
+    assert all(a <= b for a, b in zip(sizes, sizes[1:]))
+    Ls = [0, 1, 63, 64, 65, 1000, 16383, 16384, 16385, 40000, 131072, 2**22, 2**24, 2**25, 2**26 + 1]
+    sizes = [jl.decode_workspace_bytes(L, 32, 8) for L in Ls]
+    assert all(a <= b for a, b in zip(sizes, sizes[1:])), sizes
+    b1 = jl.decode_batch_workspace_bytes([32767, 100], 32, 8)
+    b2 = jl.decode_batch_workspace_bytes([32771, 100], 32, 8)
+    assert b1 <= b2

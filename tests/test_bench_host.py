@@ -44,3 +44,14 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_varlen_flops_are_the_sum_over_sequences():
+    lens = [5, 300, 0, 1, 77]
+    Hq, d, w0 = 2, 64, 40
+    f3, fc = bench.prefill_flops_varlen(lens, Hq, d, w0)
+    causal = sum(_pairs(n, w0)[0] for n in lens)
+    window = sum(_pairs(n, w0)[1] for n in lens)
+    assert fc == 4 * d * Hq * causal and f3 == 4 * d * Hq * (causal + 2 * window)
+    for L in (0, 1, 39, 40, 41, 500):
+        assert bench.window_pairs(L, w0) == _pairs(L, w0)[1]
