@@ -221,6 +221,33 @@ int jl_bifocal_decode_batch(const void* q, const void* k_cache, const void* v_ca
 int jl_rope_rows(const void* x, void* y, int64_t n_rows, int32_t num_heads, int32_t head_dim,
                  jl_dtype dtype, int64_t pos0, double rope_base, void* hip_stream);
 
+/* Bytes of the device scratch that jl_bifocal_decode_noalloc uses for its split-K partial results:
+   256 split workgroups x 32 q heads x (max, sum, 128 channels) fp32. */
+#define JL_DECODE_SCRATCH_BYTES 4259840
+
+/*
+ * jl_bifocal_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops, hosts
+ * that forbid allocation): the split-K partial results go to a scratch array
+ * of JL_DECODE_SCRATCH_BYTES that the library holds in device memory (one
+ * per GPU, kept until the process ends; its address is looked up once per
+ * device).  Nothing is allocated and no allocating routine is called.
+ *
+ * Arguments, layouts, results and errors are those of jl_bifocal_decode (the
+ * same kernels and the same split, so the outputs are bitwise those of
+ * jl_bifocal_decode).  A call whose partials exceed the scratch
+ * (jl_bifocal_decode's workspace size for the same arguments above
+ * JL_DECODE_SCRATCH_BYTES; e.g. more than 32 q heads on a 256-CU device) is
+ * JL_EUNSUPPORTED before anything is launched.  Every call on one GPU shares
+ * that GPU's scratch, so calls that overlap in time on one GPU (different
+ * streams, or different host threads without ordering) race; calls ordered
+ * on one stream do not.
+ */
+int jl_bifocal_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, int64_t L,
+                              void* o, float* lse, int32_t num_q_heads, int32_t num_kv_heads,
+                              const int32_t* q_to_kv, int32_t head_dim, jl_dtype dtype, int64_t w0,
+                              int64_t w_pretrained, double rope_base, float softmax_scale, void* hip_stream);
+
 /* Message describing the last non-JL_OK return on the calling thread. */
 const char* jl_last_error(void);
 

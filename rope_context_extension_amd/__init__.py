@@ -18,11 +18,12 @@ import os
 from typing import Optional, Sequence
 
 __all__ = ["group_size", "prefill", "prefill_workspace_bytes", "decode", "decode_workspace_bytes",
-           "decode_batch", "decode_batch_workspace_bytes", "rope_rows", "PreparedCall",
+           "decode_batch", "decode_batch_workspace_bytes", "decode_noalloc", "rope_rows", "PreparedCall",
            "lib", "JetLongError", "LIB_PATH", "BF16", "FP32"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjetlong.so")
 BF16, FP32 = 0, 1
+DECODE_SCRATCH_BYTES = 4259840  # JL_DECODE_SCRATCH_BYTES: partials the no-allocation decode holds
 BF16_MAX_SEQ_LEN = 8388544   # JL_BF16_MAX_SEQ_LEN: longest sequence of the bf16 prefill
 FP32_MAX_SEQ_LEN = 16777216  # JL_FP32_MAX_SEQ_LEN: longest sequence of the fp32 prefill
 _STATUS = {0: "JL_OK", -1: "JL_EINVAL", -2: "JL_EUNSUPPORTED", -3: "JL_ENOSPC", -4: "JL_EHIP"}
@@ -65,6 +66,11 @@ def lib() -> ctypes.CDLL:
             c.c_void_p, c.c_void_p, c.c_void_p, c.c_int64, c.c_void_p, c.c_void_p,
             c.c_int32, c.c_int32, c.POINTER(c.c_int32), c.c_int32, c.c_int, c.c_int64, c.c_int64,
             c.c_double, c.c_float, c.c_void_p, c.POINTER(c.c_size_t), c.c_void_p]
+        L.jl_bifocal_decode_noalloc.restype = c.c_int
+        L.jl_bifocal_decode_noalloc.argtypes = [
+            c.c_void_p, c.c_void_p, c.c_void_p, c.c_int64, c.c_void_p, c.c_void_p,
+            c.c_int32, c.c_int32, c.POINTER(c.c_int32), c.c_int32, c.c_int, c.c_int64, c.c_int64,
+            c.c_double, c.c_float, c.c_void_p]
         L.jl_bifocal_decode_batch.restype = c.c_int
         L.jl_bifocal_decode_batch.argtypes = [
             c.c_void_p, c.c_void_p, c.c_void_p, c.c_int64,                    # q k_cache v_cache cache_rows
@@ -319,6 +325,37 @@ def decode(q, k_cache, v_cache, L: int, *, w0: int, w_pretrained: int, rope_base
         if prepare:
             return call
         return call()
+
+
+def decode_noalloc(q, k_cache, v_cache, L: int, *, w0: int, w_pretrained: int, rope_base: float,
+                   scale: Optional[float] = None, q_to_kv=None, out=None, lse=None):
+    """The decode step of decode() through jl_bifocal_decode_noalloc: the
+    library allocates nothing and takes its partial results from its own
+    device scratch (JL_DECODE_SCRATCH_BYTES per GPU).  Pass out (and lse) to
+    keep the call itself free of allocation; calls that overlap in time on
+    one GPU share that scratch and race.  Returns (o, lse or None)."""
+    import torch
+    _need(isinstance(q, torch.Tensor) and q.dim() == 2, "q must be a [Hq, d] tensor")
+    _need(isinstance(k_cache, torch.Tensor) and k_cache.dim() == 3, "k_cache must be a [L_cap, Hkv, d] tensor")
+    Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    _check_tensor("q", q, (Hq, d), torch.bfloat16)
+    _check_tensor("k_cache", k_cache, (k_cache.shape[0], Hkv, d), torch.bfloat16)
+    _check_tensor("v_cache", v_cache, tuple(k_cache.shape), torch.bfloat16)
+    _need(0 <= int(L) <= k_cache.shape[0], f"L = {L} outside the cache's {k_cache.shape[0]} rows")
+    if out is not None:
+        _check_tensor("out", out, (Hq, d), torch.bfloat16)
+    if lse is not None:
+        _check_tensor("lse", lse, (Hq,), torch.float32)
+    _check_head_map(q_to_kv, Hq)
+    _check_devices(q.device, q=q, k_cache=k_cache, v_cache=v_cache, out=out, lse=lse)
+    with torch.cuda.device(q.device):
+        o = torch.empty_like(q) if out is None else out
+        _check(lib().jl_bifocal_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), int(L), _ptr(o), _ptr(lse),
+                                               Hq, Hkv, _i32_array(q_to_kv), d, _dtype_code(q), int(w0),
+                                               int(w_pretrained), float(rope_base),
+                                               0.0 if scale is None else float(scale), _stream(q.device)))
+    return o, lse
 
 
 def _packed_rows(lens):

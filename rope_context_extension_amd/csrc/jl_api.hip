@@ -399,6 +399,59 @@ JL_EXPORT int jl_rope_rows(const void* x, void* y, int64_t n_rows, int32_t num_h
   return JL_OK;
 }
 
+// -------------------------------------------------- decode without allocation
+
+// Split-K partials of jl_bifocal_decode_noalloc.  In host code this name is a
+// stand-in, not a device address: kernels get the address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) char scratch[JL_DECODE_SCRATCH_BYTES];
+
+namespace {
+std::once_flag g_scratch_once[JL_MAX_DEVICES];
+void* g_scratch_ptr[JL_MAX_DEVICES];
+hipError_t g_scratch_err[JL_MAX_DEVICES];
+
+// the scratch's address on the current device, looked up once per device
+int scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= JL_MAX_DEVICES) return fail(JL_EUNSUPPORTED, "device %d beyond the %d the library serves", dev,
+                                                    JL_MAX_DEVICES);
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return hip_fail(g_scratch_err[dev], "hipGetSymbolAddress(scratch)");
+  *ptr = g_scratch_ptr[dev];
+  return JL_OK;
+}
+}  // namespace
+
+JL_EXPORT int jl_bifocal_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, int64_t L, void* o,
+                                        float* lse, int32_t num_q_heads, int32_t num_kv_heads, const int32_t* q_to_kv,
+                                        int32_t head_dim, jl_dtype dtype, int64_t w0, int64_t w_pretrained,
+                                        double rope_base, float softmax_scale, void* hip_stream) {
+  // the size query validates every argument and computes the plan's partials
+  size_t need = 0;
+  const int64_t row0 = 0;
+  int rc = decode_impl(nullptr, nullptr, nullptr, -1, &row0, &L, 1, nullptr, nullptr, num_q_heads, num_kv_heads,
+                       q_to_kv, head_dim, dtype, w0, w_pretrained, rope_base, softmax_scale, nullptr, &need, nullptr);
+  if (rc) return rc;
+  if (need > (size_t)JL_DECODE_SCRATCH_BYTES)
+    return fail(JL_EUNSUPPORTED, "this decode needs %zu bytes of partial results; the no-allocation scratch holds %d",
+                need, JL_DECODE_SCRATCH_BYTES);
+  if (need == 0) return JL_OK;   // L == 0
+  if (!q || !k_cache || !v_cache || !o) return fail(JL_EINVAL, "q, caches and o must be device pointers");
+  void* ptr = nullptr;
+  rc = scratch_of_current_device(&ptr);
+  if (rc) return rc;
+  size_t cap = JL_DECODE_SCRATCH_BYTES;
+  return decode_impl(q, k_cache, v_cache, -1, &row0, &L, 1, o, lse, num_q_heads, num_kv_heads, q_to_kv, head_dim, dtype,
+                     w0, w_pretrained, rope_base, softmax_scale, ptr, &cap, hip_stream);
+}
+
 // ------------------------------------------------------------------ test hooks
 
 JL_EXPORT int jl_set_profile_events(void* before, void* mid, void* after) {

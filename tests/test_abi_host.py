@@ -298,3 +298,26 @@ def test_decode_workspace_never_shrinks_as_L_grows():
     b1 = jl.decode_batch_workspace_bytes([32767, 100], 32, 8)
     b2 = jl.decode_batch_workspace_bytes([32771, 100], 32, 8)
     assert b1 <= b2
+
+
+def _na(L=1000, Hq=32, Hkv=8, ptr=None):
+    return L_.jl_bifocal_decode_noalloc(ptr, ptr, ptr, L, ptr, None, Hq, Hkv, None, 128, jl.BF16, 16, 64, 1e6, 0.0,
+                                        None)
+
+
+L_ = L
+
+
+def test_decode_noalloc_host_checks():
+    """The no-allocation decode validates like jl_bifocal_decode, refuses a
+    call whose partials exceed its scratch, and does nothing for L = 0, all
+    before it touches a device."""
+    assert jl.DECODE_SCRATCH_BYTES == 256 * 32 * 130 * 4
+    assert _na(L=0) == JL_OK
+    assert _na(Hq=3) == JL_EINVAL
+    assert _na(L=-1) == JL_EINVAL
+    assert _na(Hq=64, L=131072) == JL_EUNSUPPORTED and b"no-allocation scratch" in L.jl_last_error()
+    assert _na() == JL_EINVAL and b"device pointers" in L.jl_last_error()
+    # within the scratch: the workspace the two-call protocol would ask for
+    for Lx in (1, 4097, 131072, 2**24):
+        assert jl.decode_workspace_bytes(Lx, 32, 8) <= jl.DECODE_SCRATCH_BYTES
