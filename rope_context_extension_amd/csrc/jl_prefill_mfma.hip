@@ -812,11 +812,22 @@ __device__ inline lds_char* pp_vbuf(const PpTiles& T, int k) {
   return T.lds + 2 * KT_BYTES + (k & 1) * VT_BYTES;
 }
 
-// copies issued by group B at half-step 2j: K_{j+1} (if any) and V_j
+// copies issued by group B at half-step 2j: K_{j+1} (if any).  The K and
+// V^T copies of a tile are split between the groups (B copies K, A copies
+// V^T): a wave that issues copies is held at each issue while the vector
+// memory unit works through the queue, and with all ten pieces of a tile in
+// one group's softmax phase that phase outlasted the other group's matrix
+// phase (same-box A/B: the split is 2.4% faster on the whole prefill).
 __device__ inline void pp_copies(const PpTiles& T, int j) {
   if (j + 1 < T.n)
     pp_issue<PP_K_PER_WAVE, KT_PIECES>(pp_kbuf(T, j + 1), T.rk, T.plan.koff,
                                        (uint32_t)(T.t0 + j + 1) * (BK * 256), T.wave & 3);
+}
+// copies issued by group A at half-step 2j+1: V_j, at the start of its
+// softmax phase, waited for at the end of that phase (issued at the end
+// instead, the copy's latency is exposed: 9% slower on the whole prefill; one
+// tile ahead into a third V^T buffer was 1.3% slower than this, same box)
+__device__ inline void pp_copies_v(const PpTiles& T, int j) {
   pp_issue<PP_V_PER_WAVE, VT_PIECES>(pp_vbuf(T, j), T.rv, T.plan.voff, (uint32_t)(T.t0 + j) * (D * BK * 2),
                                      T.wave & 3);
 }
@@ -856,13 +867,14 @@ __device__ inline void pp_matrix(const PpTiles& T, int k, bool pv, const bf16x8*
 
 // The two groups run mirrored straight-line loops with the same number of
 // barriers (half-step h: group A is in its matrix phase for even h, group B
-// for odd h).  K_k is read in half-steps 2k, 2k+1 and V_k in 2k+2, 2k+3;
-// group B copies K_{k+1} and V_k at the start of half-step 2k (ahead of its
-// softmax phase), into the buffers whose last readers finished at half-step
-// 2k-1, and waits for them at the end of half-step 2k+1 (after its matrix
-// phase), in time for group A's matrix phase at 2k+2.  Group A's phases are
-// the longer ones (its matrix phase starts every tile), so it carries no copy
-// work (measured: about 1% against group A issuing the copies).  Tiles in
+// for odd h).  K_k is read in half-steps 2k, 2k+1 and V_k in 2k+2, 2k+3.
+// Group B copies K_{k+1} at the start of half-step 2k (ahead of its softmax
+// phase), into the buffer whose last readers finished at half-step 2k-1, and
+// waits for it at the end of half-step 2k+1 (after its matrix phase), in time
+// for group A's matrix phase at 2k+2.  Group A copies V_k at the start of
+// half-step 2k+1 (its softmax phase of tile k) into the buffer of V_{k-2},
+// whose last reader finished at half-step 2k-1, and waits for it at the end
+// of that half-step, in time for its matrix phase at 2k+2.  Tiles in
 // which a wave has no pair (the last two causal tiles of group A, the first
 // two window tiles of group B) keep their MFMAs, which keeps the loops free
 // of per-wave branches around register-resident state; their softmax only
@@ -886,12 +898,16 @@ __device__ inline void pp_run(const PpTiles& T, const bf16x8* qf, PpState& st, f
   if (T.wave < 4) {
     pp_matrix(T, 0, false, qf, st, s, p, o, lane);
     pp_barrier();
+    pp_copies_v(T, 0);
     pp_softmax_tile<KIND>(T, 0, s, p, st, o, wr, g);
+    pp_wait_copies();
     pp_barrier();
     for (int j = 1; j < n; ++j) {
       pp_matrix(T, j, true, qf, st, s, p, o, lane);
       pp_barrier();
+      pp_copies_v(T, j);
       pp_softmax_tile<KIND>(T, j, s, p, st, o, wr, g);
+      pp_wait_copies();
       pp_barrier();
     }
     pp_pv(pp_vbuf(T, n - 1), p, lane, o);
