@@ -278,7 +278,8 @@ def measure_ceilings(jl, torch, dev, ev, stream):
     del buf
     torch.cuda.synchronize()
     out["method"] = ("mfma: one 8-wave workgroup per CU, four independent v_mfma_f32_32x32x16_bf16 chains per "
-                     f"wave, {iters} x 32 MFMAs per wave; read: 4 GiB streamed with 16-byte loads, median of 5")
+                     f"wave, {iters} x 32 MFMAs per wave; read: 4 GiB streamed, one workgroup per CU over its "
+                     "own contiguous share, eight 16-byte loads in flight per thread, median of 5")
     return out
 
 

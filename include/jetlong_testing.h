@@ -69,7 +69,9 @@ int jl_test_decode_plan(const int64_t* lens, int32_t num_seqs, int32_t cus, int3
    accumulator chains and nothing else; *flops receives the FLOPs of the
    launch.  jl_bench_read_peak: a streaming read of `bytes` (a multiple of 16,
    16-byte aligned device memory) with 16-byte loads, default or
-   non-temporal cache policy.  sink: one device float, written only under a
+   non-temporal cache policy, each workgroup (one per compute unit) streaming
+   its own contiguous share with eight 16-byte loads in flight per thread.
+   sink: one device float, written only under a
    condition the kernels never meet.  Asynchronous on hip_stream; the caller
    times them.  JL_EINVAL on bad arguments. */
 int jl_bench_mfma_peak(int64_t iters, float* sink, int64_t* flops, void* hip_stream);

@@ -18,16 +18,17 @@
 //
 // A workgroup has one wave per kv head (8 waves) and walks its keys in
 // 64-key sub-chunks:
-//   angles  the workgroup fills an LDS table of cos/sin(Delta_j theta_m) for
-//           the sub-chunk's remote keys, shared by every kv head.  A thread
+//   angles  the workgroup fills an LDS table of fp32 cos/sin(Delta_j theta_m)
+//           for the sub-chunk's remote keys, shared by every kv head.  A thread
 //           owns one m and every eighth key: it evaluates the first angle
 //           exactly and steps to the next key by composing with one of two
 //           fixed rotations (over 8 keys Delta moves by floor(8/G) - 8 or
 //           that plus one), one complex product per entry;
 //   scores  per 16-key block a lane holds one key's rotary pairs (m, m + 64)
-//           for 16 values of m, rotates them in registers and feeds them as
-//           the A operand of v_mfma_f32_16x16x32_bf16 against the query
-//           block (B operand: the kv head's q heads as columns);
+//           for 16 values of m, rotates them in fp32 registers (one bf16
+//           rounding, of the rotated key) and feeds them as the A operand of
+//           v_mfma_f32_16x16x32_bf16 against the query block (B operand: the
+//           kv head's q heads as columns);
 //   softmax the sub-chunk's scores of a head sit in 4 lanes x 16 values, so
 //           the max and sum need two lane exchanges; the result is online
 //           across sub-chunks.  Probabilities go to a wave-private LDS row
@@ -91,11 +92,6 @@ __device__ inline int lane_now() {
   return l;
 }
 
-// x.lo * y.lo + x.hi * y.hi in fp32 (v_dot2_f32_bf16)
-__device__ inline float dot2(bf16x2 x, uint32_t y) {
-  return __builtin_amdgcn_fdot2_f32_bf16(x, __builtin_bit_cast(bf16x2, y), 0.f, false);
-}
-
 // channel held in slot j of MFMA step kb by lane group gq (0..3): the lane
 // holds the rotary pairs (16 gq + x, 64 + 16 gq + x), x = 0..15.
 __device__ inline int d_of(int kb, int gq, int j) { return (kb >> 1) * 64 + 16 * gq + 8 * (kb & 1) + j; }
@@ -131,9 +127,13 @@ __device__ inline void load_v_half(VTile& t, int kh, __amdgpu_buffer_rsrc_t rv, 
 
 // Scores of one 16-key block against the rotated query columns: the lane's
 // key rows k[m], k[m + 64] (4 x 16 bytes, pairs 16 gq ..) are rotated by the
-// key's table angles with dot2 and fed as MFMA A operands; steps kb = h take
+// key's table angles in fp32 and fed as MFMA A operands; steps kb = h take
 // rotated k[m] and kb = 2 + h rotated k[m + 64] for pairs 8 h .. 8 h + 7.
-__device__ inline f32x4 remote_block(const u32x4 (&kw)[4], const uint2* trow, const __bf16* qcol, int gq) {
+// The rotation is not done with v_dot2_f32_bf16 on bf16 angle pairs: that
+// rounds the coefficients to bf16 before the rotated key is rounded again
+// (up to 6e-3 on the outputs of short caches), and costs the same time
+// (same-box A/B: within 1% at 32769, 65537 and 131072 keys).
+__device__ inline f32x4 remote_block(const u32x4 (&kw)[4], const float2* trow, const __bf16* qcol, int gq) {
   const uint32_t* a = (const uint32_t*)&kw[0];
   const uint32_t* b = (const uint32_t*)&kw[2];
   f32x4 sr = {0.f, 0.f, 0.f, 0.f};
@@ -143,11 +143,10 @@ __device__ inline f32x4 remote_block(const u32x4 (&kw)[4], const uint2* trow, co
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int x2 = 4 * h + x;    // pairs 2 x2 and 2 x2 + 1: (a, b) = (k[m], k[m + 64])
-      const uint4 t = *(const uint4*)&trow[16 * gq + 2 * x2];
-      const bf16x2 ab_lo = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(b[x2], a[x2], 0x05040100u));
-      const bf16x2 ab_hi = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(b[x2], a[x2], 0x07060302u));
-      w1[x] = pack_bf16(dot2(ab_lo, t.x), dot2(ab_hi, t.z));     // a c - b s
-      w2[x] = pack_bf16(dot2(ab_lo, t.y), dot2(ab_hi, t.w));     // a s + b c
+      const float4 t = *(const float4*)&trow[16 * gq + 2 * x2];   // (c, s) of both pairs, fp32
+      const float a0 = bf_lo(a[x2]), a1 = bf_hi(a[x2]), b0 = bf_lo(b[x2]), b1 = bf_hi(b[x2]);
+      w1[x] = pack_bf16(__builtin_fmaf(a0, t.x, -b0 * t.y), __builtin_fmaf(a1, t.z, -b1 * t.w));   // a c - b s
+      w2[x] = pack_bf16(__builtin_fmaf(a0, t.y, b0 * t.x), __builtin_fmaf(a1, t.w, b1 * t.z));    // a s + b c
     }
     const bf16x8 q1 = *(const bf16x8*)(qcol + d_of(h, gq, 0));
     const bf16x8 q2 = *(const bf16x8*)(qcol + d_of(2 + h, gq, 0));
@@ -177,14 +176,14 @@ __device__ inline bool wait_all(const int* done, int target) {
 
 // Thread (tk, tm)'s part of a sub-chunk's angle table: m = tm, keys tk + 8 r,
 // stepping the thread's angle chain (advanced to the next sub-chunk).
-__device__ inline void fill_trig(uint2 (*tb)[TPITCH], float4* chain, float4 st, int tid, int tm, int tk,
+__device__ inline void fill_trig(float2 (*tb)[TPITCH], float4* chain, float4 st, int tid, int tm, int tk,
                                  int thr, int dlo_g) {
   const float4 ch = chain[tid];
   float c = ch.x, s = ch.y;
   int rem = __float_as_int(ch.z);
 #pragma unroll
   for (int r = 0; r < SUB / TRIG_STEP; ++r) {
-    tb[tk + TRIG_STEP * r][tm] = make_uint2(pack_bf16(c, -s), pack_bf16(s, c));
+    tb[tk + TRIG_STEP * r][tm] = make_float2(c, s);
     const int r8 = rem + TRIG_STEP;
     const bool up = r8 >= thr;
     rem = r8 - (up ? thr : dlo_g);
@@ -208,10 +207,9 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
   // fetch the same columns of different rows, which then fall on distinct
   // banks.
   __shared__ __align__(16) __bf16 qlds[2][MAX_HKV * NG * QPITCH];   // [variant][slot][d]; slot = kvh*NG + n
-  // angle table of the sub-chunk: per (key, m) the bf16 pairs (c, -s) and
-  // (s, c) of c, s = cos, sin(Delta_j theta_m), the two dot products of a
-  // rotation
-  __shared__ __align__(16) uint2 trig[NTRIG][SUB][TPITCH];   // [sub-chunk % NTRIG]
+  // angle table of the sub-chunk: per (key, m) the fp32 pair
+  // c, s = cos, sin(Delta_j theta_m)
+  __shared__ __align__(16) float2 trig[NTRIG][SUB][TPITCH];   // [sub-chunk % NTRIG]
   __shared__ __align__(16) uint32_t prob[MAX_HKV][NG][SUB / 2];   // wave-private [q head][key pair]
   __shared__ int heads[MAX_HKV * NG];
   // per m the two angle-table step rotations, per thread its angle chain
@@ -318,7 +316,7 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
     // sub-chunk sc's table was filled in sub-chunk sc - 2 (or before the
     // loop): every wave has finished that
     if (sc >= 2) in_time &= wait_all(done, sc - 1);
-    const uint2 (*tb)[TPITCH] = trig[sc % NTRIG];
+    const float2 (*tb)[TPITCH] = trig[sc % NTRIG];
     float alpha = 1.f;
     if (active) {
 

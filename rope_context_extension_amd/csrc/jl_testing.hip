@@ -26,6 +26,7 @@ unsigned blocks(int64_t n) { return (unsigned)((n + 255) / 256); }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Dense bf16 MFMA issue with nothing else: 8 waves (two per SIMD), each with
 // four independent 32x32x16 accumulator chains, iters x 32 MFMAs per wave.
@@ -55,11 +56,10 @@ __global__ void __launch_bounds__(512, 1) mfma_peak_kernel(int64_t iters, float*
   if (r == -1.2345e-30f) sink[0] = r;
 }
 
-// Streaming read of n16 16-byte words: each thread keeps four loads in
-// flight per step of a grid-stride loop.  NT: non-temporal loads (the cache
-// policy decode uses for its V rows).
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
+// Streaming read: workgroup b reads its own contiguous share of the buffer
+// with 16-byte loads, eight in flight per thread (the access pattern of the
+// decode split, where each workgroup streams its own key range).  NT:
+// non-temporal loads.
 template <bool NT>
 __device__ inline u32x4 ld16(const u32x4* p) {
   if constexpr (NT) return __builtin_nontemporal_load(p);
@@ -68,19 +68,16 @@ __device__ inline u32x4 ld16(const u32x4* p) {
 
 template <bool NT>
 __global__ void __launch_bounds__(256) read_peak_kernel(const u32x4* __restrict__ buf, int64_t n16, float* sink) {
-  const int64_t stride = (int64_t)gridDim.x * 256;
+  const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t lo = (int64_t)blockIdx.x * per;
+  const int64_t hi = lo + per < n16 ? lo + per : n16;
   uint32_t acc = 0;
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    u32x4 v[4];
+  for (int64_t i = lo + threadIdx.x; i < hi; i += 256 * 8) {
+    u32x4 v[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = ld16<NT>(buf + i + u * stride);
+    for (int u = 0; u < 8; ++u) v[u] = i + u * 256 < hi ? ld16<NT>(buf + i + u * 256) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-  }
-  for (; i < n16; i += stride) {
-    const u32x4 v = ld16<NT>(buf + i);
-    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   if (acc == 0x9e3779b9u && n16 < 0) sink[0] = (float)acc;
 }
@@ -109,7 +106,7 @@ hipError_t jl_launch_mfma_peak(int64_t iters, float* sink, hipStream_t st) {
 }
 
 hipError_t jl_launch_read_peak(const void* buf, int64_t bytes, int nt, float* sink, hipStream_t st) {
-  const unsigned grid = (unsigned)jl_device_shape().cus * 8;
+  const unsigned grid = (unsigned)jl_device_shape().cus;   // one workgroup per compute unit
   if (nt) read_peak_kernel<true><<<grid, 256, 0, st>>>((const u32x4*)buf, bytes / 16, sink);
   else read_peak_kernel<false><<<grid, 256, 0, st>>>((const u32x4*)buf, bytes / 16, sink);
   return hipGetLastError();
