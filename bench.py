@@ -295,6 +295,96 @@ def time_calls(ev, stream, fn, n, warm=2):
     return ev.elapsed_ms(a, b) / n
 
 
+def decode_length_timings(jl, torch, W, dev, ev, stream, lengths=None, plain=True):
+    """Decode steps (32 q / 8 kv heads, d = 128, w0 = 4096, w_pretrained = 32768) at each length over
+    2 GiB of distinct cache windows: bifocal and, with plain, Delta-free (w_pretrained = L: G = 1)."""
+    lengths = W.DECODE_LENGTHS if lengths is None else lengths
+    dcfg = W.decode_8b(CACHE_POOL_ROWS)
+    Hq, Hkv, d = dcfg.num_q_heads, dcfg.num_kv_heads, dcfg.head_dim
+    gen = torch.Generator(device=dev).manual_seed(dcfg.seed + 1)
+    pools = [(torch.randn((CACHE_POOL_ROWS, Hkv, d), generator=gen, device=dev).bfloat16(),
+              torch.randn((CACHE_POOL_ROWS, Hkv, d), generator=gen, device=dev).bfloat16()) for _ in range(4)]
+    qd = torch.randn((Hq, d), generator=gen, device=dev).bfloat16()
+    od = torch.empty_like(qd)
+    lsed = torch.empty((Hq,), dtype=torch.float32, device=dev)
+    wsd = torch.empty(max(16, jl.decode_workspace_bytes(CACHE_POOL_ROWS, Hq, Hkv)), dtype=torch.uint8, device=dev)
+    outd = {}
+    for Lx in lengths:
+        if not 1 <= Lx <= CACHE_POOL_ROWS:
+            raise SystemExit(f"decode length {Lx} outside 1 .. {CACHE_POOL_ROWS}")
+        row = {}
+        for key, wpt in (("bifocal", dcfg.w_pretrained), ("plain", Lx)):
+            if key == "plain" and not plain:
+                continue
+            calls = [jl.decode(qd, kc[w * Lx:(w + 1) * Lx], vc[w * Lx:(w + 1) * Lx], Lx, w0=dcfg.w0,
+                               w_pretrained=wpt, rope_base=dcfg.rope_base, out=od, lse=lsed, workspace=wsd,
+                               prepare=True)
+                     for kc, vc in pools for w in range(CACHE_POOL_ROWS // Lx)]
+            n = max(100, len(calls) * 4)
+            us = 1e3 * time_calls(ev, stream, lambda it=iter(range(10**9)): calls[next(it) % len(calls)](), n,
+                                  warm=len(calls))
+            b = 2 * Lx * Hkv * d * 2
+            row[key] = {"us_per_step": round(us, 2), "GB/s": round(b / (us * 1e-6) / 1e9, 1),
+                        "frac_hbm": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        row["G"] = jl.group_size(Lx, dcfg.w_pretrained)
+        row["kv_bytes"] = 2 * Lx * Hkv * d * 2
+        if plain:
+            row["bifocal_over_plain"] = round(row["bifocal"]["us_per_step"] / row["plain"]["us_per_step"], 4)
+        outd[str(Lx)] = row
+        log(f"[bench] decode L={Lx}: {row['bifocal']['us_per_step']} us ({row['bifocal']['frac_hbm']:.3f} of peak)"
+            + (f", plain {row['plain']['us_per_step']} us" if plain else ""))
+    del pools
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return outd
+
+
+PREFILL_CONFIG_NAMES = ("qwen3_1.7b_L32768", "qwen3_1.7b_L65536", "qwen3_4b_varlen8_w01024",
+                        "qwen3_4b_varlen8_w04096", "qwen3_4b_varlen8_w08192")
+
+
+def prefill_config_timings(jl, torch, W, dev, ev, stream, names=PREFILL_CONFIG_NAMES, calls=3):
+    """Prefill throughput of the other prefill workloads: Qwen3-1.7B heads at 32K (G=1) and 64K (G=2),
+    the Qwen3-4B varlen layer at w0 = 1024, 4096, 8192.  Inputs are drawn on the GPU (the timing does
+    not depend on the values)."""
+    known = {c.name: c for c in [W.QWEN3_1P7B_32K, W.QWEN3_1P7B_64K] + [W.varlen_4b(w) for w in (1024, 4096, 8192)]}
+    res = {}
+    for name in names:
+        if name not in known:
+            raise SystemExit(f"unknown prefill config {name!r}; known: {', '.join(known)}")
+        c = known[name]
+        T = c.total_tokens
+        g2 = torch.Generator(device=dev).manual_seed(c.seed)
+        qx = torch.randn((T, c.num_q_heads, c.head_dim), generator=g2, device=dev).bfloat16()
+        kx = torch.randn((T, c.num_kv_heads, c.head_dim), generator=g2, device=dev).bfloat16()
+        vx = torch.randn((T, c.num_kv_heads, c.head_dim), generator=g2, device=dev).bfloat16()
+        cu = W.cu_seqlens_of(c.seqlens) if len(c.seqlens) > 1 else None
+        ox = torch.empty_like(qx)
+        lx = torch.empty((c.num_q_heads, T), dtype=torch.float32, device=dev)
+        wsx = torch.empty(jl.prefill_workspace_bytes(T, c.num_q_heads, c.num_kv_heads, c.head_dim, jl.BF16,
+                                                     w_pretrained=c.w_pretrained, cu_seqlens=cu),
+                          dtype=torch.uint8, device=dev)
+
+        def call():
+            jl.prefill(qx, kx, vx, w0=c.w0, w_pretrained=c.w_pretrained, rope_base=c.rope_base, cu_seqlens=cu,
+                       out=ox, lse=lx, workspace=wsx)
+
+        ms = time_calls(ev, stream, call, calls, warm=1)
+        f3, fc = prefill_flops_varlen(c.seqlens, c.num_q_heads, c.head_dim, c.w0)
+        gs = [jl.group_size(n, c.w_pretrained) for n in c.seqlens]
+        res[c.name] = {"call_ms": round(ms, 3), "tflops_3pass": round(f3 / (ms * 1e-3) / 1e12, 2),
+                       "frac_3pass": round(f3 / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                       "tflops_causal_basis": round(fc / (ms * 1e-3) / 1e12, 2),
+                       "frac_causal": round(fc / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                       "flops_3pass": f3, "flops_causal": fc, "w0": c.w0, "G": gs,
+                       "seqlens": list(c.seqlens)}
+        log(f"[bench] prefill {c.name}: {ms:.2f} ms, {res[c.name]['tflops_3pass']} TFLOP/s (F_3pass), "
+            f"{res[c.name]['tflops_causal_basis']} (causal)")
+        del qx, kx, vx, ox, lx, wsx
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -310,6 +400,11 @@ def main():
                     help="only copy a 1 GiB buffer three times (counter calibration run)")
     ap.add_argument("--mfma-peak", action="store_true", help="only measure the MFMA-only ceiling")
     ap.add_argument("--read-peak", action="store_true", help="only measure the streaming-read ceiling")
+    ap.add_argument("--prefill-config", action="append", default=[], metavar="NAME",
+                    help=f"only time the named prefill workload(s) ({', '.join(PREFILL_CONFIG_NAMES)}); "
+                         "for per-workload profiler runs")
+    ap.add_argument("--decode-length", action="append", type=int, default=[], metavar="L",
+                    help="only time decode steps at these cache lengths (bifocal); for per-length profiler runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the path shards by "
@@ -339,6 +434,13 @@ def main():
         c = measure_ceilings(jl, torch, dev, ev, stream)
         c["device"] = torch.cuda.get_device_properties(dev).name
         print(json.dumps(c), flush=True)
+        return
+    if args.prefill_config:
+        print(json.dumps(prefill_config_timings(jl, torch, W, dev, ev, stream, names=args.prefill_config)), flush=True)
+        return
+    if args.decode_length:
+        print(json.dumps(decode_length_timings(jl, torch, W, dev, ev, stream, args.decode_length, plain=False)),
+              flush=True)
         return
 
     cfg = W.QWEN3_8B_128K
@@ -418,28 +520,6 @@ def main():
                               args.decode_steps, warm=4)
     torch.cuda.synchronize()
 
-    def run_decode_lengths():
-        """Decode steps at the decode config's lengths, bifocal and plain (w_pretrained = L: G = 1)."""
-        outd = {}
-        for Lx in W.DECODE_LENGTHS:
-            row = {}
-            for key, wpt in (("bifocal", dcfg.w_pretrained), ("plain", Lx)):
-                calls = decode_steps(Lx, wpt)
-                n = max(100, len(calls) * 4)
-                us = 1e3 * time_calls(ev, stream, lambda it=iter(range(10**9)): calls[next(it) % len(calls)](), n,
-                                      warm=len(calls))
-                b = 2 * Lx * Hkv * d * 2
-                row[key] = {"us_per_step": round(us, 2), "GB/s": round(b / (us * 1e-6) / 1e9, 1),
-                            "frac_hbm": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
-            row["G"] = jl.group_size(Lx, dcfg.w_pretrained)
-            row["kv_bytes"] = 2 * Lx * Hkv * d * 2
-            row["bifocal_over_plain"] = round(row["bifocal"]["us_per_step"] / row["plain"]["us_per_step"], 4)
-            outd[str(Lx)] = row
-            log(f"[bench] decode L={Lx}: {row['bifocal']['us_per_step']} us ({row['bifocal']['frac_hbm']:.3f} of "
-                f"peak), plain {row['plain']['us_per_step']} us")
-        torch.cuda.synchronize()
-        return outd
-
     def run_extras():
         """The disjoint-merge variant and plain attention at the same shapes, on the inputs above."""
         od_ = torch.empty_like(o)
@@ -508,50 +588,12 @@ def main():
         return {"lens": lens, "us_per_step": round(us, 2), "kv_bytes": kvb,
                 "GB/s": round(kvb / (us * 1e-6) / 1e9, 1), "frac_hbm": round(kvb / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
 
-    def run_prefill_configs():
-        """Prefill throughput of the other prefill workloads (inputs drawn on the GPU: the timing does
-        not depend on the values)."""
-        res = {}
-        cases = [(W.QWEN3_1P7B_32K, None), (W.QWEN3_1P7B_64K, None)] + \
-                [(W.varlen_4b(w), w) for w in (1024, 4096, 8192)]
-        for c, _ in cases:
-            T = c.total_tokens
-            g2 = torch.Generator(device=dev).manual_seed(c.seed)
-            qx = torch.randn((T, c.num_q_heads, c.head_dim), generator=g2, device=dev).bfloat16()
-            kx = torch.randn((T, c.num_kv_heads, c.head_dim), generator=g2, device=dev).bfloat16()
-            vx = torch.randn((T, c.num_kv_heads, c.head_dim), generator=g2, device=dev).bfloat16()
-            cu = W.cu_seqlens_of(c.seqlens) if len(c.seqlens) > 1 else None
-            ox = torch.empty_like(qx)
-            lx = torch.empty((c.num_q_heads, T), dtype=torch.float32, device=dev)
-            wsx = torch.empty(jl.prefill_workspace_bytes(T, c.num_q_heads, c.num_kv_heads, c.head_dim, jl.BF16,
-                                                         w_pretrained=c.w_pretrained, cu_seqlens=cu),
-                              dtype=torch.uint8, device=dev)
-
-            def call():
-                jl.prefill(qx, kx, vx, w0=c.w0, w_pretrained=c.w_pretrained, rope_base=c.rope_base, cu_seqlens=cu,
-                           out=ox, lse=lx, workspace=wsx)
-
-            ms = time_calls(ev, stream, call, 3, warm=1)
-            f3, fc = prefill_flops_varlen(c.seqlens, c.num_q_heads, c.head_dim, c.w0)
-            gs = [jl.group_size(n, c.w_pretrained) for n in c.seqlens]
-            res[c.name] = {"call_ms": round(ms, 3), "tflops_3pass": round(f3 / (ms * 1e-3) / 1e12, 2),
-                           "frac_3pass": round(f3 / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                           "tflops_causal_basis": round(fc / (ms * 1e-3) / 1e12, 2),
-                           "frac_causal": round(fc / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                           "flops_3pass": f3, "flops_causal": fc, "w0": c.w0, "G": gs,
-                           "seqlens": list(c.seqlens)}
-            log(f"[bench] prefill {c.name}: {ms:.2f} ms, {res[c.name]['tflops_3pass']} TFLOP/s (F_3pass), "
-                f"{res[c.name]['tflops_causal_basis']} (causal)")
-            del qx, kx, vx, ox, lx, wsx
-            torch.cuda.empty_cache()
-        return res
-
-    dl_obj = None if args.headline_only else run_decode_lengths()
     dj_obj, ov_obj = (None, None) if args.headline_only else run_extras()
     db_obj = None if args.headline_only else run_decode_batch()
     del q, k, v, o, ws, pools, head_calls
     torch.cuda.empty_cache()
-    pc_obj = None if args.headline_only else run_prefill_configs()
+    dl_obj = None if args.headline_only else decode_length_timings(jl, torch, W, dev, ev, stream)
+    pc_obj = None if args.headline_only else prefill_config_timings(jl, torch, W, dev, ev, stream)
     ceil = None if args.headline_only else measure_ceilings(jl, torch, dev, ev, stream)
 
     tflops = F3 / (call_ms * 1e-3) / 1e12
