@@ -211,7 +211,6 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
   // c, s = cos, sin(Delta_j theta_m)
   __shared__ __align__(16) float2 trig[NTRIG][SUB][TPITCH];   // [sub-chunk % NTRIG]
   __shared__ __align__(16) uint32_t prob[MAX_HKV][NG][SUB / 2];   // wave-private [q head][key pair]
-  __shared__ int heads[MAX_HKV * NG];
   // per m the two angle-table step rotations, per thread its angle chain
   // (cos, sin, j mod G) at its next key.  Both live in LDS so that no memory
   // load but the tile prefetches sits in the key loop: the load counter is
@@ -233,48 +232,66 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
   const int c_begin = ((int)blockIdx.x - ds.wg_begin[b]) * nsub * SUB;
   const int nsc = min(nsub, (L - c_begin + SUB - 1) / SUB);     // sub-chunks holding keys: >= 1
 
-  // slot s = kvh * NG + n  <->  the n-th q head (in head order) of kv head kvh
-  if (tid < Hq) heads[tid] = hm.head_of_slot[tid];
-
   const int kl = lane & 15, gq = lane >> 4;        // column / row index, lane group
   const int kvh = wave;                              // this wave's kv head
-  // query column kl (columns past NG repeat real heads; their results are
-  // never stored)
-  const int qrow = (kvh * NG + (kl & (NG - 1))) * QPITCH;
   const bool active = kvh < Hkv;
+  const int tm = tid & 63;
+
+  // Loads the prologue's arithmetic needs go out before the tile loads: the
+  // vector load counter completes in order, so a load issued after the tiles
+  // could only be waited for together with them, and the query rotation and
+  // the angle-table set-up would run after the tiles arrive instead of while
+  // they stream in.
+  //   qrow: query column kl is q head head_of_slot[kvh * NG + kl % NG] (the
+  //         query rows sit in LDS by head; columns past NG repeat real heads,
+  //         whose results are never stored);
+  //   qa, qb: this thread's query elements, channels tm and tm + 64 of heads
+  //         wave + 8 r.
+  const uint64_t tf = fr.turn_frac[tm];
+  const int qrow = (int)hm.head_of_slot[kvh * NG + (kl & (NG - 1))] * QPITCH;
+  __bf16 qa[NG], qb[NG];
+#pragma unroll
+  for (int r = 0; r < NG; ++r) {
+    const int h = min(wave + NWAVES * r, Hq - 1);    // unconditional loads: a branch would wait at its end
+    qa[r] = q[h * D + tm];
+    qb[r] = q[h * D + tm + 64];
+  }
+
   const int row_bytes = Hkv * D * 2;
-  const int nrows = min(L - c_begin, nsub * SUB);
+  // a wave without a kv head gets empty resources: its tile loads (issued
+  // like every other wave's, so that no branch sits between the loads and the
+  // waits for them) read zeros without touching memory
+  const int nrec = active ? min(L - c_begin, nsub * SUB) * row_bytes : 0;
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const char*)kc + (row0 + c_begin) * row_bytes), 0, nrows * row_bytes, BUF_RSRC_WORD3);
+      (void*)((const char*)kc + (row0 + c_begin) * row_bytes), 0, nrec, BUF_RSRC_WORD3);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const char*)vc + (row0 + c_begin) * row_bytes), 0, nrows * row_bytes, BUF_RSRC_WORD3);
+      (void*)((const char*)vc + (row0 + c_begin) * row_bytes), 0, nrec, BUF_RSRC_WORD3);
   const int koff = kl * row_bytes + 256 * kvh + 32 * gq;       // key kl, channels 16 gq ..
   const int voff = 8 * gq * row_bytes + 256 * kvh + 16 * kl;   // key 8 gq, channels 8 kl ..
   KTile kt;
   VTile vt;
-  if (active) {
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) load_k_blk(kt, blk, rk, 0, row_bytes, koff);
-    load_v_half(vt, 0, rv, 0, row_bytes, voff);
-    load_v_half(vt, 1, rv, 0, row_bytes, voff);
-  }
-  __syncthreads();
+  for (int blk = 0; blk < 4; ++blk) load_k_blk(kt, blk, rk, 0, row_bytes, koff);
+  load_v_half(vt, 0, rv, 0, row_bytes, voff);
+  load_v_half(vt, 1, rv, 0, row_bytes, voff);
   {
     // the query in both variants: as given (base; bf16 input, so the base
     // scores carry no rounding of q at all) and rotated by Delta_q.  The
     // softmax scale is applied to the fp32 scores (folded into the exp2
     // argument), not to the bf16 query.
     const int dq = jl_remote_pos(i, G) - i;
-    for (int e = tid; e < Hq * 64; e += NT) {
-      const int slot = e >> 6, m = e & 63;
-      const __bf16* qr = q + heads[slot] * D;
-      const float x1 = (float)qr[m], x2 = (float)qr[m + 64];
-      float c, s;
-      jl_rope_sincos(dq, fr.turn_frac[m], &s, &c);
-      qlds[0][slot * QPITCH + m] = (__bf16)x1;
-      qlds[0][slot * QPITCH + m + 64] = (__bf16)x2;
-      qlds[1][slot * QPITCH + m] = (__bf16)(x1 * c - x2 * s);
-      qlds[1][slot * QPITCH + m + 64] = (__bf16)(x2 * c + x1 * s);
+    float c, s;
+    jl_rope_sincos(dq, tf, &s, &c);
+    // rows h >= Hq (past the real heads, never read) get a copy of head
+    // Hq - 1: no branch, so the loads above stay ahead of the tiles
+#pragma unroll
+    for (int r = 0; r < NG; ++r) {
+      const int h = wave + NWAVES * r;
+      const float x1 = (float)qa[r], x2 = (float)qb[r];
+      qlds[0][h * QPITCH + tm] = qa[r];
+      qlds[0][h * QPITCH + tm + 64] = qb[r];
+      qlds[1][h * QPITCH + tm] = (__bf16)(x1 * c - x2 * s);
+      qlds[1][h * QPITCH + tm + 64] = (__bf16)(x2 * c + x1 * s);
     }
   }
 
@@ -283,11 +300,10 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
   // dlo - 7, dlo = floor(8 / G): the second when (j mod G) + 8 >= (dlo + 1) G.
   // The first angle is exact; each later one is the previous composed with
   // the step (one complex product, about an fp32 ulp each).
-  const int tm = tid & 63, tk = tid >> 6;
+  const int tk = tid >> 6;
   const int dlo = TRIG_STEP / G;
   const int dlo_g = dlo * G, thr = dlo_g + G;
   {
-    const uint64_t tf = fr.turn_frac[tm];
     float4 st;   // (cos, sin) of both steps for m = tm
     jl_rope_sincos(dlo - TRIG_STEP, tf, &st.y, &st.x);
     jl_rope_sincos(dlo - TRIG_STEP + 1, tf, &st.w, &st.z);
