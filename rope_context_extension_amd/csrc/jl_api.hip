@@ -44,6 +44,21 @@ void build_freqs(JlFreqs* fr, int d, double base) {
   for (int m = d / 2; m < JL_MAX_HALF; ++m) fr->turn_frac[m] = 0;
 }
 
+// The table for (d, base), built once per thread: 64 long double
+// pow/fmod/ldexp evaluations cost more host time than a short decode step
+// takes on the GPU, and a generation loop asks for the same table every step.
+const JlFreqs& freqs_for(int d, double base) {
+  thread_local int c_d = -1;
+  thread_local double c_base = 0.0;
+  thread_local JlFreqs c_fr;
+  if (c_d != d || c_base != base) {
+    build_freqs(&c_fr, d, base);
+    c_d = d;
+    c_base = base;
+  }
+  return c_fr;
+}
+
 int build_head_map(JlHeadMap* hm, int Hq, int Hkv, const int32_t* q_to_kv) {
   if (Hq < 1 || Hkv < 1) return fail(JL_EINVAL, "num_q_heads and num_kv_heads must be >= 1");
   if (Hq > JL_MAX_HEADS) return fail(JL_EUNSUPPORTED, "num_q_heads > %d", JL_MAX_HEADS);
@@ -212,8 +227,7 @@ static int prefill_impl(const void* q, const void* k, const void* v, void* o, fl
   if (dtype == JL_BF16 && (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15))
     return fail(JL_EINVAL, "bf16 tensors must be 16-byte aligned");
 
-  JlFreqs fr;
-  build_freqs(&fr, head_dim, rope_base);
+  const JlFreqs& fr = freqs_for(head_dim, rope_base);
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
   hipStream_t st = (hipStream_t)hip_stream;
   char* wsb = (char*)workspace;
@@ -346,8 +360,7 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache, 
   if (((uintptr_t)workspace & 15) || (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15))
     return fail(JL_EINVAL, "q, caches and workspace must be 16-byte aligned");
 
-  JlFreqs fr;
-  build_freqs(&fr, head_dim, rope_base);
+  const JlFreqs& fr = freqs_for(head_dim, rope_base);
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
   if (g_ev_before) (void)hipEventRecord(g_ev_before, (hipStream_t)hip_stream);
   hipError_t e = jl_launch_decode_bf16(q, k_cache, v_cache, ds, o, lse, num_q_heads, num_kv_heads, hm, scale, fr,
@@ -391,8 +404,7 @@ JL_EXPORT int jl_rope_rows(const void* x, void* y, int64_t n_rows, int32_t num_h
   if (n_rows > 0 && pos0 + n_rows - 1 > (int64_t)INT32_MAX) return fail(JL_EUNSUPPORTED, "positions >= 2^31");
   if (n_rows == 0) return JL_OK;
   if (!x || !y) return fail(JL_EINVAL, "x and y must be device pointers");
-  JlFreqs fr;
-  build_freqs(&fr, head_dim, rope_base);
+  const JlFreqs& fr = freqs_for(head_dim, rope_base);
   hipError_t e = jl_launch_rope_rows(x, y, dtype == JL_BF16 ? 2 : 4, n_rows, num_heads, head_dim, pos0, fr,
                                      (hipStream_t)hip_stream);
   if (e != hipSuccess) return hip_fail(e, "rope launch");
@@ -508,8 +520,7 @@ JL_EXPORT int jl_test_rope_angles_device(const int32_t* pos, int64_t n, int32_t 
       !(rope_base > 0.0) || (n > 0 && (!pos || !cos_out || !sin_out)))
     return fail(JL_EINVAL, "bad arguments");
   if (n == 0) return JL_OK;
-  JlFreqs fr;
-  build_freqs(&fr, head_dim, rope_base);
+  const JlFreqs& fr = freqs_for(head_dim, rope_base);
   hipError_t e = jl_launch_test_angles(pos, n, fr.turn_frac[m], cos_out, sin_out, (hipStream_t)hip_stream);
   return e == hipSuccess ? JL_OK : hip_fail(e, "test kernel");
 }
