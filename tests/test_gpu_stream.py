@@ -53,6 +53,22 @@ def test_rope_rows_matches_oracle(pos0):
     assert torch.allclose(nx.double(), ny, rtol=1e-5, atol=1e-6)
 
 
+def test_rope_rows_alternating_bases_and_dims():
+    """The library keeps the last frequency table it built (per host thread),
+    keyed by head_dim and base: calls that alternate both must each get their
+    own table, checked against the fp64 oracle (a stale table would rotate
+    by the wrong angles)."""
+    jl, torch = gpu_or_skip()
+    g = torch.Generator("cpu").manual_seed(11)
+    pos0, n, H = 4000, 64, 2
+    for d, base in [(128, 1e6), (128, 1e4), (64, 1e4), (128, 1e6), (64, 5e5), (128, 1e4)]:
+        x = torch.randn((n, H, d), generator=g)
+        ref = oracle.rope(x.double().numpy(), np.arange(pos0, pos0 + n), oracle.rope_theta(d, base))
+        y = jl.rope_rows(x.cuda(), pos0, rope_base=base).cpu().double().numpy()
+        _say(f"[rope] d={d} base={base:g}: max err {max_abs(y, ref):.2e}")
+        assert max_abs(y, ref) <= 1e-5
+
+
 def test_rope_rows_empty_and_rejects():
     jl, torch = gpu_or_skip()
     x = torch.zeros((0, 2, 128), dtype=torch.bfloat16, device="cuda")
