@@ -35,7 +35,8 @@ Prints ONE JSON line:
             varlen lengths, 8K .. 128K) in one call, KV bytes over time;
   overhead  the bifocal calls over plain attention at the same shapes (the same
             library with w_pretrained = L, i.e. G = 1: plain causal RoPE prefill
-            and Delta-free decode);
+            and Delta-free decode); also the prefill call that writes the decode
+            cache of its keys, beside the separate row rotation it replaces;
   cpu_baseline  the fp64 oracle on the host cores: a sample of query rows of
             the same layer (the value), the whole tiny fp32 config and whole
             decode steps (median of 3), and the full layer extrapolated from
@@ -545,6 +546,19 @@ def main():
         dj_do = float((od_.float() - o.float()).abs().max().item())
         del od_, lsed_
 
+        # the prefill that also writes the decode cache of its keys, beside the separate row rotation
+        # that would otherwise build that cache (one read and one write of k)
+        kc_ = torch.empty_like(k)
+
+        def prefill_kcache():
+            jl.prefill(q, k, v, w0=cfg.w0, w_pretrained=cfg.w_pretrained, rope_base=cfg.rope_base, out=o,
+                       lse=lse, workspace=ws, k_cache_out=kc_)
+
+        kc_ms = time_calls(ev, stream, prefill_kcache, 3, warm=1)
+        rows_ms = time_calls(ev, stream, lambda: jl.rope_rows(k, 0, rope_base=cfg.rope_base, out=kc_), 5, warm=1)
+        torch.cuda.synchronize()
+        del kc_
+
         # plain attention at the same shapes: G = 1 (w_pretrained = L) makes every aliased position the
         # absolute one, so the same library runs plain causal RoPE attention (one full-causal pass)
         def prefill_plain():
@@ -567,7 +581,9 @@ def main():
         ov = {"prefill_plain_causal_ms": round(plain_ms, 3),
               "prefill_bifocal_over_plain": round(call_ms / plain_ms, 4),
               "decode_plain_us_per_step": round(dec_plain_us, 2),
-              "decode_bifocal_over_plain": round(dec_us / dec_plain_us, 4)}
+              "decode_bifocal_over_plain": round(dec_us / dec_plain_us, 4),
+              "prefill_with_cache_output_ms": round(kc_ms, 3),
+              "cache_by_separate_rope_rows_ms": round(rows_ms, 3)}
         log(f"[bench] plain causal prefill {plain_ms:.2f} ms, Delta-free decode {dec_plain_us:.1f} us; "
             f"disjoint merge {dj_ms:.2f} ms (far pass {dj_far_ms:.2f} ms)")
         return dj, ov

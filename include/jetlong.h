@@ -121,6 +121,32 @@ int jl_bifocal_prefill(const void* q, const void* k, const void* v, void* o, flo
                        size_t* workspace_bytes, void* hip_stream);
 
 /*
+ * jl_bifocal_prefill that also writes the decode cache of its keys
+ * (technical summary, Methodology item 2: the cache holds the keys rotated by
+ * base RoPE at their absolute positions, and generation continues from it
+ * without rewriting it).  The pre-pass that rotates k for the attention
+ * passes also stores the base-rotated key of every token in the input's
+ * layout, so a prefill followed by decode steps needs no second pass over k:
+ *
+ *   k_cache    [total_tokens, num_kv_heads, head_dim] dtype (written),
+ *              16-byte aligned, overlapping none of q, k, v, o, lse or the
+ *              workspace.  Row t of sequence b (t = cu_seqlens[b] + p) holds
+ *              k[t] rotated at position p of that sequence, the same bits
+ *              jl_rope_rows writes for those rows at pos0 = 0.
+ *
+ * Every other argument, the workspace size, o, lse and the errors are those
+ * of jl_bifocal_prefill (o and lse are bitwise its results); a size query
+ * (workspace NULL) ignores k_cache, and a call with a workspace and
+ * total_tokens > 0 needs k_cache non-NULL (JL_EINVAL).
+ */
+int jl_bifocal_prefill_kcache(const void* q, const void* k, const void* v, void* o, float* lse,
+                              void* k_cache, const int64_t* cu_seqlens, int32_t num_seqs,
+                              int64_t total_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                              const int32_t* q_to_kv, int32_t head_dim, jl_dtype dtype, int64_t w0,
+                              int64_t w_pretrained, double rope_base, float softmax_scale,
+                              void* workspace, size_t* workspace_bytes, void* hip_stream);
+
+/*
  * The same bifocal prefill with the far pairs computed directly instead of as
  * a difference of two passes (technical summary, Methodology item 2: pairs
  * inside the local window see base-RoPE q/k, all farther pairs see the

@@ -61,6 +61,13 @@ def lib() -> ctypes.CDLL:
                 c.c_int32, c.c_int32, c.POINTER(c.c_int32),                       # Hq Hkv q_to_kv
                 c.c_int32, c.c_int, c.c_int64, c.c_int64, c.c_double, c.c_float,  # d dtype w0 wpt base scale
                 c.c_void_p, c.POINTER(c.c_size_t), c.c_void_p]                    # ws ws_bytes stream
+        L.jl_bifocal_prefill_kcache.restype = c.c_int
+        L.jl_bifocal_prefill_kcache.argtypes = [
+            c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,  # q k v o lse k_cache
+            c.POINTER(c.c_int64), c.c_int32, c.c_int64,                           # cu_seqlens nseq T
+            c.c_int32, c.c_int32, c.POINTER(c.c_int32),                           # Hq Hkv q_to_kv
+            c.c_int32, c.c_int, c.c_int64, c.c_int64, c.c_double, c.c_float,      # d dtype w0 wpt base scale
+            c.c_void_p, c.POINTER(c.c_size_t), c.c_void_p]                        # ws ws_bytes stream
         L.jl_bifocal_decode.restype = c.c_int
         L.jl_bifocal_decode.argtypes = [
             c.c_void_p, c.c_void_p, c.c_void_p, c.c_int64, c.c_void_p, c.c_void_p,
@@ -153,6 +160,12 @@ def _check_tensor(name: str, t, shape, dtype) -> None:
     _need(t.is_contiguous(), f"{name} must be contiguous")
 
 
+def _overlap(a, b) -> bool:
+    """Whether two tensors' byte ranges intersect."""
+    a0, b0 = a.data_ptr(), b.data_ptr()
+    return a0 < b0 + b.numel() * b.element_size() and b0 < a0 + a.numel() * a.element_size()
+
+
 def _check_devices(device, **tensors) -> None:
     """Every tensor lives on the same GPU as the first one."""
     for name, t in tensors.items():
@@ -208,7 +221,11 @@ def _dtype_code(t) -> int:
 
 
 def _prefill_call(q, k, v, o, lse, cu, nseq, T, Hq, Hkv, kvmap, d, dt, w0, w_pt, base, scale,
-                  ws, ws_bytes, stream, disjoint=False):
+                  ws, ws_bytes, stream, disjoint=False, kc=None):
+    if kc is not None:
+        return lib().jl_bifocal_prefill_kcache(q, k, v, o, lse, kc, cu, nseq, T, Hq, Hkv, kvmap, d, dt, int(w0),
+                                               int(w_pt), float(base), float(scale), ws, ctypes.byref(ws_bytes),
+                                               stream)
     fn = lib().jl_bifocal_prefill_disjoint if disjoint else lib().jl_bifocal_prefill
     return fn(q, k, v, o, lse, cu, nseq, T, Hq, Hkv, kvmap, d, dt, int(w0), int(w_pt), float(base),
               float(scale), ws, ctypes.byref(ws_bytes), stream)
@@ -227,12 +244,14 @@ def prefill_workspace_bytes(total_tokens: int, num_q_heads: int, num_kv_heads: i
 
 def prefill(q, k, v, *, w0: int, w_pretrained: int, rope_base: float, cu_seqlens=None,
             scale: Optional[float] = None, q_to_kv=None, out=None, lse=None, return_lse=True,
-            workspace=None, disjoint: bool = False):
+            workspace=None, disjoint: bool = False, k_cache_out=None):
     """Bifocal causal prefill.  q [T, Hq, d], k/v [T, Hkv, d] raw projections
     (bf16 or fp32, CUDA, contiguous).  Returns (o [T, Hq, d], lse [Hq, T] fp32
     or None).  cu_seqlens: host list of packed sequence offsets.  disjoint:
     merge the window pass with a far-only pass instead of the three-pass
-    inclusion-exclusion (bf16 only)."""
+    inclusion-exclusion (bf16 only).  k_cache_out: a [T, Hkv, d] tensor of
+    q's dtype that receives the base-rotated keys (each sequence's decode
+    cache, the bits rope_rows gives at pos0 = 0); three-pass form only."""
     import torch
     _need(isinstance(q, torch.Tensor) and q.dim() == 3, "q must be a [T, Hq, d] tensor")
     dt = _dtype_code(q)
@@ -246,11 +265,17 @@ def prefill(q, k, v, *, w0: int, w_pretrained: int, rope_base: float, cu_seqlens
         _check_tensor("out", out, (T, Hq, d), q.dtype)
     if return_lse and lse is not None:
         _check_tensor("lse", lse, (Hq, T), torch.float32)
+    if k_cache_out is not None:
+        _need(not disjoint, "k_cache_out is written by the three-pass form only")
+        _check_tensor("k_cache_out", k_cache_out, (T, Hkv, d), q.dtype)
+        for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse if return_lse else None)):
+            _need(t is None or not _overlap(k_cache_out, t), f"k_cache_out overlaps {name}")
     _check_head_map(q_to_kv, Hq)
     if cu_seqlens is not None:
         _need(len(cu_seqlens) >= 2 and int(cu_seqlens[0]) == 0 and int(cu_seqlens[-1]) == T,
               "cu_seqlens must start at 0 and end at the token count")
-    _check_devices(q.device, q=q, k=k, v=v, out=out, lse=lse if return_lse else None, workspace=workspace)
+    _check_devices(q.device, q=q, k=k, v=v, out=out, lse=lse if return_lse else None, workspace=workspace,
+                   k_cache_out=k_cache_out)
     # the plan follows the shape of the current device: make it the tensors' device
     with torch.cuda.device(q.device):
         nseq = 1 if cu_seqlens is None else len(cu_seqlens) - 1
@@ -267,7 +292,7 @@ def prefill(q, k, v, *, w0: int, w_pretrained: int, rope_base: float, cu_seqlens
         _check(_prefill_call(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse) if return_lse else None,
                              cu, nseq, T, Hq, Hkv, kvmap, d, dt, w0, w_pretrained, rope_base,
                              0.0 if scale is None else scale, _ptr(workspace), n, _stream(q.device),
-                             disjoint))
+                             disjoint, None if k_cache_out is None else _ptr(k_cache_out)))
     return o, (lse if return_lse else None)
 
 

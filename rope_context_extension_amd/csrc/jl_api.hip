@@ -145,7 +145,7 @@ static int prefill_impl(const void* q, const void* k, const void* v, void* o, fl
                         int32_t num_q_heads, int32_t num_kv_heads, const int32_t* q_to_kv,
                         int32_t head_dim, jl_dtype dtype, int64_t w0, int64_t w_pretrained,
                         double rope_base, float softmax_scale, void* workspace,
-                        size_t* workspace_bytes, void* hip_stream, bool disjoint) {
+                        size_t* workspace_bytes, void* hip_stream, bool disjoint, void* k_cache) {
   if (workspace_bytes == nullptr) return fail(JL_EINVAL, "workspace_bytes is NULL");
   if (total_tokens < 0) return fail(JL_EINVAL, "total_tokens < 0");
   if (dtype != JL_BF16 && dtype != JL_FP32) return fail(JL_EINVAL, "unknown dtype %d", (int)dtype);
@@ -226,6 +226,7 @@ static int prefill_impl(const void* q, const void* k, const void* v, void* o, fl
   if (((uintptr_t)workspace & 255) != 0) return fail(JL_EINVAL, "workspace must be 256-byte aligned");
   if (dtype == JL_BF16 && (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15))
     return fail(JL_EINVAL, "bf16 tensors must be 16-byte aligned");
+  if (k_cache != nullptr && ((uintptr_t)k_cache & 15)) return fail(JL_EINVAL, "k_cache must be 16-byte aligned");
 
   const JlFreqs& fr = freqs_for(head_dim, rope_base);
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
@@ -238,6 +239,7 @@ static int prefill_impl(const void* q, const void* k, const void* v, void* o, fl
   ws.kr = pl.seqs.any_remote ? (void*)(wsb + pl.off_kr) : ws.kb;
   ws.vt = dtype == JL_BF16 ? (void*)(wsb + pl.off_vt) : nullptr;
   ws.qb_lo = ws.qr_lo = ws.kb_lo = ws.kr_lo = nullptr;
+  ws.kc = k_cache;
   {
     const size_t no = align256((size_t)num_q_heads * total_tokens * head_dim * 4);
     const size_t nl = align256((size_t)num_q_heads * total_tokens * 4);
@@ -292,7 +294,20 @@ JL_EXPORT int jl_bifocal_prefill(const void* q, const void* k, const void* v, vo
                                  size_t* workspace_bytes, void* hip_stream) {
   return prefill_impl(q, k, v, o, lse, cu_seqlens, num_seqs, total_tokens, num_q_heads, num_kv_heads, q_to_kv,
                       head_dim, dtype, w0, w_pretrained, rope_base, softmax_scale, workspace, workspace_bytes,
-                      hip_stream, false);
+                      hip_stream, false, nullptr);
+}
+
+JL_EXPORT int jl_bifocal_prefill_kcache(const void* q, const void* k, const void* v, void* o, float* lse,
+                                        void* k_cache, const int64_t* cu_seqlens, int32_t num_seqs,
+                                        int64_t total_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                                        const int32_t* q_to_kv, int32_t head_dim, jl_dtype dtype, int64_t w0,
+                                        int64_t w_pretrained, double rope_base, float softmax_scale,
+                                        void* workspace, size_t* workspace_bytes, void* hip_stream) {
+  if (k_cache == nullptr && workspace != nullptr && total_tokens > 0)
+    return fail(JL_EINVAL, "k_cache must be a device pointer");
+  return prefill_impl(q, k, v, o, lse, cu_seqlens, num_seqs, total_tokens, num_q_heads, num_kv_heads, q_to_kv,
+                      head_dim, dtype, w0, w_pretrained, rope_base, softmax_scale, workspace, workspace_bytes,
+                      hip_stream, false, k_cache);
 }
 
 JL_EXPORT int jl_bifocal_prefill_disjoint(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -303,7 +318,7 @@ JL_EXPORT int jl_bifocal_prefill_disjoint(const void* q, const void* k, const vo
                                           size_t* workspace_bytes, void* hip_stream) {
   return prefill_impl(q, k, v, o, lse, cu_seqlens, num_seqs, total_tokens, num_q_heads, num_kv_heads, q_to_kv,
                       head_dim, dtype, w0, w_pretrained, rope_base, softmax_scale, workspace, workspace_bytes,
-                      hip_stream, true);
+                      hip_stream, true, nullptr);
 }
 
 // One or more sequences: lens[b] keys at cache rows row0[b] .. row0[b] + lens[b] - 1.

@@ -74,6 +74,7 @@ struct JlPrefillWs {
   void* o2;      // [Hq][T][d] fp32: normalised pass-2 output
   void* lse1;    // [Hq][T] fp32: pass-1 LogSumExp, log2 units
   void* lse2;    // [Hq][T] fp32: pass-2 LogSumExp, log2 units
+  void* kc;      // [T][Hkv][d] dtype: base-rotated k in cache layout (optional output), or nullptr
   int64_t t_pad;
 };
 

@@ -18,6 +18,14 @@ namespace {
 
 template <typename T>
 __device__ inline float ld_f(const T* p) { return (float)(*p); }
+
+// The rotation of one half-split pair by (c, s), with its fused multiply-adds
+// written out: the pre-pass and the row rotation below give the same bits
+// for the same input and position, so a cache built by either matches.
+__device__ inline void rot_pair(float x1, float x2, float c, float s, float* y1, float* y2) {
+  *y1 = __builtin_fmaf(x1, c, -(x2 * s));
+  *y2 = __builtin_fmaf(x2, c, x1 * s);
+}
 template <typename T>
 __device__ inline void st_f(T* p, float x) { *p = (T)x; }
 
@@ -33,13 +41,18 @@ __device__ inline void st_split(T* hi, T* lo, float y) {
 // One thread per (token, frequency m); it rotates pair (m, m + d/2) of every
 // q and k head of that token with one sin/cos evaluation per grid.  q is
 // multiplied by qscale first (the bf16 path folds softmax scale * log2(e)
-// into q, so its score products come out in log2 units).
+// into q, so its score products come out in log2 units).  With kc set, the
+// base-rotated k is also written in the input's [T][Hkv][d] layout: the
+// decode cache of the same tokens (technical summary on gist.science,
+// Methodology item 2: the cache holds keys rotated at their absolute
+// positions), at the cost of one extra write of k instead of a second pass
+// over it.
 template <typename T>
 __global__ void __launch_bounds__(256) rope_prepass_kernel(
     const T* __restrict__ q, const T* __restrict__ k, T* __restrict__ qb, T* __restrict__ qr,
     T* __restrict__ kb, T* __restrict__ kr, T* __restrict__ qb_lo, T* __restrict__ qr_lo,
-    T* __restrict__ kb_lo, T* __restrict__ kr_lo, int64_t total, int64_t t_pad, int Hq, int Hkv,
-    int d, JlSeqs seqs, JlFreqs fr, int write_remote, float qscale) {
+    T* __restrict__ kb_lo, T* __restrict__ kr_lo, T* __restrict__ kc, int64_t total, int64_t t_pad, int Hq,
+    int Hkv, int d, JlSeqs seqs, JlFreqs fr, int write_remote, float qscale) {
   const int half = d >> 1;
   const int tpb = 256 / half;               // tokens per block
   const int tl = threadIdx.x / half;
@@ -94,29 +107,40 @@ __global__ void __launch_bounds__(256) rope_prepass_kernel(
   for (int h = 0; h < Hq; ++h) {
     const T* x = q + (t * Hq + h) * d;
     const float x1 = ld_f(x + m) * qscale, x2 = ld_f(x + m + half) * qscale;
+    float y1, y2;
     T* yb = qb + ((int64_t)h * t_pad + t) * d;
     T* lb = lo ? qb_lo + ((int64_t)h * lrows + lrow) * d : nullptr;
-    st_split(yb + m, lb ? lb + m : nullptr, x1 * cb - x2 * sb);
-    st_split(yb + m + half, lb ? lb + m + half : nullptr, x2 * cb + x1 * sb);
+    rot_pair(x1, x2, cb, sb, &y1, &y2);
+    st_split(yb + m, lb ? lb + m : nullptr, y1);
+    st_split(yb + m + half, lb ? lb + m + half : nullptr, y2);
     if (write_remote) {
       T* yr = qr + ((int64_t)h * t_pad + t) * d;
       T* lr = lo ? qr_lo + ((int64_t)h * lrows + lrow) * d : nullptr;
-      st_split(yr + m, lr ? lr + m : nullptr, x1 * cr - x2 * sr);
-      st_split(yr + m + half, lr ? lr + m + half : nullptr, x2 * cr + x1 * sr);
+      rot_pair(x1, x2, cr, sr, &y1, &y2);
+      st_split(yr + m, lr ? lr + m : nullptr, y1);
+      st_split(yr + m + half, lr ? lr + m + half : nullptr, y2);
     }
   }
   for (int h = 0; h < Hkv; ++h) {
     const T* x = k + (t * Hkv + h) * d;
     const float x1 = ld_f(x + m), x2 = ld_f(x + m + half);
+    float y1, y2;
     T* yb = kb + ((int64_t)h * t_pad + t) * d;
     T* lb = lo ? kb_lo + ((int64_t)h * lrows + lrow) * d : nullptr;
-    st_split(yb + m, lb ? lb + m : nullptr, x1 * cb - x2 * sb);
-    st_split(yb + m + half, lb ? lb + m + half : nullptr, x2 * cb + x1 * sb);
+    rot_pair(x1, x2, cb, sb, &y1, &y2);
+    st_split(yb + m, lb ? lb + m : nullptr, y1);
+    st_split(yb + m + half, lb ? lb + m + half : nullptr, y2);
+    if (kc != nullptr) {
+      T* yc = kc + (t * Hkv + h) * d;
+      st_f(yc + m, y1);
+      st_f(yc + m + half, y2);
+    }
     if (write_remote) {
       T* yr = kr + ((int64_t)h * t_pad + t) * d;
       T* lr = lo ? kr_lo + ((int64_t)h * lrows + lrow) * d : nullptr;
-      st_split(yr + m, lr ? lr + m : nullptr, x1 * cr - x2 * sr);
-      st_split(yr + m + half, lr ? lr + m + half : nullptr, x2 * cr + x1 * sr);
+      rot_pair(x1, x2, cr, sr, &y1, &y2);
+      st_split(yr + m, lr ? lr + m : nullptr, y1);
+      st_split(yr + m + half, lr ? lr + m + half : nullptr, y2);
     }
   }
 }
@@ -144,8 +168,10 @@ __global__ void __launch_bounds__(256) rope_rows_kernel(const T* x, T* y, int64_
       const T* xr = x + (r * H + h) * d;
       T* yr = y + (r * H + h) * d;
       const float x1 = ld_f(xr + m), x2 = ld_f(xr + m + half);
-      st_f(yr + m, x1 * c - x2 * s);
-      st_f(yr + m + half, x2 * c + x1 * s);
+      float y1, y2;
+      rot_pair(x1, x2, c, s, &y1, &y2);
+      st_f(yr + m, y1);
+      st_f(yr + m + half, y2);
     }
   }
 }
@@ -204,12 +230,12 @@ hipError_t jl_launch_rope_prepass(const void* q, const void* k, const JlPrefillW
     rope_prepass_kernel<__bf16><<<grid, 256, 0, st>>>(
         (const __bf16*)q, (const __bf16*)k, (__bf16*)ws.qb, (__bf16*)ws.qr, (__bf16*)ws.kb,
         (__bf16*)ws.kr, (__bf16*)ws.qb_lo, (__bf16*)ws.qr_lo, (__bf16*)ws.kb_lo,
-        (__bf16*)ws.kr_lo, total_tokens, ws.t_pad, Hq, Hkv, d, seqs, fr, wr, qscale);
+        (__bf16*)ws.kr_lo, (__bf16*)ws.kc, total_tokens, ws.t_pad, Hq, Hkv, d, seqs, fr, wr, qscale);
   } else {
     rope_prepass_kernel<float><<<grid, 256, 0, st>>>(
         (const float*)q, (const float*)k, (float*)ws.qb, (float*)ws.qr, (float*)ws.kb,
-        (float*)ws.kr, nullptr, nullptr, nullptr, nullptr, total_tokens, ws.t_pad, Hq, Hkv, d,
-        seqs, fr, wr, qscale);
+        (float*)ws.kr, nullptr, nullptr, nullptr, nullptr, (float*)ws.kc, total_tokens, ws.t_pad, Hq, Hkv,
+        d, seqs, fr, wr, qscale);
   }
   return hipGetLastError();
 }

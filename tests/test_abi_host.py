@@ -138,6 +138,34 @@ def test_disjoint_prefill_host_checks():
     assert _pf(fn="jl_bifocal_prefill_disjoint", ws=0x1000, nbytes=n)[0] == JL_EINVAL
 
 
+def _pf_kc(kc, **kw):
+    a = dict(q=None, k=None, v=None, o=None, lse=None, cu=None, nseq=1, T=256, Hq=4, Hkv=2, kvmap=None,
+             d=128, dt=jl.BF16, w0=16, wpt=64, base=10000.0, scale=0.0, ws=None, nbytes=0)
+    a.update(kw)
+    n = ctypes.c_size_t(a["nbytes"])
+    rc = L.jl_bifocal_prefill_kcache(a["q"], a["k"], a["v"], a["o"], a["lse"], kc, a["cu"], a["nseq"], a["T"],
+                                     a["Hq"], a["Hkv"], a["kvmap"], a["d"], a["dt"], a["w0"], a["wpt"],
+                                     a["base"], a["scale"], a["ws"], ctypes.byref(n), None)
+    return rc, n.value
+
+
+def test_kcache_prefill_host_checks():
+    # the size query is the three-pass call's and ignores the cache pointer
+    rc, n = _pf()
+    assert _pf_kc(None) == (JL_OK, n) and _pf_kc(0x1000) == (JL_OK, n)
+    assert _pf_kc(None, dt=jl.FP32, d=64) == _pf(dt=jl.FP32, d=64)
+    # the argument checks of the three-pass call, before anything is launched
+    assert _pf_kc(0x1000, Hq=3, Hkv=2)[0] == JL_EINVAL
+    assert _pf_kc(0x1000, d=96)[0] == JL_EUNSUPPORTED
+    ptrs = dict(ws=0x1000, nbytes=n, q=0x1000, k=0x1000, v=0x1000, o=0x1000)
+    assert _pf_kc(0x1000, **dict(ptrs, nbytes=n - 1))[0] == JL_ENOSPC
+    # a call that would launch needs the cache pointer, 16-byte aligned
+    assert _pf_kc(None, **ptrs)[0] == JL_EINVAL and b"k_cache" in L.jl_last_error()
+    assert _pf_kc(0x1008, **ptrs)[0] == JL_EINVAL and b"k_cache" in L.jl_last_error()
+    # nothing to write: no tokens
+    assert _pf_kc(None, T=0, ws=0x1000, nbytes=0) == (JL_OK, 0)
+
+
 def _dec(**kw):
     a = dict(L=1000, Hq=32, Hkv=8, kvmap=None, d=128, dt=jl.BF16, w0=16, wpt=64, base=1e6, ws=None, nbytes=0)
     a.update(kw)

@@ -42,6 +42,11 @@ def test_prefill_good_structure_fails_on_device_only():
     ("cu_end", ValueError, "cu_seqlens"),
     ("q_2d", ValueError, "q must be"),
     ("q_int", TypeError, "unsupported dtype"),
+    ("kcache_shape", ValueError, "k_cache_out has shape"),
+    ("kcache_dtype", TypeError, "k_cache_out has dtype"),
+    ("kcache_alias_k", ValueError, "k_cache_out overlaps k"),
+    ("kcache_disjoint", ValueError, "three-pass form only"),
+    ("kcache_cpu", ValueError, "GPU tensor"),
 ])
 def test_prefill_rejects_bad_tensors(case, exc, msg):
     T, Hq, Hkv, d = 40, 4, 2, 128
@@ -71,6 +76,17 @@ def test_prefill_rejects_bad_tensors(case, exc, msg):
         q = q[0]
     elif case == "q_int":
         q = torch.zeros((T, Hq, d), dtype=torch.int16)
+    elif case == "kcache_shape":
+        kw["k_cache_out"] = torch.zeros((T, Hq, d), dtype=bf)
+    elif case == "kcache_dtype":
+        kw["k_cache_out"] = torch.zeros((T, Hkv, d), dtype=torch.float32)
+    elif case == "kcache_alias_k":
+        kw["k_cache_out"] = k
+    elif case == "kcache_disjoint":
+        kw["k_cache_out"] = torch.zeros((T, Hkv, d), dtype=bf)
+        kw["disjoint"] = True
+    elif case == "kcache_cpu":
+        kw["k_cache_out"] = torch.zeros((T, Hkv, d), dtype=bf)   # right structure: fails on the device check
     with pytest.raises(exc, match=msg):
         jl.prefill(q, k, v, **kw)
 

@@ -3,8 +3,9 @@ Methodology item 2: the cache holds keys rotated by base RoPE at their
 absolute positions; generation applies the correction rotation on the fly and
 never rewrites the cache, also when the length crosses a G boundary).
 
-The cache is built and extended with the library's base-RoPE row rotation
-(`jl_rope_rows`), the decode loop appends one token per step across
+The prompt's cache is written by the prefill itself (`jl_bifocal_prefill_kcache`,
+checked bitwise against `jl_rope_rows`), extended with the row rotation,
+the decode loop appends one token per step across
 L = 32768 -> 32769 (G 1 -> 2), and every step is checked against the last row
 of the fp64 oracle prefill at that length and against the library's own
 prefill."""
@@ -69,6 +70,61 @@ def test_rope_rows_alternating_bases_and_dims():
         assert max_abs(y, ref) <= 1e-5
 
 
+@pytest.mark.parametrize("dtype_name", ["bf16", "fp32"])
+def test_prefill_writes_the_decode_cache(dtype_name):
+    """Packed sequences with different G: the cache output of the prefill
+    holds, row for row, the base-rotated keys (bitwise the row rotation at
+    each sequence's positions, and the fp64 oracle's rotation within the
+    dtype's rounding), and the attention outputs are bitwise those of the
+    call without the cache output."""
+    jl, torch = gpu_or_skip()
+    dt = torch.bfloat16 if dtype_name == "bf16" else torch.float32
+    Hq, Hkv, d, w0, wpt, base = (4, 2, 128, 64, 256, 1e4)
+    lens = [300, 40, 1000, 513]                       # G = 2, 1, 4, 3
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    T = cu[-1]
+    g = torch.Generator("cpu").manual_seed(23)
+    q = torch.randn((T, Hq, d), generator=g).to(dt)
+    k = torch.randn((T, Hkv, d), generator=g).to(dt)
+    v = torch.randn((T, Hkv, d), generator=g).to(dt)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    kc = torch.full((T, Hkv, d), float("nan"), dtype=dt, device="cuda")
+    o1, l1 = jl.prefill(qd, kd, vd, w0=w0, w_pretrained=wpt, rope_base=base, cu_seqlens=cu, k_cache_out=kc)
+    o0, l0 = jl.prefill(qd, kd, vd, w0=w0, w_pretrained=wpt, rope_base=base, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    ib = torch.int16 if dt == torch.bfloat16 else torch.int32
+    assert torch.equal(o1.view(ib), o0.view(ib)) and torch.equal(l1, l0)
+    theta = oracle.rope_theta(d, base)
+    for b, n in enumerate(lens):
+        rows = kc[cu[b]:cu[b + 1]]
+        ref_bits = jl.rope_rows(kd[cu[b]:cu[b + 1]], 0, rope_base=base)
+        assert torch.equal(rows.view(ib), ref_bits.view(ib)), f"sequence {b}"
+        ref = oracle.rope(k[cu[b]:cu[b + 1]].double().numpy(), np.arange(n), theta)
+        got = rows.cpu().double().numpy()
+        err = np.abs(got - ref)
+        _say(f"[kcache] {dtype_name} seq {b} L={n} G={jl.group_size(n, wpt)}: max err {err.max():.2e}")
+        if dt == torch.bfloat16:
+            assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-6)   # one bf16 rounding of the rotated key
+        else:
+            assert err.max() <= 1e-5                               # fp32 rotation against fp64 angles
+    assert not torch.isnan(kc).any()                  # every row written
+
+
+def test_prefill_cache_output_rejects():
+    jl, torch = gpu_or_skip()
+    q = torch.zeros((64, 4, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((64, 2, 128), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros_like(k)
+    with pytest.raises(ValueError):                    # wrong shape
+        jl.prefill(q, k, v, w0=16, w_pretrained=32, rope_base=1e4, k_cache_out=torch.zeros_like(q))
+    with pytest.raises(ValueError):                    # the disjoint form has no cache output
+        jl.prefill(q, k, v, w0=16, w_pretrained=32, rope_base=1e4, disjoint=True, k_cache_out=torch.zeros_like(k))
+    with pytest.raises(ValueError):                    # the cache output may not alias k
+        jl.prefill(q, k, v, w0=16, w_pretrained=32, rope_base=1e4, k_cache_out=k)
+
+
 def test_rope_rows_empty_and_rejects():
     jl, torch = gpu_or_skip()
     x = torch.zeros((0, 2, 128), dtype=torch.bfloat16, device="cuda")
@@ -94,14 +150,21 @@ def test_streaming_chain_across_g_boundary():
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     assert jl.group_size(32768, wpt) == 1 and jl.group_size(32769, wpt) == 2
 
-    # prefill of the prompt, and the cache of its base-rotated keys
+    # prefill of the prompt, writing the cache of its base-rotated keys on the way
     cap = L_end + 3
     k_cache = torch.zeros((cap, Hkv, d), dtype=torch.bfloat16, device="cuda")
     v_cache = torch.zeros((cap, Hkv, d), dtype=torch.bfloat16, device="cuda")
-    jl.rope_rows(kd[:L0], 0, rope_base=base, out=k_cache[:L0])
     v_cache[:L0] = vd[:L0]
-    o_pf, _ = jl.prefill(qd[:L0], kd[:L0], vd[:L0], w0=w0, w_pretrained=wpt, rope_base=base)
+    o_pf, lse_pf = jl.prefill(qd[:L0], kd[:L0], vd[:L0], w0=w0, w_pretrained=wpt, rope_base=base,
+                              k_cache_out=k_cache[:L0])
+    # the same cache rows from the row rotation, and the same attention without the cache output
+    k_rows = jl.rope_rows(kd[:L0], 0, rope_base=base)
+    o_plain, lse_plain = jl.prefill(qd[:L0], kd[:L0], vd[:L0], w0=w0, w_pretrained=wpt, rope_base=base)
     torch.cuda.synchronize()
+    assert torch.equal(k_cache[:L0].view(torch.int16), k_rows.view(torch.int16))
+    assert torch.equal(o_pf.view(torch.int16), o_plain.view(torch.int16))
+    assert torch.equal(lse_pf, lse_plain)
+    assert not k_cache[L0:].any()                      # nothing written past the prompt
     prompt_k, prompt_v = k_cache[:L0].clone(), v_cache[:L0].clone()
 
     ws = torch.empty(jl.decode_workspace_bytes(L_end, Hq, Hkv), dtype=torch.uint8, device="cuda")
