@@ -73,22 +73,39 @@ def test_head_map():
 
 def test_decode_equals_last_prefill_row():
     """decode(L) on the cache of base-rotated keys equals the last row of the
-    bifocal prefill at L (both from the library)."""
+    bifocal prefill at L: the oracle's last row, and the library's.  The
+    decode runs twice, on a cache rotated on the host (fp64, rounded to bf16)
+    and on the cache the library's prefill writes; each result is checked
+    against the oracle at the bf16 bars, and against the library's own
+    prefill row at twice them (two results each within the bar of the
+    oracle)."""
     jl, torch = gpu_or_skip()
     L, Hq, Hkv, w0, wpt, base = 1500, 8, 2, 200, 400, 1e6   # G = 4
     g = torch.Generator("cpu").manual_seed(11)
     q = torch.randn((L, Hq, 128), generator=g).bfloat16()
     k = torch.randn((L, Hkv, 128), generator=g).bfloat16()
     v = torch.randn((L, Hkv, 128), generator=g).bfloat16()
-    o_p, lse_p = jl.prefill(q.cuda(), k.cuda(), v.cuda(), w0=w0, w_pretrained=wpt, rope_base=base)
+    kc_lib = torch.empty((L, Hkv, 128), dtype=torch.bfloat16, device="cuda")
+    o_p, lse_p = jl.prefill(q.cuda(), k.cuda(), v.cuda(), w0=w0, w_pretrained=wpt, rope_base=base,
+                            k_cache_out=kc_lib)
     # cache and query rotated at absolute positions (fp64 on the host, rounded to bf16)
     th = oracle.rope_theta(128, base)
     kc = torch.from_numpy(oracle.rope(k.double().numpy(), np.arange(L), th)).bfloat16()
     qb = torch.from_numpy(oracle.rope(q[L - 1:L].double().numpy(), np.array([L - 1]), th)[0]).bfloat16()
-    o_d, lse_d = jl.decode(qb.cuda(), kc.cuda(), v.cuda(), L, w0=w0, w_pretrained=wpt, rope_base=base)
-    torch.cuda.synchronize()
-    assert max_abs(o_d.float().cpu().numpy(), o_p[L - 1].float().cpu().numpy()) <= 2 * BF16_O_ATOL
-    assert lse_rel_err(lse_d.cpu().numpy(), lse_p[:, L - 1].cpu().numpy()) <= 2 * BF16_LSE_RTOL
+    o_ref, lse_ref = oracle.prefill(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                    w0=w0, w_pretrained=wpt, rope_base=base, rows=[L - 1])
+    for name, cache in (("host-rotated cache", kc.cuda()), ("prefill-written cache", kc_lib)):
+        o_d, lse_d = jl.decode(qb.cuda(), cache, v.cuda(), L, w0=w0, w_pretrained=wpt, rope_base=base)
+        torch.cuda.synchronize()
+        od, ld = o_d.float().cpu().numpy(), lse_d.cpu().numpy()
+        e_o, e_l = max_abs(od, o_ref[0]), lse_rel_err(ld, lse_ref[:, 0])
+        print(f"[decode] {name}: vs oracle max|do|={e_o:.3e} lse rel={e_l:.3e}")
+        assert e_o <= BF16_O_ATOL and e_l <= BF16_LSE_RTOL
+        assert max_abs(od, o_p[L - 1].float().cpu().numpy()) <= 2 * BF16_O_ATOL
+        assert lse_rel_err(ld, lse_p[:, L - 1].cpu().numpy()) <= 2 * BF16_LSE_RTOL
+    # the library's prefill row itself, against the oracle
+    assert max_abs(o_p[L - 1].float().cpu().numpy(), o_ref[0]) <= BF16_O_ATOL
+    assert lse_rel_err(lse_p[:, L - 1].cpu().numpy(), lse_ref[:, 0]) <= BF16_LSE_RTOL
 
 
 def test_empty_cache_is_noop():
