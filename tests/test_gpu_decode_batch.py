@@ -164,3 +164,42 @@ def test_batch_max_sequences():
     torch.cuda.synchronize()
     _check_against_oracle(q, kc, vc, row0, lens, o.float().cpu().numpy(), lse.cpu().numpy(),
                           [b for b in range(64) if lens[b]], w0, wpt, base)
+
+
+def test_batch_decode_on_the_packed_prefill_cache():
+    """Packed varlen prefill that writes its keys' cache, then one batched
+    decode step per sequence straight on that packed cache (row0 =
+    cu_seqlens): each sequence's step at L = its length must equal the last
+    row of its prefill, against the fp64 oracle (bf16 bars) and against the
+    library's prefill row (twice the bars: both within the bar of the
+    oracle)."""
+    jl, torch = gpu_or_skip()
+    Hq, Hkv, d, w0, wpt, base = 8, 2, 128, 96, 300, 1e6
+    lens = [250, 700, 1200, 301]                       # G = 1, 3, 4, 2
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    T = cu[-1]
+    g = torch.Generator("cpu").manual_seed(29)
+    q = torch.randn((T, Hq, d), generator=g).bfloat16()
+    k = torch.randn((T, Hkv, d), generator=g).bfloat16()
+    v = torch.randn((T, Hkv, d), generator=g).bfloat16()
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    kc = torch.empty((T, Hkv, d), dtype=torch.bfloat16, device="cuda")
+    o_p, lse_p = jl.prefill(qd, kd, vd, w0=w0, w_pretrained=wpt, rope_base=base, cu_seqlens=cu, k_cache_out=kc)
+    # the newest query of each sequence, base-rotated at its position L_b - 1
+    qlast = torch.stack([jl.rope_rows(qd[cu[b + 1] - 1:cu[b + 1]], lens[b] - 1, rope_base=base)[0]
+                         for b in range(len(lens))])
+    o_d, lse_d = jl.decode_batch(qlast, kc, vd, lens, row0=cu[:-1], w0=w0, w_pretrained=wpt, rope_base=base)
+    torch.cuda.synchronize()
+    for b, n in enumerate(lens):
+        s0, s1 = cu[b], cu[b + 1]
+        oo, ll = oracle.prefill(q[s0:s1].double().numpy(), k[s0:s1].double().numpy(), v[s0:s1].double().numpy(),
+                                w0=w0, w_pretrained=wpt, rope_base=base, rows=[n - 1])
+        od, ld = o_d[b].float().cpu().numpy(), lse_d[b].cpu().numpy()
+        e_o, e_l = max_abs(od, oo[0]), lse_rel_err(ld, ll[:, 0])
+        _say(f"[prefill->batch] seq {b} L={n} G={jl.group_size(n, wpt)}: vs oracle max|do|={e_o:.3e} "
+             f"lse rel={e_l:.3e}")
+        assert e_o <= BF16_O_ATOL and e_l <= BF16_LSE_RTOL
+        assert max_abs(od, o_p[s1 - 1].float().cpu().numpy()) <= 2 * BF16_O_ATOL
+        assert lse_rel_err(ld, lse_p[:, s1 - 1].cpu().numpy()) <= 2 * BF16_LSE_RTOL
