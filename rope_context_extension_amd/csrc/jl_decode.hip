@@ -221,15 +221,34 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // the workgroup's sequence (uniform)
+  // The workgroup's sequence (uniform).  Sequence 0's fields are read at
+  // fixed offsets, with no load depending on another, so a single-sequence
+  // call has everything its first tile loads need after one round of
+  // argument loads (each dependent round costs a few hundred ns); a batch
+  // call searches the prefix sums and reads its sequence's fields again.
   int b = 0;
-  while (b + 1 < ds.nseq && (int)blockIdx.x >= ds.wg_begin[b + 1]) ++b;
-  const int L = ds.L[b], G = ds.G[b], w0 = ds.w0[b], nsub = ds.nsub;
-  const int nwg = ds.wg_begin[ds.nseq];
+  int L = ds.L[0], G = ds.G[0], w0 = ds.w0[0], wg_first = ds.wg_begin[0];
+  int64_t row0 = ds.row0[0];
+  int nsub = ds.nsub;
+  // An empty statement that takes these values keeps their loads (and those
+  // of the pointers and head counts the first tile loads use) ahead of the
+  // branch: otherwise the compiler merges the sequence-0 loads with the
+  // batch path's behind the nseq test, and sinks the rest to their uses, one
+  // dependent round later each.
+  asm volatile("" : "+s"(L), "+s"(G), "+s"(w0), "+s"(wg_first), "+s"(row0), "+s"(nsub), "+s"(Hq), "+s"(Hkv),
+               "+s"(q), "+s"(kc), "+s"(vc));
+  if (ds.nseq > 1) {
+    while (b + 1 < ds.nseq && (int)blockIdx.x >= ds.wg_begin[b + 1]) ++b;
+    L = ds.L[b];
+    G = ds.G[b];
+    w0 = ds.w0[b];
+    wg_first = ds.wg_begin[b];
+    row0 = ds.row0[b];
+  }
+  const int nwg = ds.wg_begin[JL_MAX_SEQS];          // the plan repeats the total past the last sequence
   q += (int64_t)b * Hq * D;
-  const int64_t row0 = ds.row0[b];
   const int i = L - 1;
-  const int c_begin = ((int)blockIdx.x - ds.wg_begin[b]) * nsub * SUB;
+  const int c_begin = ((int)blockIdx.x - wg_first) * nsub * SUB;
   const int nsc = min(nsub, (L - c_begin + SUB - 1) / SUB);     // sub-chunks holding keys: >= 1
 
   const int kl = lane & 15, gq = lane >> 4;        // column / row index, lane group
@@ -468,9 +487,12 @@ __global__ void __launch_bounds__(256) decode_reduce_kernel(const float* __restr
   __shared__ float4 red_a[4][4];
   const int slot = blockIdx.x, part = blockIdx.y, sq = blockIdx.z, tid = threadIdx.x;
   const int w_first = ds.wg_begin[sq];
-  const int nwg = ds.wg_begin[sq + 1] - w_first;     // this sequence's partials
+  int nwg = ds.wg_begin[sq + 1] - w_first;           // this sequence's partials
+  int stride = ds.wg_begin[JL_MAX_SEQS];             // the total, at a fixed offset
+  // the partials' addresses in the same round of argument loads as the
+  // counts (the compiler would load them behind the early return below)
+  asm volatile("" : "+s"(nwg), "+s"(stride), "+s"(part_ml), "+s"(part_o));
   if (nwg == 0) return;                               // L = 0: nothing to write
-  const int stride = ds.wg_begin[ds.nseq];
   const int lane = tid & 63, wave = tid >> 6;
   const int c4 = tid & 3, grp = tid >> 2;
   const float2* ml = (const float2*)part_ml + (int64_t)slot * stride + w_first;

@@ -121,7 +121,7 @@ hipError_t jl_launch_prefill_bf16(const JlPrefillWs& ws, void* o, float* lse, in
 struct JlDecSeqs {
   int32_t nseq;
   int32_t nsub;                        // 64-key sub-chunks per workgroup (one value per call)
-  int32_t wg_begin[JL_MAX_SEQS + 1];   // prefix sums of the workgroups per sequence
+  int32_t wg_begin[JL_MAX_SEQS + 1];   // prefix sums of the workgroups per sequence; entries nseq .. JL_MAX_SEQS hold the total
   int32_t L[JL_MAX_SEQS];              // cached keys, the query at L - 1
   int32_t G[JL_MAX_SEQS];
   int32_t w0[JL_MAX_SEQS];             // window, L when every key is base (w0 >= L or G = 1)
