@@ -30,8 +30,15 @@ COMMON = [
 ]
 
 
+# Per-source flags.  The decode kernels take their leading arguments in
+# scalar registers at wave launch (kernel-argument preloading, at most 14
+# dwords on gfx950): a decode step's first loads then wait for no load of a
+# kernel argument.
+EXTRA = {"jl_decode.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"]}
+
+
 def _compile(src: str, obj: str) -> None:
-    cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -198,11 +198,18 @@ __device__ inline void fill_trig(float2 (*tb)[TPITCH], float4* chain, float4 st,
 // Partial records, laid out for the merge (nwg: workgroups of the call):
 //   part_ml [Hq][nwg][2]    (max in log2 units, sum)
 //   part_o  [Hq][nwg][128]  unnormalised accumulator
+// The leading arguments (14 dwords: the most gfx950 preloads into scalar
+// registers at wave launch, with the library's decode source built for it)
+// are everything the first loads of a single-sequence call need: the
+// caches, the query, and sequence 0's first cache row and length, the
+// sub-chunk count, the head counts, the sequence count and G.  A wave then
+// issues its first loads without waiting for a kernel-argument load.
 template <int NG>
 __global__ void __launch_bounds__(NT) decode_split_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ kc, const __bf16* __restrict__ vc,
-    float* __restrict__ part_ml, float* __restrict__ part_o, int Hq, int Hkv, JlHeadMap hm,
-    JlDecSeqs ds, float scale_log2, JlFreqs fr) {
+    const __bf16* __restrict__ kc, const __bf16* __restrict__ vc, const __bf16* __restrict__ q,
+    int64_t row0_first, int L_first, int nsub, int Hkv, int Hq, int nseq, int G_first,
+    float* __restrict__ part_ml, float* __restrict__ part_o, JlHeadMap hm, JlDecSeqs ds, float scale_log2,
+    JlFreqs fr) {
   // Row pitches carry 16 bytes of padding: the 16 lanes of an LDS read pass
   // fetch the same columns of different rows, which then fall on distinct
   // banks.
@@ -221,30 +228,23 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // The workgroup's sequence (uniform).  Sequence 0's fields are read at
-  // fixed offsets, with no load depending on another, so a single-sequence
-  // call has everything its first tile loads need after one round of
-  // argument loads (each dependent round costs a few hundred ns); a batch
-  // call searches the prefix sums and reads its sequence's fields again.
+  // The workgroup's sequence (uniform).  Sequence 0's first row, length and
+  // G come as arguments (its workgroups start at 0); a batch call searches
+  // the prefix sums and reads its sequence's fields.
   int b = 0;
-  int L = ds.L[0], G = ds.G[0], w0 = ds.w0[0], wg_first = ds.wg_begin[0];
-  int64_t row0 = ds.row0[0];
-  int nsub = ds.nsub;
-  // An empty statement that takes these values keeps their loads (and those
-  // of the pointers and head counts the first tile loads use) ahead of the
-  // branch: otherwise the compiler merges the sequence-0 loads with the
-  // batch path's behind the nseq test, and sinks the rest to their uses, one
-  // dependent round later each.
-  asm volatile("" : "+s"(L), "+s"(G), "+s"(w0), "+s"(wg_first), "+s"(row0), "+s"(nsub), "+s"(Hq), "+s"(Hkv),
-               "+s"(q), "+s"(kc), "+s"(vc));
-  if (ds.nseq > 1) {
-    while (b + 1 < ds.nseq && (int)blockIdx.x >= ds.wg_begin[b + 1]) ++b;
+  int L = L_first, G = G_first, wg_first = 0;
+  int64_t row0 = row0_first;
+  if (nseq > 1) {
+    while (b + 1 < nseq && (int)blockIdx.x >= ds.wg_begin[b + 1]) ++b;
     L = ds.L[b];
     G = ds.G[b];
-    w0 = ds.w0[b];
     wg_first = ds.wg_begin[b];
     row0 = ds.row0[b];
+    // resolved inside the branch: a load still pending where the two paths
+    // join would be waited for on the single-sequence path as well
+    asm volatile("" : "+s"(L), "+s"(G), "+s"(wg_first), "+s"(row0));
   }
+  const int w0 = ds.w0[b];                           // first needed after the first loads
   const int nwg = ds.wg_begin[JL_MAX_SEQS];          // the plan repeats the total past the last sequence
   q += (int64_t)b * Hq * D;
   const int i = L - 1;
@@ -477,21 +477,22 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
 constexpr int RED_GROUPS = 64;
 constexpr int RED_DEPTH = 8;
 
+// Leading arguments (preloaded like the split kernel's): the partials, their
+// stride (the call's workgroup count) and sequence 0's workgroup count.
 __global__ void __launch_bounds__(256) decode_reduce_kernel(const float* __restrict__ part_ml,
-                                                            const float* __restrict__ part_o, JlDecSeqs ds,
-                                                            int Hq, JlHeadMap hm,
+                                                            const float* __restrict__ part_o, int stride,
+                                                            int nwg_first, JlDecSeqs ds, int Hq, JlHeadMap hm,
                                                             __bf16* __restrict__ o,
                                                             float* __restrict__ lse) {
   __shared__ float red_m[RED_GROUPS];
   __shared__ float red_l[4];
   __shared__ float4 red_a[4][4];
   const int slot = blockIdx.x, part = blockIdx.y, sq = blockIdx.z, tid = threadIdx.x;
-  const int w_first = ds.wg_begin[sq];
-  int nwg = ds.wg_begin[sq + 1] - w_first;           // this sequence's partials
-  int stride = ds.wg_begin[JL_MAX_SEQS];             // the total, at a fixed offset
-  // the partials' addresses in the same round of argument loads as the
-  // counts (the compiler would load them behind the early return below)
-  asm volatile("" : "+s"(nwg), "+s"(stride), "+s"(part_ml), "+s"(part_o));
+  int w_first = 0, nwg = nwg_first;                  // this sequence's partials
+  if (sq > 0) {
+    w_first = ds.wg_begin[sq];
+    nwg = ds.wg_begin[sq + 1] - w_first;
+  }
   if (nwg == 0) return;                               // L = 0: nothing to write
   const int lane = tid & 63, wave = tid >> 6;
   const int c4 = tid & 3, grp = tid >> 2;
@@ -629,9 +630,9 @@ hipError_t jl_launch_decode_bf16(const void* q, const void* k_cache, const void*
   float* part_o = part_ml + (int64_t)nwg * Hq * 2;
   const float sl2 = scale * LOG2E;
 #define JL_DEC(NGV)                                                                          \
-  decode_split_kernel<NGV><<<nwg, NT, 0, st>>>((const __bf16*)q, (const __bf16*)k_cache,   \
-                                               (const __bf16*)v_cache, part_ml, part_o,     \
-                                               Hq, Hkv, hm, ds, sl2, fr)
+  decode_split_kernel<NGV><<<nwg, NT, 0, st>>>(                                             \
+      (const __bf16*)k_cache, (const __bf16*)v_cache, (const __bf16*)q, ds.row0[0], ds.L[0], ds.nsub, \
+      Hkv, Hq, ds.nseq, ds.G[0], part_ml, part_o, hm, ds, sl2, fr)
   switch (NG) {
     case 1: JL_DEC(1); break;
     case 2: JL_DEC(2); break;
@@ -643,6 +644,7 @@ hipError_t jl_launch_decode_bf16(const void* q, const void* k_cache, const void*
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (hipEvent_t mid = jl_profile_mid_event()) (void)hipEventRecord(mid, st);
-  decode_reduce_kernel<<<dim3(Hq, 8, ds.nseq), 256, 0, st>>>(part_ml, part_o, ds, Hq, hm, (__bf16*)o, lse);
+  decode_reduce_kernel<<<dim3(Hq, 8, ds.nseq), 256, 0, st>>>(part_ml, part_o, nwg, ds.wg_begin[1], ds, Hq, hm,
+                                                             (__bf16*)o, lse);
   return hipGetLastError();
 }
