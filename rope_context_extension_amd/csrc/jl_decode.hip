@@ -235,7 +235,13 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
   int L = L_first, G = G_first, wg_first = 0;
   int64_t row0 = row0_first;
   if (nseq > 1) {
-    while (b + 1 < nseq && (int)blockIdx.x >= ds.wg_begin[b + 1]) ++b;
+    // b = how many sequence starts after the first lie at or before this
+    // workgroup (the starts never decrease): lane k - 1 compares start k, so
+    // the search is one vector load and a ballot instead of one dependent
+    // argument load per sequence
+    const int k = lane + 1;
+    const int start = ds.wg_begin[min(k, JL_MAX_SEQS)];
+    b = __builtin_amdgcn_readfirstlane(__popcll(__ballot(k < nseq && (int)blockIdx.x >= start)));
     L = ds.L[b];
     G = ds.G[b];
     wg_first = ds.wg_begin[b];
