@@ -19,7 +19,9 @@ Prints ONE JSON line:
             ceiling); traffic comes from the committed counter summary when it
             was measured on the current kernel source;
   decode    sustained decode steps at 128K (KV bytes 2 L Hkv d 2 per step; both
-            kernels of a step, timed over back-to-back steps) against the HBM
+            kernels of a step, timed over back-to-back steps: the median of 3
+            batches after about 30 ms of warm-up steps, since a batch timed
+            from idle runs before the clocks have ramped up) against the HBM
             peak; decode_lengths: the same at 16K, 32K, 32769, 64K, 65537 and
             128K keys, bifocal and Delta-free (plain) side by side;
   prefill_configs  the other prefill workloads: Qwen3-1.7B heads at 32K (G=1)
@@ -296,19 +298,38 @@ def time_calls(ev, stream, fn, n, warm=2):
     return ev.elapsed_ms(a, b) / n
 
 
-def decode_length_timings(jl, torch, W, dev, ev, stream, lengths=None, plain=True):
+def time_steady(ev, stream, fn, n, reps=3, warm_ms=30.0):
+    """Median ms per call over `reps` batches of n back-to-back calls, after
+    about warm_ms of back-to-back warm-up calls.  The GPU clocks ramp up under
+    load: a batch of a few ms timed from idle reads 2-6% slow (decode steps
+    at 32K and 128K keys), and a decode loop in service runs at the ramped
+    clocks."""
+    probe = time_calls(ev, stream, fn, 8, warm=2)
+    for _ in range(int(warm_ms / max(probe, 1e-3))):
+        fn()
+    return float(statistics.median([time_calls(ev, stream, fn, n, warm=0) for _ in range(reps)]))
+
+
+def decode_length_timings(jl, torch, W, dev, ev, stream, lengths=None, plain=True, caches=None):
     """Decode steps (32 q / 8 kv heads, d = 128, w0 = 4096, w_pretrained = 32768) at each length over
-    2 GiB of distinct cache windows: bifocal and, with plain, Delta-free (w_pretrained = L: G = 1)."""
+    2 GiB of distinct cache windows: bifocal and, with plain, Delta-free (w_pretrained = L: G = 1).
+
+    caches = (pools, q, out, lse, workspace) reuses the headline run's cache pools, allocated when the
+    run starts, as a server allocates its KV cache."""
     lengths = W.DECODE_LENGTHS if lengths is None else lengths
     dcfg = W.decode_8b(CACHE_POOL_ROWS)
     Hq, Hkv, d = dcfg.num_q_heads, dcfg.num_kv_heads, dcfg.head_dim
-    gen = torch.Generator(device=dev).manual_seed(dcfg.seed + 1)
-    pools = [(torch.randn((CACHE_POOL_ROWS, Hkv, d), generator=gen, device=dev).bfloat16(),
-              torch.randn((CACHE_POOL_ROWS, Hkv, d), generator=gen, device=dev).bfloat16()) for _ in range(4)]
-    qd = torch.randn((Hq, d), generator=gen, device=dev).bfloat16()
-    od = torch.empty_like(qd)
-    lsed = torch.empty((Hq,), dtype=torch.float32, device=dev)
-    wsd = torch.empty(max(16, jl.decode_workspace_bytes(CACHE_POOL_ROWS, Hq, Hkv)), dtype=torch.uint8, device=dev)
+    if caches is None:
+        gen = torch.Generator(device=dev).manual_seed(dcfg.seed + 1)
+        pools = [(torch.randn((CACHE_POOL_ROWS, Hkv, d), generator=gen, device=dev).bfloat16(),
+                  torch.randn((CACHE_POOL_ROWS, Hkv, d), generator=gen, device=dev).bfloat16()) for _ in range(4)]
+        qd = torch.randn((Hq, d), generator=gen, device=dev).bfloat16()
+        od = torch.empty_like(qd)
+        lsed = torch.empty((Hq,), dtype=torch.float32, device=dev)
+        wsd = torch.empty(max(16, jl.decode_workspace_bytes(CACHE_POOL_ROWS, Hq, Hkv)), dtype=torch.uint8,
+                          device=dev)
+    else:
+        pools, qd, od, lsed, wsd = caches
     outd = {}
     for Lx in lengths:
         if not 1 <= Lx <= CACHE_POOL_ROWS:
@@ -322,8 +343,7 @@ def decode_length_timings(jl, torch, W, dev, ev, stream, lengths=None, plain=Tru
                                prepare=True)
                      for kc, vc in pools for w in range(CACHE_POOL_ROWS // Lx)]
             n = max(100, len(calls) * 4)
-            us = 1e3 * time_calls(ev, stream, lambda it=iter(range(10**9)): calls[next(it) % len(calls)](), n,
-                                  warm=len(calls))
+            us = 1e3 * time_steady(ev, stream, lambda it=iter(range(10**9)): calls[next(it) % len(calls)](), n)
             b = 2 * Lx * Hkv * d * 2
             row[key] = {"us_per_step": round(us, 2), "GB/s": round(b / (us * 1e-6) / 1e9, 1),
                         "frac_hbm": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
@@ -336,7 +356,8 @@ def decode_length_timings(jl, torch, W, dev, ev, stream, lengths=None, plain=Tru
             + (f", plain {row['plain']['us_per_step']} us" if plain else ""))
     del pools
     torch.cuda.synchronize()
-    torch.cuda.empty_cache()
+    if caches is None:
+        torch.cuda.empty_cache()
     return outd
 
 
@@ -517,8 +538,8 @@ def main():
     dec_in_step_us = float(np.mean([ev.elapsed_ms(r[5], r[7]) for r in recs])) * 1e3
 
     # sustained decode: back-to-back steps over the rotated cache windows
-    dec_us = 1e3 * time_calls(ev, stream, lambda it=iter(range(10**9)): head_calls[next(it) % len(head_calls)](),
-                              args.decode_steps, warm=4)
+    dec_us = 1e3 * time_steady(ev, stream, lambda it=iter(range(10**9)): head_calls[next(it) % len(head_calls)](),
+                               args.decode_steps)
     torch.cuda.synchronize()
 
     def run_extras():
@@ -567,9 +588,9 @@ def main():
 
         plain_ms = time_calls(ev, stream, prefill_plain, 3, warm=1)
         plain_calls = decode_steps(L, L)
-        dec_plain_us = 1e3 * time_calls(ev, stream,
-                                        lambda it=iter(range(10**9)): plain_calls[next(it) % len(plain_calls)](),
-                                        args.decode_steps, warm=8)
+        dec_plain_us = 1e3 * time_steady(ev, stream,
+                                         lambda it=iter(range(10**9)): plain_calls[next(it) % len(plain_calls)](),
+                                         args.decode_steps)
         torch.cuda.synchronize()
         dj = {"call_ms": round(dj_ms, 3), "tflops_actual": round(Fc / (dj_ms * 1e-3) / 1e12, 2),
               "frac_actual": round(Fc / (dj_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -597,20 +618,26 @@ def main():
         lb = torch.empty((len(lens), Hq), dtype=torch.float32, device=dev)
         step = jl.decode_batch(qb, kb_, vb, lens, row0=row0, w0=dcfg.w0, w_pretrained=dcfg.w_pretrained,
                                rope_base=dcfg.rope_base, out=ob, lse=lb, prepare=True)
-        us = 1e3 * time_calls(ev, stream, step, 50, warm=4)
+        us = 1e3 * time_steady(ev, stream, step, 50)
         torch.cuda.synchronize()
         kvb = 2 * sum(lens) * Hkv * d * 2
         log(f"[bench] batched decode of {len(lens)} sequences: {us:.1f} us per step ({kvb / us / 1e3:.0f} GB/s)")
         return {"lens": lens, "us_per_step": round(us, 2), "kv_bytes": kvb,
                 "GB/s": round(kvb / (us * 1e-6) / 1e9, 1), "frac_hbm": round(kvb / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
 
+    # Every HBM-bound leg runs before any large buffer goes back to the driver: for about 20 s after
+    # several GB are freed, every stream on the device runs slower (a 4 GiB read: 6.5 against 7.2 TB/s
+    # after a 40 GB free, whether its buffer was allocated before or after), which looks like the
+    # freed memory being cleared in the background.  The decode legs use the pools allocated at the
+    # start, as a server allocates its KV cache.
+    dl_obj = None if args.headline_only else decode_length_timings(jl, torch, W, dev, ev, stream,
+                                                                   caches=(pools, qd, od, lsed, wsd))
+    ceil = None if args.headline_only else measure_ceilings(jl, torch, dev, ev, stream)
     dj_obj, ov_obj = (None, None) if args.headline_only else run_extras()
     db_obj = None if args.headline_only else run_decode_batch()
     del q, k, v, o, ws, pools, head_calls
     torch.cuda.empty_cache()
-    dl_obj = None if args.headline_only else decode_length_timings(jl, torch, W, dev, ev, stream)
     pc_obj = None if args.headline_only else prefill_config_timings(jl, torch, W, dev, ev, stream)
-    ceil = None if args.headline_only else measure_ceilings(jl, torch, dev, ev, stream)
 
     tflops = F3 / (call_ms * 1e-3) / 1e12
     pass2_tflops = Fc / (pass2_ms * 1e-3) / 1e12
