@@ -475,33 +475,28 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
 }
 
 // Merge of the split-K partials through their LogSumExp statistics.
-// Workgroup (slot, part) produces 16 channels of one head: thread (grp,
-// c4) takes partials grp, grp + 64, ... (eight loads in flight per round,
-// 16 bytes of channels each) with an online max.  The 64 groups then meet
-// through lane exchanges: the common max over one lane per group, the
-// weighted sums over the 16 groups of a wave, and the 4 waves through LDS.
-constexpr int RED_GROUPS = 64;
-constexpr int RED_DEPTH = 8;
+// Workgroup (slot, part) is one wave and produces 16 channels of one head:
+// lane (grp, c4) takes partials grp, grp + 16, ... (sixteen loads in flight
+// per round, 16 bytes of channels each) with an online max, and the 16
+// groups meet through lane exchanges alone (no LDS, no workgroup barrier).
+constexpr int RED_GROUPS = 16;
+constexpr int RED_DEPTH = 16;
 
 // Leading arguments (preloaded like the split kernel's): the partials, their
 // stride (the call's workgroup count) and sequence 0's workgroup count.
-__global__ void __launch_bounds__(256) decode_reduce_kernel(const float* __restrict__ part_ml,
-                                                            const float* __restrict__ part_o, int stride,
-                                                            int nwg_first, JlDecSeqs ds, int Hq, JlHeadMap hm,
-                                                            __bf16* __restrict__ o,
-                                                            float* __restrict__ lse) {
-  __shared__ float red_m[RED_GROUPS];
-  __shared__ float red_l[4];
-  __shared__ float4 red_a[4][4];
-  const int slot = blockIdx.x, part = blockIdx.y, sq = blockIdx.z, tid = threadIdx.x;
+__global__ void __launch_bounds__(64) decode_reduce_kernel(const float* __restrict__ part_ml,
+                                                           const float* __restrict__ part_o, int stride,
+                                                           int nwg_first, JlDecSeqs ds, int Hq, JlHeadMap hm,
+                                                           __bf16* __restrict__ o,
+                                                           float* __restrict__ lse) {
+  const int slot = blockIdx.x, part = blockIdx.y, sq = blockIdx.z, lane = threadIdx.x;
   int w_first = 0, nwg = nwg_first;                  // this sequence's partials
   if (sq > 0) {
     w_first = ds.wg_begin[sq];
     nwg = ds.wg_begin[sq + 1] - w_first;
   }
   if (nwg == 0) return;                               // L = 0: nothing to write
-  const int lane = tid & 63, wave = tid >> 6;
-  const int c4 = tid & 3, grp = tid >> 2;
+  const int c4 = lane & 3, grp = lane >> 2;
   const float2* ml = (const float2*)part_ml + (int64_t)slot * stride + w_first;
   const float* po = part_o + ((int64_t)slot * stride + w_first) * D + part * 16 + c4 * 4;
   float m = -INFINITY, l = 0.f;
@@ -529,37 +524,28 @@ __global__ void __launch_bounds__(256) decode_reduce_kernel(const float* __restr
     }
     m = mu;
   }
-  if (c4 == 0) red_m[grp] = m;
-  __syncthreads();
-  float M = red_m[lane];                       // group 0 holds partial 0: M is finite
+  float M = m;                                  // groups without partials hold -inf; group 0 has partial 0
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  for (int off = 4; off <= 32; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
   const float wt = __builtin_amdgcn_exp2f(m - M);   // 0 for groups without partials
   l *= wt;
   acc.x *= wt; acc.y *= wt; acc.z *= wt; acc.w *= wt;
 #pragma unroll
-  for (int off = 4; off <= 32; off <<= 1) {      // the wave's 16 groups (lane bits 2..5)
+  for (int off = 4; off <= 32; off <<= 1) {      // the 16 groups (lane bits 2..5)
     l += __shfl_xor(l, off, 64);
     acc.x += __shfl_xor(acc.x, off, 64);
     acc.y += __shfl_xor(acc.y, off, 64);
     acc.z += __shfl_xor(acc.z, off, 64);
     acc.w += __shfl_xor(acc.w, off, 64);
   }
-  if (lane < 4) red_a[wave][lane] = acc;
-  if (lane == 0) red_l[wave] = l;
-  __syncthreads();
-  if (tid < 16) {
-    const int cc = tid >> 2, e = tid & 3;   // channel part*16 + 4 cc + e
-    float A = 0.f, Lt = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float4 a = red_a[w][cc];
-      A += e == 0 ? a.x : e == 1 ? a.y : e == 2 ? a.z : a.w;
-      Lt += red_l[w];
-    }
+  if (lane < 4) {                                // lane c4 holds channels part * 16 + 4 c4 .. + 3
     const int head = hm.head_of_slot[slot];
-    o[((int64_t)sq * Hq + head) * D + part * 16 + tid] = (__bf16)(A / Lt);
-    if (lse != nullptr && part == 0 && tid == 0) lse[(int64_t)sq * Hq + head] = (M + __log2f(Lt)) * LN2;
+    __bf16* dst = o + ((int64_t)sq * Hq + head) * D + part * 16 + 4 * c4;
+    dst[0] = (__bf16)(acc.x / l);
+    dst[1] = (__bf16)(acc.y / l);
+    dst[2] = (__bf16)(acc.z / l);
+    dst[3] = (__bf16)(acc.w / l);
+    if (lse != nullptr && part == 0 && lane == 0) lse[(int64_t)sq * Hq + head] = (M + __log2f(l)) * LN2;
   }
 }
 
@@ -650,7 +636,7 @@ hipError_t jl_launch_decode_bf16(const void* q, const void* k_cache, const void*
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (hipEvent_t mid = jl_profile_mid_event()) (void)hipEventRecord(mid, st);
-  decode_reduce_kernel<<<dim3(Hq, 8, ds.nseq), 256, 0, st>>>(part_ml, part_o, nwg, ds.wg_begin[1], ds, Hq, hm,
+  decode_reduce_kernel<<<dim3(Hq, 8, ds.nseq), 64, 0, st>>>(part_ml, part_o, nwg, ds.wg_begin[1], ds, Hq, hm,
                                                              (__bf16*)o, lse);
   return hipGetLastError();
 }
