@@ -62,6 +62,14 @@ int jl_test_device_shape(int32_t* cus, int32_t* xcds);
    a length outside 0 .. 2^31 - 1. */
 int jl_test_decode_plan(const int64_t* lens, int32_t num_seqs, int32_t cus, int32_t* nsub, int32_t* nwg);
 
+/* The same plan's workgroup prefix sums: wg_begin[b] = first split workgroup
+   of sequence b, for b = 0 .. JL_MAX_SEQS (JL_MAX_SEQS + 1 entries, written
+   by the call).  The decode kernels rely on two properties of it: the entries
+   never decrease (a workgroup finds its sequence by counting the starts at
+   or before it), and every entry from num_seqs on holds the total workgroup
+   count (read at a fixed offset).  Same errors as jl_test_decode_plan. */
+int jl_test_decode_prefix(const int64_t* lens, int32_t num_seqs, int32_t cus, int32_t* wg_begin);
+
 /* Ceiling kernels for benchmarks: what the chip achieves on its own, the
    denominators beside the published peaks.
    jl_bench_mfma_peak: one workgroup of 8 waves per compute unit, each wave

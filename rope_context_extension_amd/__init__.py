@@ -106,6 +106,8 @@ def lib() -> ctypes.CDLL:
         L.jl_test_decode_plan.restype = c.c_int
         L.jl_test_decode_plan.argtypes = [c.POINTER(c.c_int64), c.c_int32, c.c_int32, c.POINTER(c.c_int32),
                                           c.POINTER(c.c_int32)]
+        L.jl_test_decode_prefix.restype = c.c_int
+        L.jl_test_decode_prefix.argtypes = [c.POINTER(c.c_int64), c.c_int32, c.c_int32, c.POINTER(c.c_int32)]
         _lib = L
     return _lib
 

@@ -513,6 +513,18 @@ JL_EXPORT int jl_test_decode_plan(const int64_t* lens, int32_t num_seqs, int32_t
   return JL_OK;
 }
 
+JL_EXPORT int jl_test_decode_prefix(const int64_t* lens, int32_t num_seqs, int32_t cus, int32_t* wg_begin) {
+  if (!lens || !wg_begin || num_seqs < 1 || num_seqs > JL_MAX_SEQS || cus < 1)
+    return fail(JL_EINVAL, "bad arguments");
+  int64_t row0[JL_MAX_SEQS] = {0};
+  for (int b = 0; b < num_seqs; ++b)
+    if (lens[b] < 0 || lens[b] > (int64_t)INT32_MAX) return fail(JL_EINVAL, "bad length");
+  JlDecSeqs ds;
+  jl_decode_plan(lens, row0, num_seqs, 0, 1, cus, &ds);
+  for (int b = 0; b <= JL_MAX_SEQS; ++b) wg_begin[b] = ds.wg_begin[b];
+  return JL_OK;
+}
+
 JL_EXPORT int jl_test_group_size_device(const int64_t* L, int64_t n, int64_t w_pretrained, int64_t* G_out,
                                         void* hip_stream) {
   if (n < 0 || w_pretrained < 1 || (n > 0 && (!L || !G_out))) return fail(JL_EINVAL, "bad arguments");

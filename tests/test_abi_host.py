@@ -4,6 +4,7 @@ before launching anything."""
 
 import ctypes
 
+import numpy as np
 import pytest
 
 import oracle
@@ -12,6 +13,7 @@ from jl_testutil import ensure_built, header_symbols
 jl = ensure_built()
 L = jl.lib()
 JL_OK, JL_EINVAL, JL_EUNSUPPORTED, JL_ENOSPC = 0, -1, -2, -3
+JL_MAX_SEQS = 64                 # include/jetlong.h
 
 
 def test_exports_every_declared_symbol():
@@ -299,6 +301,40 @@ def test_decode_plan_follows_the_compute_unit_count():
         assert nsub == 1 or sum(-(-n // (64 * (nsub - 1))) for n in (131072, 12345)) > cus
     bad = ctypes.c_int32()
     assert L.jl_test_decode_plan((ctypes.c_int64 * 1)(5), 1, 0, ctypes.byref(bad), ctypes.byref(bad)) == JL_EINVAL
+
+
+def test_decode_prefix_sums_support_the_kernels_search():
+    """The split kernel finds a workgroup's sequence by counting the sequence
+    starts after the first that lie at or before it (one ballot), and both
+    decode kernels read the total workgroup count from the last prefix-sum
+    slot.  Both rest on the plan's prefix sums: they never decrease, and
+    every entry from the sequence count on holds the total.  The count must
+    equal a linear search over the starts for every workgroup, also with
+    sequences of no keys (which own no workgroups)."""
+    rng = np.random.default_rng(7)
+    cases = [[131072], [0, 5, 0], [32769, 1, 64, 65], [0] * 7 + [100],
+             [int(x) for x in rng.integers(0, 200000, size=64)],
+             [int(x) for x in rng.integers(0, 3, size=40)]]
+    for lens in cases:
+        for cus in (256, 80, 7):
+            arr = (ctypes.c_int64 * len(lens))(*lens)
+            wb = (ctypes.c_int32 * (JL_MAX_SEQS + 1))()
+            assert L.jl_test_decode_prefix(arr, len(lens), cus, wb) == JL_OK, L.jl_last_error()
+            wb = list(wb)
+            nsub, nwg = _plan(lens, cus)
+            n = len(lens)
+            assert wb[0] == 0 and all(wb[i] <= wb[i + 1] for i in range(JL_MAX_SEQS))
+            assert all(wb[i] == nwg for i in range(n, JL_MAX_SEQS + 1))
+            for b in range(n):                   # each sequence owns its keys' workgroups
+                assert wb[b + 1] - wb[b] == -(-lens[b] // (64 * nsub))
+            for w in range(nwg):
+                lin = 0
+                while lin + 1 < n and w >= wb[lin + 1]:
+                    lin += 1
+                cnt = sum(1 for k in range(1, min(n, 65)) if w >= wb[k])
+                assert cnt == lin and lens[lin] > 0, (lens, cus, w)
+    bad = (ctypes.c_int32 * (JL_MAX_SEQS + 1))()
+    assert L.jl_test_decode_prefix((ctypes.c_int64 * 1)(-1), 1, 256, bad) == JL_EINVAL
 
 
 def test_device_shape_default_without_a_device():
