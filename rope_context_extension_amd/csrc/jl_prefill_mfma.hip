@@ -583,13 +583,15 @@ __global__ void __launch_bounds__(NT, 2) prefill_pass_kernel(PrefillArgs A, JlHe
 // Half-step h (h = 0 .. 2n+1 for n key tiles): group g is in phase
 // ph = h - g; an even phase 2k is the matrix phase of tile k (S(k), PV(k-1)),
 // an odd phase 2k+1 the softmax of tile k.  K_k is read in half-steps 2k and
-// 2k+1 and V_k in 2k+2 and 2k+3; both are copied into LDS two half-steps
-// ahead (issued at half-step 2k - 2 for K_k, 2k for V_k), so two buffers of
-// each suffice and the copies are waited for only at odd half-steps.
+// 2k+1 and V_k in 2k+2 and 2k+3.  Group B copies K_k into LDS at the start of
+// half-step 2k - 2 and group A copies V_k at the start of half-step 2k + 1,
+// each during its own softmax phase; each waits for its copies at the end of
+// an odd half-step, before the barrier ahead of the tile's first reader, so
+// two buffers of each suffice.
 constexpr int PP_NT = 512;
 constexpr int PP_BQ = 256;
-// the four waves of group A issue every copy (group B's softmax phase stays
-// free of memory instructions)
+// a tile's 16-byte pieces are spread over the four waves of the group that
+// copies it (group B the K tiles, group A the V^T tiles)
 constexpr int PP_K_PER_WAVE = (KT_PIECES + 3) / 4;   // 5
 constexpr int PP_V_PER_WAVE = (VT_PIECES + 3) / 4;   // 5
 constexpr int BUF_RSRC_WORD3 = 0x00020000;           // raw buffer, 32-bit data format
@@ -717,10 +719,10 @@ __device__ inline void pp_pv(const lds_char* vt, const bf16x8* p, int lane, f32x
 // is 0 and not applied); returns the sum of the fp32 values, accumulated in
 // four independent chains of plain adds.  The sum is not taken with
 // v_dot2c_f32_bf16 over the packed bf16 values: on gfx950 that instruction
-// waits for the matrix pipe, and issued beside the other wave's MFMAs it runs
-// about seven times slower than an add (measured: 38 cycles per dot2 against
-// 5.6 alone), which made this phase longer than the matrix phase it is meant
-// to hide behind.
+// waits for the matrix pipe, and issued beside another wave's MFMAs it ran
+// about seven times slower than an add in a micro-benchmark (38 cycles per
+// dot2 against 5.6 alone).  In this kernel the two forms timed the same; the
+// adds sum the fp32 weights exactly as they are, before their bf16 rounding.
 template <bool SHIFT>
 __device__ inline float pp_exp_tile(const f32x16* s, float shift, bf16x8* p) {
   float sum[4] = {0.f, 0.f, 0.f, 0.f};
