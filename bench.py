@@ -175,9 +175,14 @@ def cpu_model() -> str:
 
 
 def blas_threads() -> int:
+    """Threads of numpy's BLAS, which runs the oracle's products (the process's other pools, torch's
+    OpenMP pool among them, do no oracle work)."""
+    import numpy  # noqa: F401  (loads the BLAS whose pool is counted)
     try:
         import threadpoolctl
-        return sum(p.get("num_threads", 0) for p in threadpoolctl.threadpool_info()) or os.cpu_count()
+        n = [p.get("num_threads", 0) for p in threadpoolctl.threadpool_info()
+             if p.get("user_api") == "blas" and "numpy" in p.get("filepath", "")]
+        return max(n) if n else os.cpu_count()
     except Exception:
         return os.cpu_count()
 
