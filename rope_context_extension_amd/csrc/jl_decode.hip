@@ -198,10 +198,10 @@ __device__ inline void fill_trig(float2 (*tb)[TPITCH], float4* chain, float4 st,
 // Partial records, laid out for the merge (nwg: workgroups of the call):
 //   part_ml [Hq][nwg][2]    (max in log2 units, sum)
 //   part_o  [Hq][nwg][128]  unnormalised accumulator
-// The leading arguments (14 dwords: the most gfx950 preloads into scalar
-// registers at wave launch, with the library's decode source built for it)
-// are everything the first loads of a single-sequence call need: the
-// caches, the query, and sequence 0's first cache row and length, the
+// The leading arguments (14 dwords, the most gfx950 preloads into scalar
+// registers at wave launch; the library's build turns preloading on for
+// this file) are everything the first loads of a single-sequence call need:
+// the caches, the query, and sequence 0's first cache row and length, the
 // sub-chunk count, the head counts, the sequence count and G.  A wave then
 // issues its first loads without waiting for a kernel-argument load.
 template <int NG>

@@ -203,3 +203,48 @@ def test_batch_decode_on_the_packed_prefill_cache():
         assert e_o <= BF16_O_ATOL and e_l <= BF16_LSE_RTOL
         assert max_abs(od, o_p[s1 - 1].float().cpu().numpy()) <= 2 * BF16_O_ATOL
         assert lse_rel_err(ld, lse_p[:, s1 - 1].cpu().numpy()) <= 2 * BF16_LSE_RTOL
+
+
+def test_decode_past_one_round_of_partials():
+    """A sequence longer than 256 workgroups of the largest sub-chunk count
+    (256 x 65536 keys) leaves the merge more partials per head than it takes
+    in one round (256).  With w0 >= L every key takes the base path and no
+    position enters a score, so softmax attention over all keys must equal
+    the LSE merge of one batched call over two halves of the keys, whose
+    merges take one round each.  Planted keys (one per 65536-key workgroup,
+    scores about 9 to 12 above the others' unit spread) carry most of the
+    softmax mass, so the output depends on the weight of every partial."""
+    jl, torch = gpu_or_skip()
+    Hq, Hkv, d, base, wpt = 4, 1, 128, 1e6, 32768
+    L = 259 * 65536 - 5
+    L1 = 130 * 65536 + 12345                            # inside a workgroup's range
+    _say(f"[decode-long] L={L} halves {L1} + {L - L1}")
+    g = torch.Generator(device="cuda").manual_seed(61)
+    q = torch.randn((Hq, d), generator=g, device="cuda")
+    kc = torch.randn((L, Hkv, d), generator=g, device="cuda").bfloat16()
+    vc = torch.randn((L, Hkv, d), generator=g, device="cuda").bfloat16()
+    qn = (q / q.norm(dim=1, keepdim=True)).sum(0)       # scores about c for every head
+    for w in range(259):
+        j = 65536 * w + (1000 + 37 * w) % 60000
+        c = 9.0 + 0.75 * ((7 * w) % 5)
+        kc[j, 0] = (c * qn).bfloat16()
+        vc[j, 0] = torch.randn((d,), generator=g, device="cuda").bfloat16()
+    qb = q.bfloat16()
+    kw = dict(w0=L, w_pretrained=wpt, rope_base=base)
+    o, lse = jl.decode(qb, kc, vc, L, **kw)
+    oh, lh = jl.decode_batch(torch.stack([qb, qb]), kc, vc, [L1, L - L1], row0=[0, L1], **kw)
+    torch.cuda.synchronize()
+    oh, lh = oh.double().cpu(), lh.double().cpu()
+    M = lh.max(dim=0).values
+    z = torch.exp(lh - M)                               # [2, Hq]
+    o_ref = (z[:, :, None] * oh).sum(0) / z.sum(0)[:, None]
+    lse_ref = M + torch.log(z.sum(0))
+    og, lg = o.double().cpu(), lse.double().cpu()
+    e_o = (og - o_ref).abs().max().item()
+    e_l = (lg - lse_ref).abs().max().item()
+    scale_o = o_ref.abs().max().item()
+    _say(f"[decode-long] max|O| {scale_o:.3f}, max|dO| {e_o:.2e}, max|dlse| {e_l:.2e}, "
+         f"half masses {z[0].mean().item():.3f} / {z[1].mean().item():.3f}")
+    assert 0.1 < scale_o < 10.0                         # the planted keys dominate the output (0.265 seen)
+    assert e_o <= 1e-2 * scale_o                        # two bf16 roundings of the halves, one of the whole
+    assert e_l <= 1e-4                                  # fp32 sums over 17M keys, natural-log units
