@@ -60,6 +60,12 @@ def test_qwen3_8b_decode_lengths(L):
     (777, 3, 3, 100, 256),       # odd kv-head count: a wave with one kv head
     (129, 8, 1, 20, 40),         # one kv head, 8 q heads per kv head, G = 4
     (2000, 64, 8, 200, 600),     # 64 q heads, G = 4
+    # the angle table steps over 8 keys by floor(8 / G) - 8 or that plus one:
+    # G = 8 (a step of 1), G = 9 and larger (a step of 0)
+    (2000, 4, 2, 50, 250),       # G = 8
+    (2000, 4, 2, 50, 223),       # G = 9
+    (3000, 8, 2, 100, 130),      # G = 24
+    (70000, 8, 2, 4096, 1000),   # G = 70, many sub-chunks per workgroup
 ])
 def test_small_decode_cases(L, Hq, Hkv, w0, wpt):
     jl, torch = gpu_or_skip()

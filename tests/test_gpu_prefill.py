@@ -108,6 +108,8 @@ def test_fp32_varlen_and_head_map():
     (129, 2, 1, 33, 40),           # tile edges
     (64, 2, 1, 10, 16),
     (2, 2, 1, 1, 1),
+    (1000, 2, 1, 50, 60),          # G = 17
+    (2300, 4, 2, 300, 100),        # G = 23, ragged tail
 ])
 def test_bf16_full_rows(L, Hq, Hkv, w0, wpt):
     jl, torch = gpu_or_skip()
