@@ -196,23 +196,29 @@ static int prefill_impl(const void* q, const void* k, const void* v, void* o, fl
   const size_t nq = (size_t)num_q_heads * pl.t_pad * head_dim * el;
   const size_t nk = (size_t)num_kv_heads * pl.t_pad * head_dim * el;
   size_t off = 0;
-  pl.off_qb = off; off += align256(nq);
-  pl.off_qr = off; if (pl.seqs.any_remote) off += align256(nq);
+  // the bf16 kernels rotate q themselves: only the fp32 path keeps rotated q
+  const bool q_in_ws = dtype != JL_BF16;
+  pl.off_qb = off; if (q_in_ws) off += align256(nq);
+  pl.off_qr = off; if (q_in_ws && pl.seqs.any_remote) off += align256(nq);
   pl.off_kb = off; off += align256(nk);
   pl.off_kr = off; if (pl.seqs.any_remote) off += align256(nk);
   pl.off_vt = off;
   if (dtype == JL_BF16) off += align256((size_t)num_kv_heads * head_dim * pl.seqs.vt_cols * el);
-  // split-operand residuals of the first JL_LO_ROWS positions (bf16 path)
+  // split-operand residuals of k's first JL_LO_ROWS positions (bf16 path; the
+  // kernels form q's residuals from q)
   const size_t lrows = (size_t)num_seqs * JL_LO_ROWS;
-  const size_t nqlo = (size_t)num_q_heads * lrows * head_dim * el;
   const size_t nklo = (size_t)num_kv_heads * lrows * head_dim * el;
-  pl.off_lo = off; if (dtype == JL_BF16) off += 2 * align256(nqlo) + 2 * align256(nklo);
-  // passes 1 and 2 hand (o_k, lse_k) to the pass-3 launch that merges them
+  pl.off_lo = off; if (dtype == JL_BF16) off += 2 * align256(nklo);
+  // passes 1 and 2 hand (o_k, lse_k) to the pass-3 launch that merges them;
+  // pass 1 only for the first JL_LO_ROWS rows (the 256-row kernel keeps its
+  // pass-1 output in LDS)
   const bool merge = dtype == JL_BF16 && pl.seqs.any_remote;
   const size_t no = align256((size_t)num_q_heads * total_tokens * head_dim * 4);
   const size_t nl = align256((size_t)num_q_heads * total_tokens * 4);
-  pl.off_o = off; if (merge) off += 2 * no;
-  pl.off_lse = off; if (merge) off += 2 * nl;
+  const size_t no1 = align256((size_t)num_q_heads * lrows * head_dim * 4);
+  const size_t nl1 = align256((size_t)num_q_heads * lrows * 4);
+  pl.off_o = off; if (merge) off += no1 + no;
+  pl.off_lse = off; if (merge) off += nl1 + nl;
   pl.total = total_tokens == 0 ? 0 : off;
 
   if (workspace == nullptr) {
@@ -233,47 +239,41 @@ static int prefill_impl(const void* q, const void* k, const void* v, void* o, fl
   hipStream_t st = (hipStream_t)hip_stream;
   char* wsb = (char*)workspace;
   JlPrefillWs ws;
-  ws.qb = wsb + pl.off_qb;
-  ws.qr = pl.seqs.any_remote ? (void*)(wsb + pl.off_qr) : ws.qb;
+  ws.qb = q_in_ws ? (void*)(wsb + pl.off_qb) : nullptr;
+  ws.qr = q_in_ws && pl.seqs.any_remote ? (void*)(wsb + pl.off_qr) : ws.qb;
   ws.kb = wsb + pl.off_kb;
   ws.kr = pl.seqs.any_remote ? (void*)(wsb + pl.off_kr) : ws.kb;
   ws.vt = dtype == JL_BF16 ? (void*)(wsb + pl.off_vt) : nullptr;
   ws.qb_lo = ws.qr_lo = ws.kb_lo = ws.kr_lo = nullptr;
   ws.kc = k_cache;
   {
-    const size_t no = align256((size_t)num_q_heads * total_tokens * head_dim * 4);
-    const size_t nl = align256((size_t)num_q_heads * total_tokens * 4);
+    const size_t lrows = (size_t)num_seqs * JL_LO_ROWS;
+    const size_t no1 = align256((size_t)num_q_heads * lrows * head_dim * 4);
+    const size_t nl1 = align256((size_t)num_q_heads * lrows * 4);
     ws.o1 = wsb + pl.off_o;
-    ws.o2 = wsb + pl.off_o + no;
+    ws.o2 = wsb + pl.off_o + no1;
     ws.lse1 = wsb + pl.off_lse;
-    ws.lse2 = wsb + pl.off_lse + nl;
+    ws.lse2 = wsb + pl.off_lse + nl1;
   }
   if (dtype == JL_BF16) {
     const size_t lrows = (size_t)num_seqs * JL_LO_ROWS;
-    const size_t nqlo = align256((size_t)num_q_heads * lrows * head_dim * el);
     const size_t nklo = align256((size_t)num_kv_heads * lrows * head_dim * el);
-    ws.qb_lo = wsb + pl.off_lo;
-    ws.qr_lo = wsb + pl.off_lo + nqlo;
-    ws.kb_lo = wsb + pl.off_lo + 2 * nqlo;
-    ws.kr_lo = wsb + pl.off_lo + 2 * nqlo + nklo;
-    if (!pl.seqs.any_remote) {   // remote grid == base grid: share the residuals too
-      ws.qr_lo = ws.qb_lo;
-      ws.kr_lo = ws.kb_lo;
-    }
+    ws.kb_lo = wsb + pl.off_lo;
+    ws.kr_lo = pl.seqs.any_remote ? (void*)(wsb + pl.off_lo + nklo) : ws.kb_lo;   // one grid: shared
   }
   ws.t_pad = pl.t_pad;
 
   // the bf16 kernels take q pre-multiplied by scale * log2(e)
   const float qscale = dtype == JL_BF16 ? scale * 1.4426950408889634f : 1.f;
-  hipError_t e = jl_launch_rope_prepass(q, k, ws, (int)el, total_tokens, num_q_heads, num_kv_heads,
-                                        head_dim, pl.seqs, fr, qscale, st);
+  hipError_t e = jl_launch_rope_prepass(q, k, ws, (int)el, total_tokens, q_in_ws ? num_q_heads : 0,
+                                        num_kv_heads, head_dim, pl.seqs, fr, qscale, st);
   if (e != hipSuccess) return hip_fail(e, "rope pre-pass launch");
   if (dtype == JL_BF16) {
     e = jl_launch_transpose_v(v, ws, pl.seqs, num_kv_heads, st);
     if (e != hipSuccess) return hip_fail(e, "v transpose launch");
     if (g_ev_before) (void)hipEventRecord(g_ev_before, st);
-    e = jl_launch_prefill_bf16(ws, o, lse, total_tokens, num_q_heads, num_kv_heads, hm, pl.seqs, w0,
-                               scale, pl.max_len, disjoint, st);
+    e = jl_launch_prefill_bf16(ws, q, fr, qscale, o, lse, total_tokens, num_q_heads, num_kv_heads, hm,
+                               pl.seqs, w0, scale, pl.max_len, disjoint, st);
     if (e != hipSuccess) return hip_fail(e, "bf16 prefill launch");
     if (g_ev_after) (void)hipEventRecord(g_ev_after, st);
   } else {

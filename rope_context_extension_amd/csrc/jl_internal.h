@@ -49,7 +49,9 @@ struct JlHeadMap {
 };
 
 // Workspace of the prefill path: rotated operands, head-major.
-//   qb, qr   [Hq][T_pad][d]   q rotated at p and at f(p)
+//   qb, qr   [Hq][T_pad][d]   q rotated at p and at f(p) (fp32 path only; the
+//            bf16 kernels rotate the caller's q rows themselves, and qb, qr,
+//            qb_lo, qr_lo are null there)
 //   kb, kr   [Hkv][T_pad][d]  k rotated at p and at f(p)
 //   vt       [Hkv][vt_cols / 64][d][64] v transposed in 64-key tiles (bf16
 //            path only); sequence b starts at key column vstart[b], a
@@ -57,7 +59,7 @@ struct JlHeadMap {
 //            of 64 are zero
 // Rows T .. T_pad-1 are zero.  qr / kr alias qb / kb when no sequence has
 // G > 1.
-//   qb_lo, qr_lo [Hq][nseq * JL_LO_ROWS][d], kb_lo, kr_lo [Hkv][nseq * JL_LO_ROWS][d]
+//   kb_lo, kr_lo [Hkv][nseq * JL_LO_ROWS][d]
 //            (bf16 path only) the rounding residuals bf16(x - bf16(x)) of the
 //            first JL_LO_ROWS positions of every sequence, row b * JL_LO_ROWS + p
 struct JlPrefillWs {
@@ -70,9 +72,10 @@ struct JlPrefillWs {
   void* qr_lo;
   void* kb_lo;
   void* kr_lo;
-  void* o1;      // [Hq][T][d] fp32: normalised pass-1 output (bf16 path, some G > 1)
+  void* o1;      // [Hq][nseq * JL_LO_ROWS][d] fp32: normalised pass-1 output of the first rows
+                 // (bf16 path, some G > 1; the 256-row kernel keeps its own in LDS)
   void* o2;      // [Hq][T][d] fp32: normalised pass-2 output
-  void* lse1;    // [Hq][T] fp32: pass-1 LogSumExp, log2 units
+  void* lse1;    // [Hq][nseq * JL_LO_ROWS] fp32: pass-1 LogSumExp of the first rows, log2 units
   void* lse2;    // [Hq][T] fp32: pass-2 LogSumExp, log2 units
   void* kc;      // [T][Hkv][d] dtype: base-rotated k in cache layout (optional output), or nullptr
   int64_t t_pad;
@@ -94,7 +97,8 @@ JlDevShape jl_device_shape();
 
 int64_t jl_prefill_t_pad(int64_t total_tokens);
 
-// rope pre-pass: writes qb, qr, kb, kr (elem = 2 for bf16, 4 for fp32); q is scaled by qscale
+// rope pre-pass: writes kb, kr and, for Hq > 0, qb, qr (elem = 2 for bf16, 4 for fp32; the bf16
+// path passes Hq = 0); q is scaled by qscale
 hipError_t jl_launch_rope_prepass(const void* q, const void* k, const JlPrefillWs& ws, int elem_bytes,
                                   int64_t total_tokens, int32_t Hq, int32_t Hkv, int32_t d,
                                   const JlSeqs& seqs, const JlFreqs& fr, float qscale, hipStream_t st);
@@ -111,9 +115,13 @@ hipError_t jl_launch_prefill_fp32(const JlPrefillWs& ws, const float* v, float* 
 
 // disjoint: rows >= 128 merge pass 1 with a far-only pass (pairs i - j >= w0)
 // instead of pass 2 minus pass 3
-hipError_t jl_launch_prefill_bf16(const JlPrefillWs& ws, void* o, float* lse, int64_t total_tokens,
-                                  int32_t Hq, int32_t Hkv, const JlHeadMap& hm, const JlSeqs& seqs,
-                                  int64_t w0, float scale, int32_t max_len, bool disjoint, hipStream_t st);
+// q: the caller's [T][Hq][128] bf16 query, rotated by the kernels themselves
+// (fr: the RoPE turn fractions; qscale: softmax scale * log2(e), folded into
+// q before its bf16 rounding)
+hipError_t jl_launch_prefill_bf16(const JlPrefillWs& ws, const void* q, const JlFreqs& fr, float qscale,
+                                  void* o, float* lse, int64_t total_tokens, int32_t Hq, int32_t Hkv,
+                                  const JlHeadMap& hm, const JlSeqs& seqs, int64_t w0, float scale,
+                                  int32_t max_len, bool disjoint, hipStream_t st);
 
 // decode: the sequences of one call, each with its own length, group size
 // and cache rows; workgroup w serves sequence b for wg_begin[b] <= w <

@@ -43,4 +43,14 @@ __device__ inline void jl_rope_sincos(int32_t p, uint64_t turn_frac, float* s, f
   const float y = (float)hi * (1.0f / 2147483648.0f);   // angle = pi * hi / 2^31
   sincospif(y, s, c);
 }
+
+// The rotation of one half-split pair (x1, x2) = (x[m], x[m + d/2]) by
+// (c, s) = (cos, sin) of its angle, with its fused multiply-adds written out:
+// every kernel that rotates the same input at the same position (the RoPE
+// pre-pass, the row rotation, the prefill kernels' query rotation) gets the
+// same bits.
+__device__ inline void jl_rot_pair(float x1, float x2, float c, float s, float* y1, float* y2) {
+  *y1 = __builtin_fmaf(x1, c, -(x2 * s));
+  *y2 = __builtin_fmaf(x2, c, x1 * s);
+}
 #endif

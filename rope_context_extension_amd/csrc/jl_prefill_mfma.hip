@@ -245,11 +245,6 @@ __device__ inline void softmax_exp(f32x16* s, PassState& st, float sl2, float nb
   st.l += sum;
 }
 
-__device__ inline void load_q(bf16x8* qf, const __bf16* rowp, int g) {
-#pragma unroll
-  for (int kb = 0; kb < 8; ++kb) qf[kb] = *(const bf16x8*)(rowp + kb * 16 + g * 8);
-}
-
 struct TileSrc {
   const char* k;       // K rows of (kv head, sequence), row-major 256 B rows
   const char* v;       // V^T tiles of (kv head, sequence), 16 KiB [128][64] blocks
@@ -387,28 +382,73 @@ __device__ inline bool block_item(const JlSched& sc, int Hq, int* h, int* b, int
 }
 
 struct PrefillArgs {
-  const __bf16* qb;
-  const __bf16* qr;
+  const __bf16* q;    // the caller's [T][Hq][128] query, rotated by the kernels (rope_q)
   const __bf16* kb;
   const __bf16* kr;
   const __bf16* vt;
-  const __bf16* qb_lo;
-  const __bf16* qr_lo;
   const __bf16* kb_lo;
   const __bf16* kr_lo;
   __bf16* out;        // [T][Hq][128] bf16
   float* lse;         // [Hq][T] or nullptr
-  float* o1;          // [Hq][T][128] fp32: normalised pass 1 output
+  float* o1;          // [Hq][nseq * JL_LO_ROWS][128] fp32: normalised pass 1 output of the first rows
   float* o2;          // [Hq][T][128] fp32: normalised pass 2 output
-  float* lse1;        // [Hq][T]: pass 1 LogSumExp (log2 units)
+  float* lse1;        // [Hq][nseq * JL_LO_ROWS]: pass 1 LogSumExp of the first rows (log2 units)
   float* lse2;        // [Hq][T]: pass 2 LogSumExp (log2 units)
   int64_t total;
   int64_t t_pad;
   int64_t w0;
   int Hq;
   int disjoint;       // far-only pass + window pass instead of the three passes (rows >= 128)
-  float sl2;          // factor from score products to log2 units (1: q arrives pre-scaled)
+  float sl2;          // factor from score products to log2 units (1: q is pre-scaled)
+  float qscale;       // softmax scale * log2(e), applied to q before its rotation and rounding
+  JlFreqs fr;         // RoPE turn fractions theta_m / (2 pi), 0.64 fixed point
 };
+
+// The lane's 64 channels of one query row in the MFMA B-operand layout
+// (qf[kb] holds channels kb * 16 + 8 g .. + 7, g = lane / 32), scaled by qscale,
+// rotated by RoPE at position pos and rounded to bf16: the arithmetic of the
+// RoPE pre-pass for k (technical summary on gist.science, Methodology item
+// 1: q and k rotated at their base or their aliased positions), so the
+// operands are those a pre-pass over q would have written.  Channel m < 64
+// of qf[kb] (kb < 4) and its pair partner m + 64 in qf[kb + 4] sit in the
+// same lane.  Rows past the sequence end (valid false) are zero.  With LO,
+// ql receives the rounding residuals bf16(y - bf16(y)), the split operands
+// of a sequence's first rows.
+template <bool LO>
+__device__ inline void rope_q(bf16x8* qf, bf16x8* ql, const __bf16* rowp, bool valid, int pos,
+                              const PrefillArgs& A, int g) {
+  bf16x8 x[8];
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb) x[kb] = *(const bf16x8*)(rowp + kb * 16 + g * 8);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float s, c;
+      const uint64_t tf = A.fr.turn_frac[kb * 16 + g * 8 + e];
+      if constexpr (LO) {
+        jl_rope_sincos(pos, tf, &s, &c);
+      } else {
+        // the hardware sine and cosine take the angle in turns, which the
+        // fixed-point angle already is (top 32 bits: a turn fraction in
+        // [-1/2, 1/2))
+        const float t = (float)(int32_t)(jl_angle_turns(pos, tf) >> 32) * (1.0f / 4294967296.0f);
+        s = __builtin_amdgcn_sinf(t);
+        c = __builtin_amdgcn_cosf(t);
+      }
+      const float x1 = valid ? (float)x[kb][e] * A.qscale : 0.f;
+      const float x2 = valid ? (float)x[kb + 4][e] * A.qscale : 0.f;
+      float y1, y2;
+      jl_rot_pair(x1, x2, c, s, &y1, &y2);
+      const __bf16 h1 = (__bf16)y1, h2 = (__bf16)y2;
+      qf[kb][e] = h1;
+      qf[kb + 4][e] = h2;
+      if constexpr (LO) {
+        ql[kb][e] = (__bf16)(y1 - (float)h1);
+        ql[kb + 4][e] = (__bf16)(y2 - (float)h2);
+      }
+    }
+}
 
 struct BlockCtx {
   int h, b, kvh, L, i0, w0, wave, lane, g;
@@ -453,11 +493,15 @@ __device__ inline bool make_ctx(const PrefillArgs& A, const JlHeadMap& hm, const
   return true;
 }
 
-template <bool PRECISE>
-__device__ inline void load_q_pair(bf16x8* qf, bf16x8* ql, const __bf16* q, const __bf16* q_lo,
-                                   const PrefillArgs& A, const BlockCtx& c) {
-  load_q(qf, q + ((int64_t)c.h * A.t_pad + c.s0 + c.wr.myrow) * D, c.g);
-  if constexpr (PRECISE) load_q(ql, q_lo + ((int64_t)c.h * c.lrows + c.lo_base + c.wr.myrow) * D, c.g);
+// The block's query row of this lane, rotated at its base (REMOTE false) or
+// aliased position; rows past the sequence end load row L - 1 and become zero.
+template <bool PRECISE, bool REMOTE>
+__device__ inline void load_q_pair(bf16x8* qf, bf16x8* ql, const PrefillArgs& A, const JlSeqs& seqs,
+                                   const BlockCtx& c) {
+  const bool valid = c.wr.myrow < c.L;
+  const int row = valid ? c.wr.myrow : c.L - 1;
+  const int pos = REMOTE ? jl_remote_pos(row, seqs.G[c.b]) : row;
+  rope_q<PRECISE>(qf, ql, A.q + ((c.s0 + row) * A.Hq + c.h) * D, valid, pos, A, c.g);
 }
 
 // o (unnormalised, lane holds channels db*32 + 8*(i/4) + 4*g + i%4 of its row)
@@ -497,8 +541,8 @@ __global__ void __launch_bounds__(NT, 2) prefill_pass_kernel(PrefillArgs A, JlHe
   if (ROLE == 2 && (c.only1 || c.only2)) return;
   bf16x8 qf[8];
   bf16x8 ql[FIRST ? 8 : 1];
-  if (ROLE == 1) load_q_pair<FIRST>(qf, ql, A.qb, A.qb_lo, A, c);
-  else load_q_pair<FIRST>(qf, ql, A.qr, A.qr_lo, A, c);
+  if (ROLE == 1) load_q_pair<FIRST, false>(qf, ql, A, seqs, c);
+  else load_q_pair<FIRST, true>(qf, ql, A, seqs, c);
   f32x16 o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16{};
@@ -509,6 +553,8 @@ __global__ void __launch_bounds__(NT, 2) prefill_pass_kernel(PrefillArgs A, JlHe
   const float l = st.l + __shfl_xor(st.l, 32, 64);
   if (c.wr.myrow >= c.L) return;
   const int64_t ridx = (int64_t)c.h * A.total + c.s0 + c.wr.myrow;
+  // pass 1's output of the first rows: [Hq][nseq * JL_LO_ROWS] rows
+  const int64_t lidx = (int64_t)c.h * c.lrows + c.lo_base + c.wr.myrow;
   if constexpr (ROLE != 2) {
     // lse_k in log2 units; an empty pass (w0 = 0 leaves pass 1 without keys)
     // has lse = -inf and weight 0 in the merge
@@ -518,7 +564,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_pass_kernel(PrefillArgs A, JlHe
       if (A.lse != nullptr && c.g == 0) A.lse[ridx] = lam * LN2;
       return;
     }
-    float* orow = (ROLE == 0 ? A.o2 : A.o1) + ridx * D;
+    float* orow = ROLE == 0 ? A.o2 + ridx * D : A.o1 + lidx * D;
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -527,10 +573,13 @@ __global__ void __launch_bounds__(NT, 2) prefill_pass_kernel(PrefillArgs A, JlHe
         *(float4*)(orow + db * 32 + 8 * q4 + 4 * c.g) =
             make_float4(o[db][4 * q4] * inv, o[db][4 * q4 + 1] * inv, o[db][4 * q4 + 2] * inv,
                         o[db][4 * q4 + 3] * inv);
-    if (c.g == 0) (ROLE == 0 ? A.lse2 : A.lse1)[ridx] = lam;
+    if (c.g == 0) {
+      if (ROLE == 0) A.lse2[ridx] = lam;
+      else A.lse1[lidx] = lam;
+    }
   } else {
     // ---- merge: M = max(lse_1, lse_2), z_k = 2^(lse_k - M) ----
-    const float lam1 = A.lse1[ridx];
+    const float lam1 = A.lse1[lidx];
     const float lam2 = A.lse2[ridx];
     const float lam3 = l > 0.f ? st.m + __log2f(l) : -INFINITY;
     const float M = fmaxf(lam1, lam2);
@@ -543,7 +592,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_pass_kernel(PrefillArgs A, JlHe
     const float far = z2 - z3;
     const float Z = z1 + fmaxf(far, 0.f);
     const float inv = 1.f / Z;
-    const float* o1row = A.o1 + ridx * D;
+    const float* o1row = A.o1 + lidx * D;
     const float* o2row = A.o2 + ridx * D;
     __bf16* orow = A.out + ((c.s0 + c.wr.myrow) * A.Hq + c.h) * D;
 #pragma unroll
@@ -1011,8 +1060,14 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
   T.plan = make_pp_dma(wave, lane);
   T.wave = wave;
   bf16x8 qf[8];
+  // this lane's query row (rows past the end: row L - 1's memory, zero
+  // operands) and its positions on the two grids
+  const bool q_valid = wr.myrow < L;
+  const int q_row = q_valid ? wr.myrow : L - 1;
+  const int q_rem = jl_remote_pos(q_row, __builtin_amdgcn_readfirstlane(seqs.G[b]));
+  const __bf16* q_src = A.q + ((s0 + q_row) * A.Hq + h) * D;
   if (live) {
-    load_q(qf, (BASE ? A.qb : A.qr) + ((int64_t)h * A.t_pad + s0 + wr.myrow) * D, g);
+    rope_q<false>(qf, nullptr, q_src, q_valid, BASE ? q_row : q_rem, A, g);
   } else {
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) qf[kb] = bf16x8{};
@@ -1108,7 +1163,7 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
     }
     // pass 3: the same window tiles with remote q/k
     T.rk = __builtin_amdgcn_make_buffer_rsrc((void*)(A.kr + krow), 0, 0x7fffffff, BUF_RSRC_WORD3);
-    if (live) load_q(qf, A.qr + ((int64_t)h * A.t_pad + s0 + wr.myrow) * D, g);
+    if (live) rope_q<false>(qf, nullptr, q_src, q_valid, q_rem, A, g);
 #pragma unroll
     for (int db = 0; db < 4; ++db) o[db] = f32x16{};
     st = PpState{-INFINITY, 0.f, f32x16{}};
@@ -1189,21 +1244,19 @@ void jl_build_sched(const JlSeqs& seqs, const JlHeadMap& hm, int Hq, int nxcd, J
   sc->xcd_heads = (Hq % sc->nxcd == 0) ? Hq / sc->nxcd : 0;
 }
 
-hipError_t jl_launch_prefill_bf16(const JlPrefillWs& ws, void* o, float* lse, int64_t total_tokens,
-                                  int32_t Hq, int32_t Hkv, const JlHeadMap& hm, const JlSeqs& seqs,
-                                  int64_t w0, float scale, int32_t max_len, bool disjoint, hipStream_t st) {
+hipError_t jl_launch_prefill_bf16(const JlPrefillWs& ws, const void* q, const JlFreqs& fr, float qscale,
+                                  void* o, float* lse, int64_t total_tokens, int32_t Hq, int32_t Hkv,
+                                  const JlHeadMap& hm, const JlSeqs& seqs, int64_t w0, float scale,
+                                  int32_t max_len, bool disjoint, hipStream_t st) {
   (void)Hkv;
   (void)max_len;
   JlSched sc;
   jl_build_sched(seqs, hm, Hq, jl_device_shape().xcds, &sc);
   PrefillArgs A;
-  A.qb = (const __bf16*)ws.qb;
-  A.qr = (const __bf16*)ws.qr;
+  A.q = (const __bf16*)q;
   A.kb = (const __bf16*)ws.kb;
   A.kr = (const __bf16*)ws.kr;
   A.vt = (const __bf16*)ws.vt;
-  A.qb_lo = (const __bf16*)ws.qb_lo;
-  A.qr_lo = (const __bf16*)ws.qr_lo;
   A.kb_lo = (const __bf16*)ws.kb_lo;
   A.kr_lo = (const __bf16*)ws.kr_lo;
   A.out = (__bf16*)o;
@@ -1217,8 +1270,10 @@ hipError_t jl_launch_prefill_bf16(const JlPrefillWs& ws, void* o, float* lse, in
   A.w0 = w0;
   A.Hq = Hq;
   A.disjoint = disjoint ? 1 : 0;
-  (void)scale;        // folded into q by the RoPE pre-pass (q * scale * log2 e)
+  (void)scale;        // folded into q with log2 e (qscale) before its rotation
   A.sl2 = 1.f;
+  A.qscale = qscale;
+  A.fr = fr;
   bool any_p1 = false, any_p2 = false, any_p3 = false, any_only2 = false;
   for (int b = 0; b < seqs.nseq; ++b) {
     if (seqs.len[b] == 0) continue;

@@ -19,13 +19,6 @@ namespace {
 template <typename T>
 __device__ inline float ld_f(const T* p) { return (float)(*p); }
 
-// The rotation of one half-split pair by (c, s), with its fused multiply-adds
-// written out: the pre-pass and the row rotation below give the same bits
-// for the same input and position, so a cache built by either matches.
-__device__ inline void rot_pair(float x1, float x2, float c, float s, float* y1, float* y2) {
-  *y1 = __builtin_fmaf(x1, c, -(x2 * s));
-  *y2 = __builtin_fmaf(x2, c, x1 * s);
-}
 template <typename T>
 __device__ inline void st_f(T* p, float x) { *p = (T)x; }
 
@@ -40,8 +33,11 @@ __device__ inline void st_split(T* hi, T* lo, float y) {
 
 // One thread per (token, frequency m); it rotates pair (m, m + d/2) of every
 // q and k head of that token with one sin/cos evaluation per grid.  q is
-// multiplied by qscale first (the bf16 path folds softmax scale * log2(e)
-// into q, so its score products come out in log2 units).  With kc set, the
+// multiplied by qscale first.  The bf16 path passes Hq = 0: its prefill
+// kernels rotate each query row themselves (scaled by softmax scale *
+// log2(e), with the same rotation and rounding), so q is never written to
+// the workspace; k, its split-operand residuals of the first positions and
+// the optional cache output are written here.  With kc set, the
 // base-rotated k is also written in the input's [T][Hkv][d] layout: the
 // decode cache of the same tokens (technical summary on gist.science,
 // Methodology item 2: the cache holds keys rotated at their absolute
@@ -77,7 +73,7 @@ __global__ void __launch_bounds__(256) rope_prepass_kernel(
   }
   if (p >= seqs.len[b]) {
     // residual rows past the end of a short sequence are zero
-    if (qb_lo != nullptr && p < JL_LO_ROWS) {
+    if (kb_lo != nullptr && p < JL_LO_ROWS) {
       const int64_t lrows = (int64_t)seqs.nseq * JL_LO_ROWS;
       const int64_t lrow = (int64_t)b * JL_LO_ROWS + p;
       for (int h = 0; h < Hq; ++h) {
@@ -101,7 +97,7 @@ __global__ void __launch_bounds__(256) rope_prepass_kernel(
   jl_rope_sincos(pos, fr.turn_frac[m], &sb, &cb);
   if (write_remote) jl_rope_sincos(jl_remote_pos(pos, seqs.G[b]), fr.turn_frac[m], &sr, &cr);
 
-  const bool lo = qb_lo != nullptr && pos < JL_LO_ROWS;
+  const bool lo = kb_lo != nullptr && pos < JL_LO_ROWS;
   const int64_t lrow = (int64_t)b * JL_LO_ROWS + pos;
   const int64_t lrows = (int64_t)seqs.nseq * JL_LO_ROWS;
   for (int h = 0; h < Hq; ++h) {
@@ -110,13 +106,13 @@ __global__ void __launch_bounds__(256) rope_prepass_kernel(
     float y1, y2;
     T* yb = qb + ((int64_t)h * t_pad + t) * d;
     T* lb = lo ? qb_lo + ((int64_t)h * lrows + lrow) * d : nullptr;
-    rot_pair(x1, x2, cb, sb, &y1, &y2);
+    jl_rot_pair(x1, x2, cb, sb, &y1, &y2);
     st_split(yb + m, lb ? lb + m : nullptr, y1);
     st_split(yb + m + half, lb ? lb + m + half : nullptr, y2);
     if (write_remote) {
       T* yr = qr + ((int64_t)h * t_pad + t) * d;
       T* lr = lo ? qr_lo + ((int64_t)h * lrows + lrow) * d : nullptr;
-      rot_pair(x1, x2, cr, sr, &y1, &y2);
+      jl_rot_pair(x1, x2, cr, sr, &y1, &y2);
       st_split(yr + m, lr ? lr + m : nullptr, y1);
       st_split(yr + m + half, lr ? lr + m + half : nullptr, y2);
     }
@@ -127,7 +123,7 @@ __global__ void __launch_bounds__(256) rope_prepass_kernel(
     float y1, y2;
     T* yb = kb + ((int64_t)h * t_pad + t) * d;
     T* lb = lo ? kb_lo + ((int64_t)h * lrows + lrow) * d : nullptr;
-    rot_pair(x1, x2, cb, sb, &y1, &y2);
+    jl_rot_pair(x1, x2, cb, sb, &y1, &y2);
     st_split(yb + m, lb ? lb + m : nullptr, y1);
     st_split(yb + m + half, lb ? lb + m + half : nullptr, y2);
     if (kc != nullptr) {
@@ -138,7 +134,7 @@ __global__ void __launch_bounds__(256) rope_prepass_kernel(
     if (write_remote) {
       T* yr = kr + ((int64_t)h * t_pad + t) * d;
       T* lr = lo ? kr_lo + ((int64_t)h * lrows + lrow) * d : nullptr;
-      rot_pair(x1, x2, cr, sr, &y1, &y2);
+      jl_rot_pair(x1, x2, cr, sr, &y1, &y2);
       st_split(yr + m, lr ? lr + m : nullptr, y1);
       st_split(yr + m + half, lr ? lr + m + half : nullptr, y2);
     }
@@ -169,7 +165,7 @@ __global__ void __launch_bounds__(256) rope_rows_kernel(const T* x, T* y, int64_
       T* yr = y + (r * H + h) * d;
       const float x1 = ld_f(xr + m), x2 = ld_f(xr + m + half);
       float y1, y2;
-      rot_pair(x1, x2, c, s, &y1, &y2);
+      jl_rot_pair(x1, x2, c, s, &y1, &y2);
       st_f(yr + m, y1);
       st_f(yr + m + half, y2);
     }
@@ -223,7 +219,7 @@ hipError_t jl_launch_rope_prepass(const void* q, const void* k, const JlPrefillW
   for (int b = 0; b < seqs.nseq; ++b) max_len = seqs.len[b] > max_len ? seqs.len[b] : max_len;
   const int64_t pad_rows = ws.t_pad - total_tokens;
   int64_t need = (max_len > pad_rows ? max_len : pad_rows);
-  if (ws.qb_lo != nullptr && need < JL_LO_ROWS) need = JL_LO_ROWS;
+  if (ws.kb_lo != nullptr && need < JL_LO_ROWS) need = JL_LO_ROWS;
   dim3 grid((unsigned)((need + tpb - 1) / tpb), (unsigned)(seqs.nseq + 1));
   const int wr = seqs.any_remote;
   if (elem_bytes == 2) {
