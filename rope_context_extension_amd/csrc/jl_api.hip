@@ -244,7 +244,7 @@ static int prefill_impl(const void* q, const void* k, const void* v, void* o, fl
   ws.kb = wsb + pl.off_kb;
   ws.kr = pl.seqs.any_remote ? (void*)(wsb + pl.off_kr) : ws.kb;
   ws.vt = dtype == JL_BF16 ? (void*)(wsb + pl.off_vt) : nullptr;
-  ws.qb_lo = ws.qr_lo = ws.kb_lo = ws.kr_lo = nullptr;
+  ws.kb_lo = ws.kr_lo = nullptr;
   ws.kc = k_cache;
   {
     const size_t lrows = (size_t)num_seqs * JL_LO_ROWS;

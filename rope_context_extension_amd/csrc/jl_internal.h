@@ -50,8 +50,8 @@ struct JlHeadMap {
 
 // Workspace of the prefill path: rotated operands, head-major.
 //   qb, qr   [Hq][T_pad][d]   q rotated at p and at f(p) (fp32 path only; the
-//            bf16 kernels rotate the caller's q rows themselves, and qb, qr,
-//            qb_lo, qr_lo are null there)
+//            bf16 kernels rotate the caller's q rows themselves, and qb, qr
+//            are null there)
 //   kb, kr   [Hkv][T_pad][d]  k rotated at p and at f(p)
 //   vt       [Hkv][vt_cols / 64][d][64] v transposed in 64-key tiles (bf16
 //            path only); sequence b starts at key column vstart[b], a
@@ -68,8 +68,6 @@ struct JlPrefillWs {
   void* kb;
   void* kr;
   void* vt;
-  void* qb_lo;
-  void* qr_lo;
   void* kb_lo;
   void* kr_lo;
   void* o1;      // [Hq][nseq * JL_LO_ROWS][d] fp32: normalised pass-1 output of the first rows

@@ -46,7 +46,7 @@ __device__ inline void st_split(T* hi, T* lo, float y) {
 template <typename T>
 __global__ void __launch_bounds__(256) rope_prepass_kernel(
     const T* __restrict__ q, const T* __restrict__ k, T* __restrict__ qb, T* __restrict__ qr,
-    T* __restrict__ kb, T* __restrict__ kr, T* __restrict__ qb_lo, T* __restrict__ qr_lo,
+    T* __restrict__ kb, T* __restrict__ kr,
     T* __restrict__ kb_lo, T* __restrict__ kr_lo, T* __restrict__ kc, int64_t total, int64_t t_pad, int Hq,
     int Hkv, int d, JlSeqs seqs, JlFreqs fr, int write_remote, float qscale) {
   const int half = d >> 1;
@@ -76,12 +76,6 @@ __global__ void __launch_bounds__(256) rope_prepass_kernel(
     if (kb_lo != nullptr && p < JL_LO_ROWS) {
       const int64_t lrows = (int64_t)seqs.nseq * JL_LO_ROWS;
       const int64_t lrow = (int64_t)b * JL_LO_ROWS + p;
-      for (int h = 0; h < Hq; ++h) {
-        st_f(qb_lo + ((int64_t)h * lrows + lrow) * d + m, 0.f);
-        st_f(qb_lo + ((int64_t)h * lrows + lrow) * d + m + half, 0.f);
-        st_f(qr_lo + ((int64_t)h * lrows + lrow) * d + m, 0.f);
-        st_f(qr_lo + ((int64_t)h * lrows + lrow) * d + m + half, 0.f);
-      }
       for (int h = 0; h < Hkv; ++h) {
         st_f(kb_lo + ((int64_t)h * lrows + lrow) * d + m, 0.f);
         st_f(kb_lo + ((int64_t)h * lrows + lrow) * d + m + half, 0.f);
@@ -105,16 +99,14 @@ __global__ void __launch_bounds__(256) rope_prepass_kernel(
     const float x1 = ld_f(x + m) * qscale, x2 = ld_f(x + m + half) * qscale;
     float y1, y2;
     T* yb = qb + ((int64_t)h * t_pad + t) * d;
-    T* lb = lo ? qb_lo + ((int64_t)h * lrows + lrow) * d : nullptr;
     jl_rot_pair(x1, x2, cb, sb, &y1, &y2);
-    st_split(yb + m, lb ? lb + m : nullptr, y1);
-    st_split(yb + m + half, lb ? lb + m + half : nullptr, y2);
+    st_f(yb + m, y1);
+    st_f(yb + m + half, y2);
     if (write_remote) {
       T* yr = qr + ((int64_t)h * t_pad + t) * d;
-      T* lr = lo ? qr_lo + ((int64_t)h * lrows + lrow) * d : nullptr;
       jl_rot_pair(x1, x2, cr, sr, &y1, &y2);
-      st_split(yr + m, lr ? lr + m : nullptr, y1);
-      st_split(yr + m + half, lr ? lr + m + half : nullptr, y2);
+      st_f(yr + m, y1);
+      st_f(yr + m + half, y2);
     }
   }
   for (int h = 0; h < Hkv; ++h) {
@@ -225,12 +217,12 @@ hipError_t jl_launch_rope_prepass(const void* q, const void* k, const JlPrefillW
   if (elem_bytes == 2) {
     rope_prepass_kernel<__bf16><<<grid, 256, 0, st>>>(
         (const __bf16*)q, (const __bf16*)k, (__bf16*)ws.qb, (__bf16*)ws.qr, (__bf16*)ws.kb,
-        (__bf16*)ws.kr, (__bf16*)ws.qb_lo, (__bf16*)ws.qr_lo, (__bf16*)ws.kb_lo,
+        (__bf16*)ws.kr, (__bf16*)ws.kb_lo,
         (__bf16*)ws.kr_lo, (__bf16*)ws.kc, total_tokens, ws.t_pad, Hq, Hkv, d, seqs, fr, wr, qscale);
   } else {
     rope_prepass_kernel<float><<<grid, 256, 0, st>>>(
         (const float*)q, (const float*)k, (float*)ws.qb, (float*)ws.qr, (float*)ws.kb,
-        (float*)ws.kr, nullptr, nullptr, nullptr, nullptr, (float*)ws.kc, total_tokens, ws.t_pad, Hq, Hkv,
+        (float*)ws.kr, nullptr, nullptr, (float*)ws.kc, total_tokens, ws.t_pad, Hq, Hkv,
         d, seqs, fr, wr, qscale);
   }
   return hipGetLastError();
