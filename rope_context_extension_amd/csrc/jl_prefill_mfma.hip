@@ -406,14 +406,16 @@ struct PrefillArgs {
 
 // The lane's 64 channels of one query row in the MFMA B-operand layout
 // (qf[kb] holds channels kb * 16 + 8 g .. + 7, g = lane / 32), scaled by qscale,
-// rotated by RoPE at position pos and rounded to bf16: the arithmetic of the
-// RoPE pre-pass for k (technical summary on gist.science, Methodology item
-// 1: q and k rotated at their base or their aliased positions), so the
-// operands are those a pre-pass over q would have written.  Channel m < 64
-// of qf[kb] (kb < 4) and its pair partner m + 64 in qf[kb + 4] sit in the
-// same lane.  Rows past the sequence end (valid false) are zero.  With LO,
-// ql receives the rounding residuals bf16(y - bf16(y)), the split operands
-// of a sequence's first rows.
+// rotated by RoPE at position pos and rounded to bf16 (technical summary on
+// gist.science, Methodology item 1: q and k rotated at their base or their
+// aliased positions), with the scaling, pair rotation and rounding of the
+// RoPE pre-pass for k.  Channel m < 64 of qf[kb] (kb < 4) and its pair
+// partner m + 64 in qf[kb + 4] sit in the same lane.  Rows past the sequence
+// end (valid false) are zero.  With LO (the split operands of a sequence's
+// first rows) ql receives the rounding residuals bf16(y - bf16(y)) and the
+// angles come from the pre-pass's exact sin/cos, so both are bitwise what a
+// pre-pass over q would write; otherwise from the hardware sine and cosine,
+// within 1.3e-7 of the exact values (far below q's bf16 rounding).
 template <bool LO>
 __device__ inline void rope_q(bf16x8* qf, bf16x8* ql, const __bf16* rowp, bool valid, int pos,
                               const PrefillArgs& A, int g) {

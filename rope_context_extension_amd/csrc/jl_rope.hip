@@ -35,7 +35,7 @@ __device__ inline void st_split(T* hi, T* lo, float y) {
 // q and k head of that token with one sin/cos evaluation per grid.  q is
 // multiplied by qscale first.  The bf16 path passes Hq = 0: its prefill
 // kernels rotate each query row themselves (scaled by softmax scale *
-// log2(e), with the same rotation and rounding), so q is never written to
+// log2(e), with the same pair rotation and rounding), so q is never written to
 // the workspace; k, its split-operand residuals of the first positions and
 // the optional cache output are written here.  With kc set, the
 // base-rotated k is also written in the input's [T][Hkv][d] layout: the
