@@ -26,7 +26,9 @@ Prints ONE JSON line:
             128K keys, bifocal and Delta-free (plain) side by side;
   prefill_configs  the other prefill workloads: Qwen3-1.7B heads at 32K (G=1)
             and 64K (G=2), and the Qwen3-4B varlen layer (8 sequences of
-            8K..128K) at w0 = 1024, 4096, 8192, each on both FLOP bases;
+            8K..128K) at w0 = 1024, 4096, 8192, each on both FLOP bases (the
+            median of 10 single calls after at least 3 and about 30 ms of
+            warm-up calls);
   ceilings  what the chip achieves on its own: dense bf16 MFMA issue only, and
             a streaming read (default and non-temporal cache policy);
   disjoint_merge  the same prefill with the far pairs computed directly (a
@@ -315,6 +317,26 @@ def time_steady(ev, stream, fn, n, reps=3, warm_ms=30.0):
     return float(statistics.median([time_calls(ev, stream, fn, n, warm=0) for _ in range(reps)]))
 
 
+def time_median(ev, stream, fn, n=10, warm=3, warm_ms=30.0):
+    """Median ms of n single calls of fn(), each between its own pair of events,
+    issued back to back after at least `warm` calls and about warm_ms of
+    warm-up.  A prefill call of a few ms timed from idle runs before the clocks
+    have ramped (the 32K prefill read 3.48-3.96 ms in one trace of four calls)."""
+    a, b = ev.create(), ev.create()
+    ev.record(a, stream)
+    fn()
+    ev.record(b, stream)
+    probe = ev.elapsed_ms(a, b)
+    for _ in range(max(warm - 1, int(warm_ms / max(probe, 1e-3)))):
+        fn()
+    es = [ev.create() for _ in range(n + 1)]
+    ev.record(es[0], stream)
+    for i in range(n):
+        fn()
+        ev.record(es[i + 1], stream)
+    return float(statistics.median([ev.elapsed_ms(es[i], es[i + 1]) for i in range(n)]))
+
+
 def decode_length_timings(jl, torch, W, dev, ev, stream, lengths=None, plain=True, caches=None):
     """Decode steps (32 q / 8 kv heads, d = 128, w0 = 4096, w_pretrained = 32768) at each length over
     2 GiB of distinct cache windows: bifocal and, with plain, Delta-free (w_pretrained = L: G = 1).
@@ -370,10 +392,11 @@ PREFILL_CONFIG_NAMES = ("qwen3_1.7b_L32768", "qwen3_1.7b_L65536", "qwen3_4b_varl
                         "qwen3_4b_varlen8_w04096", "qwen3_4b_varlen8_w08192")
 
 
-def prefill_config_timings(jl, torch, W, dev, ev, stream, names=PREFILL_CONFIG_NAMES, calls=3):
+def prefill_config_timings(jl, torch, W, dev, ev, stream, names=PREFILL_CONFIG_NAMES, calls=10):
     """Prefill throughput of the other prefill workloads: Qwen3-1.7B heads at 32K (G=1) and 64K (G=2),
     the Qwen3-4B varlen layer at w0 = 1024, 4096, 8192.  Inputs are drawn on the GPU (the timing does
-    not depend on the values)."""
+    not depend on the values).  Each figure is the median of `calls` single calls after at least three
+    warm-up calls and about 30 ms of warm-up."""
     known = {c.name: c for c in [W.QWEN3_1P7B_32K, W.QWEN3_1P7B_64K] + [W.varlen_4b(w) for w in (1024, 4096, 8192)]}
     res = {}
     for name in names:
@@ -396,7 +419,7 @@ def prefill_config_timings(jl, torch, W, dev, ev, stream, names=PREFILL_CONFIG_N
             jl.prefill(qx, kx, vx, w0=c.w0, w_pretrained=c.w_pretrained, rope_base=c.rope_base, cu_seqlens=cu,
                        out=ox, lse=lx, workspace=wsx)
 
-        ms = time_calls(ev, stream, call, calls, warm=1)
+        ms = time_median(ev, stream, call, calls)
         f3, fc = prefill_flops_varlen(c.seqlens, c.num_q_heads, c.head_dim, c.w0)
         gs = [jl.group_size(n, c.w_pretrained) for n in c.seqlens]
         res[c.name] = {"call_ms": round(ms, 3), "tflops_3pass": round(f3 / (ms * 1e-3) / 1e12, 2),
