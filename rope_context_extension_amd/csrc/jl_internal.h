@@ -72,7 +72,8 @@ struct JlPrefillWs {
   void* kr_lo;
   void* o1;      // [Hq][nseq * JL_LO_ROWS][d] fp32: normalised pass-1 output of the first rows
                  // (bf16 path, some G > 1; the 256-row kernel keeps its own in LDS)
-  void* o2;      // [Hq][T][d] fp32: normalised pass-2 output
+  void* o2;      // [Hq][T][d] fp32: normalised pass-2 output; the 256-row kernels keep each
+                 // full 32-row group of a wave in that wave's lane order
   void* lse1;    // [Hq][nseq * JL_LO_ROWS] fp32: pass-1 LogSumExp of the first rows, log2 units
   void* lse2;    // [Hq][T] fp32: pass-2 LogSumExp, log2 units
   void* kc;      // [T][Hkv][d] dtype: base-rotated k in cache layout (optional output), or nullptr

@@ -391,7 +391,7 @@ struct PrefillArgs {
   __bf16* out;        // [T][Hq][128] bf16
   float* lse;         // [Hq][T] or nullptr
   float* o1;          // [Hq][nseq * JL_LO_ROWS][128] fp32: normalised pass 1 output of the first rows
-  float* o2;          // [Hq][T][128] fp32: normalised pass 2 output
+  float* o2;          // [Hq][T][128] fp32: normalised pass 2 output (rows from JL_LO_ROWS on: see o2_slot)
   float* lse1;        // [Hq][nseq * JL_LO_ROWS]: pass 1 LogSumExp of the first rows (log2 units)
   float* lse2;        // [Hq][T]: pass 2 LogSumExp (log2 units)
   int64_t total;
@@ -416,12 +416,11 @@ struct PrefillArgs {
 // angles come from the pre-pass's exact sin/cos, so both are bitwise what a
 // pre-pass over q would write; otherwise from the hardware sine and cosine,
 // within 1.3e-7 of the exact values (far below q's bf16 rounding).
+// The rotation of the caller's bf16 channels x (x[kb]: channels kb * 16 + 8 g
+// .. + 7 of the row, as load_q_raw reads them).
 template <bool LO>
-__device__ inline void rope_q(bf16x8* qf, bf16x8* ql, const __bf16* rowp, bool valid, int pos,
-                              const PrefillArgs& A, int g) {
-  bf16x8 x[8];
-#pragma unroll
-  for (int kb = 0; kb < 8; ++kb) x[kb] = *(const bf16x8*)(rowp + kb * 16 + g * 8);
+__device__ inline void rotate_q(bf16x8* qf, bf16x8* ql, const bf16x8* x, bool valid, int pos,
+                                const PrefillArgs& A, int g) {
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -450,6 +449,19 @@ __device__ inline void rope_q(bf16x8* qf, bf16x8* ql, const __bf16* rowp, bool v
         ql[kb + 4][e] = (__bf16)(y2 - (float)h2);
       }
     }
+}
+
+__device__ inline void load_q_raw(bf16x8* x, const __bf16* rowp, int g) {
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb) x[kb] = *(const bf16x8*)(rowp + kb * 16 + g * 8);
+}
+
+template <bool LO>
+__device__ inline void rope_q(bf16x8* qf, bf16x8* ql, const __bf16* rowp, bool valid, int pos,
+                              const PrefillArgs& A, int g) {
+  bf16x8 x[8];
+  load_q_raw(x, rowp, g);
+  rotate_q<LO>(qf, ql, x, valid, pos, A, g);
 }
 
 struct BlockCtx {
@@ -711,6 +723,19 @@ __device__ inline void pp_wait_copies() {
 __device__ inline float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Output channels of a row in 16-byte pieces.  Lanes t and t + 32 (g = 0, 1)
+// hold the same row; for a slot pair (q4 = 2m, 2m + 1) lane g has channels
+// base + 4g .. + 3 of slot 2m in a and base + 8 + 4g .. + 3 of slot 2m + 1 in
+// b.  One swap of the upper half of a with the lower half of b gives lane g
+// the 8 channels base + 8g .. + 7, so that one 16-byte store per lane covers
+// 32 contiguous bytes of the row where two 8-byte stores covered 16.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ inline u32x4 pair_channels(u32x2 a, u32x2 b) {
+  const auto lo = __builtin_amdgcn_permlane32_swap(a[0], b[0], false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap(a[1], b[1], false, false);
+  return u32x4{lo[0], hi[0], lo[1], hi[1]};
 }
 
 __device__ inline float pair_sum(float x) {
@@ -997,14 +1022,27 @@ __device__ inline void pp_run(const PpTiles& T, const bf16x8* qf, PpState& st, f
 // output's own rounding.
 constexpr int O1_BYTES = PP_NT * 128;
 
-// The lane's 64 channels of an fp32 output row (channels db*32 + 8*q4 + 4*g
-// + 0..3 in slot 4*db + q4), all loads issued before any use: the merge
-// stores bf16 rows in between, and with the loads next to their uses the
-// compiler kept each behind the previous store (it cannot prove the two
-// arrays apart), one memory round trip per 16 bytes.
-__device__ inline void pp_load_row(float4* v, const float* row, int g) {
+// Pass 2's (or the far pass's) fp32 output of rows >= JL_LO_ROWS, as the
+// 256-row kernel writes and reads it.  slab is the wave's first row.  A lane
+// holds channels db*32 + 8*q4 + 4*g + 0..3 of its row in slot i = 4*db + q4.
+// When all 32 rows of the wave lie in the sequence, the slab's 16 KB are in
+// lane order instead of row order, slot i of lane t at (64 i + t) * 4 floats,
+// so that each store and load instruction covers 1 KB of contiguous memory
+// (row order puts 32 B of each of 32 rows in an instruction).  The last,
+// partial 32 rows of a sequence stay row-ordered: a lane-ordered slab would
+// run into the next rows.
+__device__ inline float* o2_slot(float* slab, int lane, int i, bool lane_order) {
+  return lane_order ? slab + (64 * i + lane) * 4
+                    : slab + (lane & 31) * D + (i >> 2) * 32 + 8 * (i & 3) + 4 * (lane >> 5);
+}
+
+// The lane's 16 slots, all loads issued before any use: the merge stores bf16
+// rows in between, and with the loads next to their uses the compiler kept
+// each behind the previous store (it cannot prove the two arrays apart), one
+// memory round trip per 16 bytes.
+__device__ inline void pp_load_row(float4* v, const float* slab, int lane, bool lane_order) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = *(const float4*)(row + (i >> 2) * 32 + 8 * (i & 3) + 4 * g);
+  for (int i = 0; i < 16; ++i) v[i] = *(const float4*)o2_slot((float*)slab, lane, i, lane_order);
 }
 
 // ROLE 0: pass 2 (full causal, remote q/k).  ROLE 3: passes 1 and 3 of the
@@ -1068,8 +1106,19 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
   const int q_row = q_valid ? wr.myrow : L - 1;
   const int q_rem = jl_remote_pos(q_row, __builtin_amdgcn_readfirstlane(seqs.G[b]));
   const __bf16* q_src = A.q + ((s0 + q_row) * A.Hq + h) * D;
+  // ROLE 3 rotates the same rows again for pass 3: the raw rows wait in the
+  // LDS area of pass 1's output, which pass 1 does not touch, each thread's
+  // 128 bytes where its own o1 chunks go (so no barrier is needed)
+  __attribute__((address_space(3))) bf16x8* const o1s =
+      (__attribute__((address_space(3))) bf16x8*)(lds + 2 * (KT_BYTES + VT_BYTES)) + tid;
   if (live) {
-    rope_q<false>(qf, nullptr, q_src, q_valid, BASE ? q_row : q_rem, A, g);
+    bf16x8 x[8];
+    load_q_raw(x, q_src, g);
+    if constexpr (ROLE == 3) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) o1s[c * PP_NT] = x[c];
+    }
+    rotate_q<false>(qf, nullptr, x, q_valid, BASE ? q_row : q_rem, A, g);
   } else {
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) qf[kb] = bf16x8{};
@@ -1091,33 +1140,39 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
   const float lam = l > 0.f ? st.m + __log2f(l) : -INFINITY;
   const int64_t ridx = (int64_t)h * A.total + s0 + wr.myrow;
   const bool row_ok = live && wr.myrow < L;
+  float* const o2_slab = A.o2 + ((int64_t)h * A.total + s0 + iw) * D;
+  const bool o2_lane_order = iw + 32 <= L;
   if (ROLE == 0 ? only2 : only1) {
     // the pass is the whole attention of the sequence
     if (!row_ok) return;
     __bf16* orow = A.out + ((s0 + wr.myrow) * A.Hq + h) * D;
     const float inv = 1.f / l;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int c = 0; c < 8; ++c) {
+      const int db = c >> 1;
+      u32x2 w[2];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        bf16x4 w;
+      for (int hq = 0; hq < 2; ++hq) {
+        const int q4 = 2 * (c & 1) + hq;
+        bf16x4 x;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[db][4 * q4 + e] * inv);
-        *(bf16x4*)(orow + db * 32 + 8 * q4 + 4 * g) = w;
+        for (int e = 0; e < 4; ++e) x[e] = (__bf16)(o[db][4 * q4 + e] * inv);
+        w[hq] = __builtin_bit_cast(u32x2, x);
       }
+      *(u32x4*)(orow + db * 32 + 16 * (c & 1) + 8 * g) = pair_channels(w[0], w[1]);
+    }
     if (A.lse != nullptr && g == 0) A.lse[ridx] = lam * LN2;
     return;
   }
   if constexpr (ROLE == 0 || ROLE == 4) {
     // rows without a far key (i < w0) store o = 0 and lam = -inf
     if (!row_ok) return;
-    float* orow = A.o2 + ridx * D;
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
-        *(float4*)(orow + db * 32 + 8 * q4 + 4 * g) =
+        *(float4*)o2_slot(o2_slab, lane, 4 * db + q4, o2_lane_order) =
             make_float4(o[db][4 * q4] * inv, o[db][4 * q4 + 1] * inv, o[db][4 * q4 + 2] * inv,
                         o[db][4 * q4 + 3] * inv);
     if (g == 0) A.lse2[ridx] = lam;
@@ -1131,30 +1186,36 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
     const float zf = __builtin_amdgcn_exp2f(lamf - M);
     const float Z = __builtin_amdgcn_exp2f(lam - M) + zf;
     const float inv = 1.f / Z;
-    const float* ofrow = A.o2 + ridx * D;
     __bf16* orow = A.out + ((s0 + wr.myrow) * A.Hq + h) * D;
     float4 vfs[16];
-    pp_load_row(vfs, ofrow, g);
+    pp_load_row(vfs, o2_slab, lane, o2_lane_order);
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int c = 0; c < 8; ++c) {
+      const int db = c >> 1;
+      u32x2 w[2];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = db * 32 + 8 * q4 + 4 * g;
+      for (int hq = 0; hq < 2; ++hq) {
+        const int q4 = 2 * (c & 1) + hq;
         const float4 vf = vfs[4 * db + q4];
         const float ofv[4] = {vf.x, vf.y, vf.z, vf.w};
-        bf16x4 w;
+        bf16x4 x;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (__bf16)((c1 * o[db][4 * q4 + e] + zf * ofv[e]) * inv);
-        *(bf16x4*)(orow + d0) = w;
+        for (int e = 0; e < 4; ++e) x[e] = (__bf16)((c1 * o[db][4 * q4 + e] + zf * ofv[e]) * inv);
+        w[hq] = __builtin_bit_cast(u32x2, x);
       }
+      *(u32x4*)(orow + db * 32 + 16 * (c & 1) + 8 * g) = pair_channels(w[0], w[1]);
+    }
     if (A.lse != nullptr && g == 0) A.lse[ridx] = (M + __log2f(Z)) * LN2;
   } else {
     // pass 1 done: o1 (normalised, bf16) to LDS, lam1 stays in a register
     const float lam1 = lam;
+    bf16x8 x[8];
+    if (live) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) x[c] = o1s[c * PP_NT];
+    }
     {
       const float inv = l > 0.f ? 1.f / l : 0.f;
-      __attribute__((address_space(3))) bf16x8* o1s =
-          (__attribute__((address_space(3))) bf16x8*)(lds + 2 * (KT_BYTES + VT_BYTES)) + tid;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         bf16x8 w;
@@ -1165,7 +1226,7 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
     }
     // pass 3: the same window tiles with remote q/k
     T.rk = __builtin_amdgcn_make_buffer_rsrc((void*)(A.kr + krow), 0, 0x7fffffff, BUF_RSRC_WORD3);
-    if (live) rope_q<false>(qf, nullptr, q_src, q_valid, q_rem, A, g);
+    if (live) rotate_q<false>(qf, nullptr, x, q_valid, q_rem, A, g);
 #pragma unroll
     for (int db = 0; db < 4; ++db) o[db] = f32x16{};
     st = PpState{-INFINITY, 0.f, f32x16{}};
@@ -1182,29 +1243,28 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
     const float far = z2 - z3;
     const float Z = z1 + fmaxf(far, 0.f);
     const float inv = 1.f / Z;
-    const float* o2row = A.o2 + ridx * D;
     float4 v2s[16];
-    pp_load_row(v2s, o2row, g);
-    const __attribute__((address_space(3))) bf16x8* o1s =
-        (const __attribute__((address_space(3))) bf16x8*)(lds + 2 * (KT_BYTES + VT_BYTES)) + tid;
+    pp_load_row(v2s, o2_slab, lane, o2_lane_order);
     __bf16* orow = A.out + ((s0 + wr.myrow) * A.Hq + h) * D;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const bf16x8 v1 = o1s[c * PP_NT];
+      const int db = c >> 1;
+      u32x2 w[2];
 #pragma unroll
       for (int hq = 0; hq < 2; ++hq) {
-        const int db = c >> 1, q4 = 2 * (c & 1) + hq;
-        const int d0 = db * 32 + 8 * q4 + 4 * g;
+        const int q4 = 2 * (c & 1) + hq;
         const float4 v2 = v2s[4 * db + q4];
         const float o2v[4] = {v2.x, v2.y, v2.z, v2.w};
-        bf16x4 w;
+        bf16x4 x;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float far_num = far > 0.f ? z2 * o2v[e] - c3 * o[db][4 * q4 + e] : 0.f;
-          w[e] = (__bf16)((z1 * (float)v1[4 * hq + e] + far_num) * inv);
+          x[e] = (__bf16)((z1 * (float)v1[4 * hq + e] + far_num) * inv);
         }
-        *(bf16x4*)(orow + d0) = w;
+        w[hq] = __builtin_bit_cast(u32x2, x);
       }
+      *(u32x4*)(orow + db * 32 + 16 * (c & 1) + 8 * g) = pair_channels(w[0], w[1]);
     }
     if (A.lse != nullptr && g == 0) A.lse[ridx] = (M + __log2f(Z)) * LN2;
   }
