@@ -392,8 +392,10 @@ struct PrefillArgs {
   float* lse;         // [Hq][T] or nullptr
   float* o1;          // [Hq][nseq * JL_LO_ROWS][128] fp32: normalised pass 1 output of the first rows
   float* o2;          // [Hq][T][128] fp32: normalised pass 2 output (rows from JL_LO_ROWS on: see o2_slot)
+  float* o3;          // [Hq][T][128] fp32: normalised pass 3 output of rows from JL_LO_ROWS on (as o2)
   float* lse1;        // [Hq][nseq * JL_LO_ROWS]: pass 1 LogSumExp of the first rows (log2 units)
   float* lse2;        // [Hq][T]: pass 2 LogSumExp (log2 units)
+  float* lse3;        // [Hq][T]: pass 3 LogSumExp of rows from JL_LO_ROWS on (log2 units)
   int64_t total;
   int64_t t_pad;
   int64_t w0;
@@ -962,65 +964,74 @@ __device__ inline void pp_matrix(const PpTiles& T, int k, bool pv, const bf16x8*
 // score half every tile, 16 extra vector moves (measured: 2% of the prefill).
 // Group B's loop is rotated for that: matrix phase, then the copies and
 // softmax of the same tile.
+// Group A's side of a pass (waves 0-3), from the copy of K_0 on.
 template <int KIND>
-__device__ inline void pp_run(const PpTiles& T, const bf16x8* qf, PpState& st, f32x16* o, const WaveRows& wr,
-                              int lane) {
+__device__ inline void pp_walk_a(const PpTiles& T, const bf16x8* qf, PpState& st, f32x16* o, const WaveRows& wr,
+                                 int lane) {
   const int n = T.n;
   const int g = lane >> 5;
   f32x16 s[2];
   bf16x8 p[4];
-  if (T.wave < 4)
-    pp_issue<PP_K_PER_WAVE, KT_PIECES>(pp_kbuf(T, 0), T.rk, T.plan.koff, (uint32_t)T.t0 * (BK * 256), T.wave);
+  pp_issue<PP_K_PER_WAVE, KT_PIECES>(pp_kbuf(T, 0), T.rk, T.plan.koff, (uint32_t)T.t0 * (BK * 256), T.wave);
   pp_wait_copies();
   pp_barrier();
-  if (T.wave < 4) {
-    pp_matrix(T, 0, false, qf, st, s, p, o, lane);
+  pp_matrix(T, 0, false, qf, st, s, p, o, lane);
+  pp_barrier();
+  pp_copies_v(T, 0);
+  pp_softmax_tile<KIND>(T, 0, s, p, st, o, wr, g);
+  pp_wait_copies();
+  pp_barrier();
+  for (int j = 1; j < n; ++j) {
+    pp_matrix(T, j, true, qf, st, s, p, o, lane);
     pp_barrier();
-    pp_copies_v(T, 0);
-    pp_softmax_tile<KIND>(T, 0, s, p, st, o, wr, g);
+    pp_copies_v(T, j);
+    pp_softmax_tile<KIND>(T, j, s, p, st, o, wr, g);
     pp_wait_copies();
-    pp_barrier();
-    for (int j = 1; j < n; ++j) {
-      pp_matrix(T, j, true, qf, st, s, p, o, lane);
-      pp_barrier();
-      pp_copies_v(T, j);
-      pp_softmax_tile<KIND>(T, j, s, p, st, o, wr, g);
-      pp_wait_copies();
-      pp_barrier();
-    }
-    pp_pv(pp_vbuf(T, n - 1), p, lane, o);
-    pp_mfma_order<16, PP_READ_DEPTH>();
-    pp_barrier();
-    pp_barrier();
-  } else {
-    pp_copies(T, 0);
-    pp_barrier();
-    pp_matrix(T, 0, false, qf, st, s, p, o, lane);
-    pp_wait_copies();
-    pp_barrier();
-    if (n > 1) pp_copies(T, 1);
-    pp_softmax_tile<KIND>(T, 0, s, p, st, o, wr, g);
-    pp_barrier();
-    for (int j = 1; j < n; ++j) {
-      pp_matrix(T, j, true, qf, st, s, p, o, lane);
-      pp_wait_copies();
-      pp_barrier();
-      if (j + 1 < n) pp_copies(T, j + 1);
-      pp_softmax_tile<KIND>(T, j, s, p, st, o, wr, g);
-      pp_barrier();
-    }
-    pp_pv(pp_vbuf(T, n - 1), p, lane, o);
-    pp_mfma_order<16, PP_READ_DEPTH>();
     pp_barrier();
   }
+  pp_pv(pp_vbuf(T, n - 1), p, lane, o);
+  pp_mfma_order<16, PP_READ_DEPTH>();
+  pp_barrier();
+  pp_barrier();
 }
 
-// Pass 1's normalised output of a 256-row tile, kept in LDS between the two
-// window passes of ROLE 3: 64 bf16 per lane, chunk c (8 values) of thread t
-// at (c * PP_NT + t) * 16 bytes.  o1 enters the merge with a positive weight
-// only (the cancelling pair is o2 and o3), so bf16 holds it within the
-// output's own rounding.
-constexpr int O1_BYTES = PP_NT * 128;
+// Group B's side of a pass (waves 4-7), with the same number of barriers.
+template <int KIND>
+__device__ inline void pp_walk_b(const PpTiles& T, const bf16x8* qf, PpState& st, f32x16* o, const WaveRows& wr,
+                                 int lane) {
+  const int n = T.n;
+  const int g = lane >> 5;
+  f32x16 s[2];
+  bf16x8 p[4];
+  pp_wait_copies();
+  pp_barrier();
+  pp_copies(T, 0);
+  pp_barrier();
+  pp_matrix(T, 0, false, qf, st, s, p, o, lane);
+  pp_wait_copies();
+  pp_barrier();
+  if (n > 1) pp_copies(T, 1);
+  pp_softmax_tile<KIND>(T, 0, s, p, st, o, wr, g);
+  pp_barrier();
+  for (int j = 1; j < n; ++j) {
+    pp_matrix(T, j, true, qf, st, s, p, o, lane);
+    pp_wait_copies();
+    pp_barrier();
+    if (j + 1 < n) pp_copies(T, j + 1);
+    pp_softmax_tile<KIND>(T, j, s, p, st, o, wr, g);
+    pp_barrier();
+  }
+  pp_pv(pp_vbuf(T, n - 1), p, lane, o);
+  pp_mfma_order<16, PP_READ_DEPTH>();
+  pp_barrier();
+}
+
+template <int KIND>
+__device__ inline void pp_run(const PpTiles& T, const bf16x8* qf, PpState& st, f32x16* o, const WaveRows& wr,
+                              int lane) {
+  if (T.wave < 4) pp_walk_a<KIND>(T, qf, st, o, wr, lane);
+  else pp_walk_b<KIND>(T, qf, st, o, wr, lane);
+}
 
 // Pass 2's (or the far pass's) fp32 output of rows >= JL_LO_ROWS, as the
 // 256-row kernel writes and reads it.  slab is the wave's first row.  A lane
@@ -1045,10 +1056,17 @@ __device__ inline void pp_load_row(float4* v, const float* slab, int lane, bool 
   for (int i = 0; i < 16; ++i) v[i] = *(const float4*)o2_slot((float*)slab, lane, i, lane_order);
 }
 
-// ROLE 0: pass 2 (full causal, remote q/k).  ROLE 3: passes 1 and 3 of the
-// tile one after the other (window, base q/k, then window, remote q/k) and
-// the inclusion-exclusion merge with pass 2's output; sequences with
-// w0 >= L run pass 1 over the whole causal range and write O directly.
+// ROLE 0: passes 2 and 3 (remote q/k) from one walk over the key tiles.  On a
+// sequence with G > 1 the walk takes the window tiles first under the window
+// mask (0 <= i - j < w0), which is exactly pass 3, stores that running state
+// as pass 3's output, and goes on over the far tiles under the far mask
+// (i - j >= w0); the end state has seen every causal pair once, which is
+// pass 2.  Pass 3 thus shares pass 2's K/V tiles, scores and probabilities
+// (only the few tiles that hold the window's lower edge are walked twice,
+// once per mask).  On a G = 1 sequence it is the plain causal pass.
+// ROLE 3: pass 1 (window, base q/k) and the inclusion-exclusion merge with
+// the outputs of passes 2 and 3; sequences with w0 >= L run pass 1 over the
+// whole causal range and write O directly.
 // The disjoint variant: ROLE 4 is the far pass (remote q/k, pairs with
 // i - j >= w0 only, written where pass 2's output goes) and ROLE 5 is pass 1
 // merged with it, O = (z1 o1 + zf of) / (z1 + zf), which has no cancelling
@@ -1059,7 +1077,7 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
   static_assert(ROLE == 0 || ROLE == 3 || ROLE == 4 || ROLE == 5, "pass roles of the 256-row kernel");
   constexpr int KIND = ROLE == 0 ? 0 : ROLE == 4 ? 2 : 1;
   constexpr bool BASE = ROLE == 3 || ROLE == 5;      // the first pass runs on the base grid
-  __shared__ __align__(1024) char smem[2 * (KT_BYTES + VT_BYTES) + (ROLE == 3 ? O1_BYTES : 0)];
+  __shared__ __align__(1024) char smem[2 * (KT_BYTES + VT_BYTES)];
   int h, b, u;
   if (!block_item<false>(sc, A.Hq, &h, &b, &u)) return;
   // the work item is uniform over the block; say so, so that pointers built
@@ -1081,7 +1099,9 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
   const int g = lane >> 5;
   const int kvh = __builtin_amdgcn_readfirstlane(hm.kv_of[h]);
   const int64_t s0 = uniform_i64(seqs.start[b]);
-  const int w0 = A.w0 > (int64_t)L ? L : (int)A.w0;
+  // the window of the walk: w0, or L where it covers every causal pair (w0 >= L,
+  // and ROLE 0's walk on a G = 1 sequence, which is then the plain causal pass)
+  const int w0 = A.w0 > (int64_t)L || (ROLE == 0 && only2) ? L : (int)A.w0;
   const int iw = r0 + wave * 32;
   const WaveRows wr{iw, iw + (lane & 31), w0};
   const bool live = iw < L;             // waves past the end load nothing
@@ -1106,18 +1126,9 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
   const int q_row = q_valid ? wr.myrow : L - 1;
   const int q_rem = jl_remote_pos(q_row, __builtin_amdgcn_readfirstlane(seqs.G[b]));
   const __bf16* q_src = A.q + ((s0 + q_row) * A.Hq + h) * D;
-  // ROLE 3 rotates the same rows again for pass 3: the raw rows wait in the
-  // LDS area of pass 1's output, which pass 1 does not touch, each thread's
-  // 128 bytes where its own o1 chunks go (so no barrier is needed)
-  __attribute__((address_space(3))) bf16x8* const o1s =
-      (__attribute__((address_space(3))) bf16x8*)(lds + 2 * (KT_BYTES + VT_BYTES)) + tid;
   if (live) {
     bf16x8 x[8];
     load_q_raw(x, q_src, g);
-    if constexpr (ROLE == 3) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) o1s[c * PP_NT] = x[c];
-    }
     rotate_q<false>(qf, nullptr, x, q_valid, BASE ? q_row : q_rem, A, g);
   } else {
 #pragma unroll
@@ -1127,20 +1138,54 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16{};
   PpState st{-INFINITY, 0.f, f32x16{}};
-  T.t0 = ROLE == 0 || ROLE == 4 || only1 ? 0 : tw0;
-  int t_end = tiles_end;
-  if (ROLE == 4) {
-    // far pairs of the tile's rows end at key r0 + 255 - w0
-    const int last = r0 + PP_BQ - 1 - w0;
-    t_end = last < 0 ? 0 : min(tiles_end, last / BK + 1);
+  const int64_t slab_off = ((int64_t)h * A.total + s0 + iw) * D;
+  // far pairs of the tile's rows end at key r0 + 255 - w0
+  const int far_last = r0 + PP_BQ - 1 - w0;
+  const int far_tiles = far_last < 0 ? 0 : min(tiles_end, far_last / BK + 1);
+  if constexpr (ROLE == 0) {
+    // pass 3 (the whole causal pass on a G = 1 sequence): the window tiles
+    // under the window mask; then, on a G > 1 sequence, pass 3's output from
+    // the running state and pass 2: the far tiles under the far mask.  Each
+    // group runs both walks in its own branch (joining the groups between
+    // them made the register allocator spill the carried state).
+    T.t0 = tw0;
+    T.n = tiles_end - tw0;
+    PpTiles T2 = T;
+    T2.t0 = 0;
+    T2.n = only2 ? 0 : far_tiles;
+    const auto store_pass3 = [&]() {
+      if (only2 || !live || wr.myrow >= L) return;
+      // a row without window pairs (w0 = 0) stores o3 = 0 and lse3 = -inf
+      const float l3 = pair_sum(st.l);
+      const float inv3 = l3 > 0.f ? 1.f / l3 : 0.f;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *(float4*)o2_slot(A.o3 + slab_off, lane, 4 * db + q4, iw + 32 <= L) =
+              make_float4(o[db][4 * q4] * inv3, o[db][4 * q4 + 1] * inv3, o[db][4 * q4 + 2] * inv3,
+                          o[db][4 * q4 + 3] * inv3);
+      if (g == 0) A.lse3[(int64_t)h * A.total + s0 + wr.myrow] = l3 > 0.f ? st.m + __log2f(l3) : -INFINITY;
+    };
+    if (wave < 4) {
+      pp_walk_a<1>(T, qf, st, o, wr, lane);
+      store_pass3();
+      if (T2.n > 0) pp_walk_a<2>(T2, qf, st, o, wr, lane);
+    } else {
+      pp_walk_b<1>(T, qf, st, o, wr, lane);
+      store_pass3();
+      if (T2.n > 0) pp_walk_b<2>(T2, qf, st, o, wr, lane);
+    }
+  } else {
+    T.t0 = ROLE == 4 || only1 ? 0 : tw0;
+    T.n = (ROLE == 4 ? far_tiles : tiles_end) - T.t0;
+    if (T.n > 0) pp_run<KIND>(T, qf, st, o, wr, lane);
   }
-  T.n = t_end - T.t0;
-  if (T.n > 0) pp_run<KIND>(T, qf, st, o, wr, lane);
   const float l = pair_sum(st.l);
   const float lam = l > 0.f ? st.m + __log2f(l) : -INFINITY;
   const int64_t ridx = (int64_t)h * A.total + s0 + wr.myrow;
   const bool row_ok = live && wr.myrow < L;
-  float* const o2_slab = A.o2 + ((int64_t)h * A.total + s0 + iw) * D;
+  float* const o2_slab = A.o2 + slab_off;
   const bool o2_lane_order = iw + 32 <= L;
   if (ROLE == 0 ? only2 : only1) {
     // the pass is the whole attention of the sequence
@@ -1207,61 +1252,44 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
     }
     if (A.lse != nullptr && g == 0) A.lse[ridx] = (M + __log2f(Z)) * LN2;
   } else {
-    // pass 1 done: o1 (normalised, bf16) to LDS, lam1 stays in a register
-    const float lam1 = lam;
-    bf16x8 x[8];
-    if (live) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) x[c] = o1s[c * PP_NT];
-    }
-    {
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        bf16x8 w;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] = (__bf16)(o[c >> 1][8 * (c & 1) + e] * inv);
-        o1s[c * PP_NT] = w;
-      }
-    }
-    // pass 3: the same window tiles with remote q/k
-    T.rk = __builtin_amdgcn_make_buffer_rsrc((void*)(A.kr + krow), 0, 0x7fffffff, BUF_RSRC_WORD3);
-    if (live) rotate_q<false>(qf, nullptr, x, q_valid, q_rem, A, g);
-#pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] = f32x16{};
-    st = PpState{-INFINITY, 0.f, f32x16{}};
-    if (T.n > 0) pp_run<KIND>(T, qf, st, o, wr, lane);
-    const float l3 = pair_sum(st.l);
+    // ROLE 3, pass 1 done: its accumulator o (scaled by exp2(-st.m)) and lam
+    // stay in registers; passes 2 and 3 come from the pass-2 launch.  With
+    // z_k = exp2(lam_k - M), O = (z1 o1 + [far > 0] (z2 o2 - z3 o3)) / Z,
+    // far = z2 - z3 (the far mass, clamped at zero), Z = z1 + max(far, 0).
     if (!row_ok) return;
+    float4 v2s[16], v3s[16];
+    pp_load_row(v2s, o2_slab, lane, o2_lane_order);
+    pp_load_row(v3s, A.o3 + slab_off, lane, o2_lane_order);
     const float lam2 = A.lse2[ridx];
-    const float lam3 = l3 > 0.f ? st.m + __log2f(l3) : -INFINITY;
-    const float M = fmaxf(lam1, lam2);
-    const float z1 = __builtin_amdgcn_exp2f(lam1 - M);
+    const float lam3 = A.lse3[ridx];
+    // lam and lam3 are -inf only when w0 = 0 (no window pair; o = 0, o3 = 0);
+    // a causal row always has a pair, so M is finite
+    const float M = fmaxf(lam, lam2);
+    const float z1 = __builtin_amdgcn_exp2f(lam - M);
+    const float c1 = __builtin_amdgcn_exp2f(st.m - M);   // z1 o1 = c1 o
     const float z2 = __builtin_amdgcn_exp2f(lam2 - M);
     const float z3 = __builtin_amdgcn_exp2f(lam3 - M);
-    const float c3 = l3 > 0.f ? __builtin_amdgcn_exp2f(st.m - M) : 0.f;
     const float far = z2 - z3;
     const float Z = z1 + fmaxf(far, 0.f);
     const float inv = 1.f / Z;
-    float4 v2s[16];
-    pp_load_row(v2s, o2_slab, lane, o2_lane_order);
+    const float w2 = far > 0.f ? z2 : 0.f;
+    const float w3 = far > 0.f ? z3 : 0.f;
     __bf16* orow = A.out + ((s0 + wr.myrow) * A.Hq + h) * D;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const bf16x8 v1 = o1s[c * PP_NT];
       const int db = c >> 1;
       u32x2 w[2];
 #pragma unroll
       for (int hq = 0; hq < 2; ++hq) {
         const int q4 = 2 * (c & 1) + hq;
         const float4 v2 = v2s[4 * db + q4];
+        const float4 v3 = v3s[4 * db + q4];
         const float o2v[4] = {v2.x, v2.y, v2.z, v2.w};
+        const float o3v[4] = {v3.x, v3.y, v3.z, v3.w};
         bf16x4 x;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float far_num = far > 0.f ? z2 * o2v[e] - c3 * o[db][4 * q4 + e] : 0.f;
-          x[e] = (__bf16)((z1 * (float)v1[4 * hq + e] + far_num) * inv);
-        }
+        for (int e = 0; e < 4; ++e)
+          x[e] = (__bf16)((c1 * o[db][4 * q4 + e] + (w2 * o2v[e] - w3 * o3v[e])) * inv);
         w[hq] = __builtin_bit_cast(u32x2, x);
       }
       *(u32x4*)(orow + db * 32 + 16 * (c & 1) + 8 * g) = pair_channels(w[0], w[1]);
@@ -1325,8 +1353,10 @@ hipError_t jl_launch_prefill_bf16(const JlPrefillWs& ws, const void* q, const Jl
   A.lse = lse;
   A.o1 = (float*)ws.o1;
   A.o2 = (float*)ws.o2;
+  A.o3 = (float*)ws.o3;
   A.lse1 = (float*)ws.lse1;
   A.lse2 = (float*)ws.lse2;
+  A.lse3 = (float*)ws.lse3;
   A.total = total_tokens;
   A.t_pad = ws.t_pad;
   A.w0 = w0;
@@ -1348,8 +1378,9 @@ hipError_t jl_launch_prefill_bf16(const JlPrefillWs& ws, const void* q, const Jl
   }
   const unsigned nblk = (unsigned)sc.total_units * (unsigned)Hq;   // multiple of 8 when xcd_heads
   const unsigned nfirst = (unsigned)(seqs.nseq * Hq);
-  // rows >= 128 in 256-row tiles (pass 2, then passes 1 and 3 fused); the
-  // first 128 rows of every sequence in the split-operand kernel, pass by pass
+  // rows >= 128 in 256-row tiles (passes 2 and 3 from one walk, then pass 1
+  // and the merge); the first 128 rows of every sequence in the
+  // split-operand kernel, pass by pass
   // disjoint: 256-row tiles run the far pass, then pass 1 merged with it
   // (pass 2 only for the G = 1 sequences); the first 128 rows as above
   if (any_p2) {
