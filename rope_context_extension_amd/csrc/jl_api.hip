@@ -209,16 +209,17 @@ static int prefill_impl(const void* q, const void* k, const void* v, void* o, fl
   const size_t lrows = (size_t)num_seqs * JL_LO_ROWS;
   const size_t nklo = (size_t)num_kv_heads * lrows * head_dim * el;
   pl.off_lo = off; if (dtype == JL_BF16) off += 2 * align256(nklo);
-  // the pass-2 launch hands (o_k, lse_k) of passes 2 and 3 to the launch that
-  // runs pass 1 and merges; pass 1's own only for the first JL_LO_ROWS rows
-  // (the 256-row kernel keeps its pass-1 output in registers)
+  // rows >= JL_LO_ROWS: the pass-2 launch keeps pass 3's state (accumulator,
+  // stabiliser and sum) until it has formed the far part, which it hands
+  // (o, lse) to the pass-1 launch; the first JL_LO_ROWS rows hand pass 1's
+  // and pass 2's outputs to the launch that runs pass 3 and merges
   const bool merge = dtype == JL_BF16 && pl.seqs.any_remote;
   const size_t no = align256((size_t)num_q_heads * total_tokens * head_dim * 4);
   const size_t nl = align256((size_t)num_q_heads * total_tokens * 4);
   const size_t no1 = align256((size_t)num_q_heads * lrows * head_dim * 4);
   const size_t nl1 = align256((size_t)num_q_heads * lrows * 4);
   pl.off_o = off; if (merge) off += no1 + 2 * no;
-  pl.off_lse = off; if (merge) off += nl1 + 2 * nl;
+  pl.off_lse = off; if (merge) off += nl1 + 3 * nl;
   pl.total = total_tokens == 0 ? 0 : off;
 
   if (workspace == nullptr) {
@@ -257,7 +258,7 @@ static int prefill_impl(const void* q, const void* k, const void* v, void* o, fl
     ws.o3 = wsb + pl.off_o + no1 + no;
     ws.lse1 = wsb + pl.off_lse;
     ws.lse2 = wsb + pl.off_lse + nl1;
-    ws.lse3 = wsb + pl.off_lse + nl1 + nl;
+    ws.ml3 = wsb + pl.off_lse + nl1 + nl;
   }
   if (dtype == JL_BF16) {
     const size_t lrows = (size_t)num_seqs * JL_LO_ROWS;

@@ -74,11 +74,11 @@ struct JlPrefillWs {
                  // (bf16 path, some G > 1; the 256-row kernel keeps its own in registers)
   void* o2;      // [Hq][T][d] fp32: normalised pass-2 output; the 256-row kernels keep each
                  // full 32-row group of a wave in that wave's lane order
-  void* o3;      // [Hq][T][d] fp32: normalised pass-3 output of rows >= JL_LO_ROWS, written by
-                 // the pass-2 launch (same layout as o2)
+  void* o3;      // [Hq][T][d] fp32: pass 3's accumulator of rows >= JL_LO_ROWS (scaled by
+                 // exp2(-m3)), written and read back by the pass-2 launch (same layout as o2)
   void* lse1;    // [Hq][nseq * JL_LO_ROWS] fp32: pass-1 LogSumExp of the first rows, log2 units
   void* lse2;    // [Hq][T] fp32: pass-2 LogSumExp, log2 units
-  void* lse3;    // [Hq][T] fp32: pass-3 LogSumExp of rows >= JL_LO_ROWS, log2 units
+  void* ml3;     // [Hq][T] float2: pass 3's stabiliser m3 (log2 units) and sum l3, rows >= JL_LO_ROWS
   void* kc;      // [T][Hkv][d] dtype: base-rotated k in cache layout (optional output), or nullptr
   int64_t t_pad;
 };

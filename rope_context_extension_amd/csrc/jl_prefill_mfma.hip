@@ -8,9 +8,17 @@
 //     lse_k = m_k + log l_k,  M = max(lse_1, lse_2),  z_k = exp(lse_k - M),
 //     out = (z1 o1 + z2 o2 - z3 o3) / (z1 + z2 - z3).
 //
-// One workgroup = 4 waves = 128 query rows of one head.  The three passes
-// run one after another over the same K/V tile pipeline, each with its own
-// running max, sum and accumulator (a literal flash pass):
+// Rows from 128 on (prefill_pp_kernel, 256 rows and 8 waves per workgroup,
+// two launches): passes 2 and 3 come from one walk over the remote-grid key
+// tiles, window tiles first; the walk's state after the window tiles is
+// pass 3's, its end state pass 2's, and the far part z2 o2 - z3 o3 is formed
+// from the two states before it leaves the launch.  The second launch runs
+// pass 1 and adds the far part.
+//
+// A sequence's first 128 rows (prefill_pass_kernel, one workgroup = 4 waves
+// = 128 query rows of one head): the three passes run one after another over
+// the same K/V tile pipeline, each with its own running max, sum and
+// accumulator (a literal flash pass):
 //   pass 2 (remote q/k, causal)   over every key tile up to the diagonal;
 //   pass 1 (base q/k, window)     over the tiles within w0 of the rows;
 //   after pass 1 the two results are folded into one partial I-E numerator
@@ -392,10 +400,10 @@ struct PrefillArgs {
   float* lse;         // [Hq][T] or nullptr
   float* o1;          // [Hq][nseq * JL_LO_ROWS][128] fp32: normalised pass 1 output of the first rows
   float* o2;          // [Hq][T][128] fp32: normalised pass 2 output (rows from JL_LO_ROWS on: see o2_slot)
-  float* o3;          // [Hq][T][128] fp32: normalised pass 3 output of rows from JL_LO_ROWS on (as o2)
+  float* o3;          // [Hq][T][128] fp32: pass 3's accumulator (scaled by exp2(-m3)), rows from JL_LO_ROWS on (as o2)
   float* lse1;        // [Hq][nseq * JL_LO_ROWS]: pass 1 LogSumExp of the first rows (log2 units)
   float* lse2;        // [Hq][T]: pass 2 LogSumExp (log2 units)
-  float* lse3;        // [Hq][T]: pass 3 LogSumExp of rows from JL_LO_ROWS on (log2 units)
+  float2* ml3;        // [Hq][T]: pass 3's stabiliser m3 (log2 units) and sum, rows from JL_LO_ROWS on
   int64_t total;
   int64_t t_pad;
   int64_t w0;
@@ -1059,24 +1067,30 @@ __device__ inline void pp_load_row(float4* v, const float* slab, int lane, bool 
 // ROLE 0: passes 2 and 3 (remote q/k) from one walk over the key tiles.  On a
 // sequence with G > 1 the walk takes the window tiles first under the window
 // mask (0 <= i - j < w0), which is exactly pass 3, stores that running state
-// as pass 3's output, and goes on over the far tiles under the far mask
-// (i - j >= w0); the end state has seen every causal pair once, which is
-// pass 2.  Pass 3 thus shares pass 2's K/V tiles, scores and probabilities
-// (only the few tiles that hold the window's lower edge are walked twice,
-// once per mask).  On a G = 1 sequence it is the plain causal pass.
-// ROLE 3: pass 1 (window, base q/k) and the inclusion-exclusion merge with
-// the outputs of passes 2 and 3; sequences with w0 >= L run pass 1 over the
+// (accumulator, stabiliser m3 and sum l3), and goes on over the far tiles
+// under the far mask (i - j >= w0); the end state has seen every causal pair
+// once, which is pass 2.  Pass 3 thus shares pass 2's K/V tiles, scores and
+// probabilities (only the few tiles that hold the window's lower edge are
+// walked twice, once per mask).  The inclusion-exclusion step then takes
+// pass 3 from pass 2 in the frame of pass 2's stabiliser m2: with
+// c = exp2(m3 - m2) (m only rises along the walk, so c <= 1), the far part
+// is O_far = O2 - c O3 and l_far = l2 - c l3, which is z2 o2 - z3 o3 and
+// z2 - z3 through the two passes' LogSumExp statistics (lam = m + log2 l),
+// formed without the exp2 of large lam values.  Its far mass is clamped at
+// zero, and (o_far = O_far / l_far, lam_far) goes where pass 2's output
+// would.  On a G = 1 sequence ROLE 0 is the plain causal pass.
+// ROLE 4 (the disjoint variant) is the far pass alone: remote q/k, pairs
+// with i - j >= w0 only, written to the same place; ROLE 0 then serves only
+// the G = 1 sequences.
+// ROLE 5: pass 1 (window, base q/k) merged with the far part,
+// O = (z1 o1 + zf of) / (z1 + zf); sequences with w0 >= L run pass 1 over the
 // whole causal range and write O directly.
-// The disjoint variant: ROLE 4 is the far pass (remote q/k, pairs with
-// i - j >= w0 only, written where pass 2's output goes) and ROLE 5 is pass 1
-// merged with it, O = (z1 o1 + zf of) / (z1 + zf), which has no cancelling
-// terms; ROLE 0 then serves only the G = 1 sequences.
 template <int ROLE>
 __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlHeadMap hm, JlSeqs seqs,
                                                              JlSched sc) {
-  static_assert(ROLE == 0 || ROLE == 3 || ROLE == 4 || ROLE == 5, "pass roles of the 256-row kernel");
+  static_assert(ROLE == 0 || ROLE == 4 || ROLE == 5, "pass roles of the 256-row kernel");
   constexpr int KIND = ROLE == 0 ? 0 : ROLE == 4 ? 2 : 1;
-  constexpr bool BASE = ROLE == 3 || ROLE == 5;      // the first pass runs on the base grid
+  constexpr bool BASE = ROLE == 5;                   // pass 1 runs on the base grid
   __shared__ __align__(1024) char smem[2 * (KT_BYTES + VT_BYTES)];
   int h, b, u;
   if (!block_item<false>(sc, A.Hq, &h, &b, &u)) return;
@@ -1091,7 +1105,7 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
   const bool only1 = A.w0 >= (int64_t)L;
   const bool only2 = seqs.G[b] == 1 && !only1;
   if (ROLE == 0 && (only1 || (A.disjoint && !only2))) return;
-  if ((ROLE == 3 || ROLE == 5) && only2) return;
+  if (ROLE == 5 && only2) return;
   if (ROLE == 4 && (only1 || only2)) return;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1154,18 +1168,19 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
     T2.t0 = 0;
     T2.n = only2 ? 0 : far_tiles;
     const auto store_pass3 = [&]() {
+      // pass 3's state as it stands (a row without window pairs, w0 = 0,
+      // stores m3 = -inf, l3 = 0 and a zero accumulator)
       if (only2 || !live || wr.myrow >= L) return;
-      // a row without window pairs (w0 = 0) stores o3 = 0 and lse3 = -inf
       const float l3 = pair_sum(st.l);
-      const float inv3 = l3 > 0.f ? 1.f / l3 : 0.f;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
           *(float4*)o2_slot(A.o3 + slab_off, lane, 4 * db + q4, iw + 32 <= L) =
-              make_float4(o[db][4 * q4] * inv3, o[db][4 * q4 + 1] * inv3, o[db][4 * q4 + 2] * inv3,
-                          o[db][4 * q4 + 3] * inv3);
-      if (g == 0) A.lse3[(int64_t)h * A.total + s0 + wr.myrow] = l3 > 0.f ? st.m + __log2f(l3) : -INFINITY;
+              make_float4(o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]);
+      // both lanes of the row store the same (m3, l3), so that each reads back
+      // its own store
+      A.ml3[(int64_t)h * A.total + s0 + wr.myrow] = make_float2(st.m, l3);
     };
     if (wave < 4) {
       pp_walk_a<1>(T, qf, st, o, wr, lane);
@@ -1210,20 +1225,36 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
     return;
   }
   if constexpr (ROLE == 0 || ROLE == 4) {
+    // the far part: pass 2 minus pass 3 (ROLE 0), or the far pass (ROLE 4);
     // rows without a far key (i < w0) store o = 0 and lam = -inf
     if (!row_ok) return;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float lf = l;
+    float c = 0.f;
+    float4 s3[16];
+    if constexpr (ROLE == 0) {
+      pp_load_row(s3, A.o3 + slab_off, lane, o2_lane_order);
+      const float2 ml3 = A.ml3[ridx];
+      c = ml3.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml3.x - st.m);
+      lf = l - c * ml3.y;
+    }
+    const bool far = lf > 0.f;                           // the far mass, clamped at zero
+    const float inv = far ? 1.f / lf : 0.f;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float4 v = make_float4(o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]);
+        if constexpr (ROLE == 0) {
+          const float4 w = s3[4 * db + q4];
+          v = make_float4(v.x - c * w.x, v.y - c * w.y, v.z - c * w.z, v.w - c * w.w);
+        }
         *(float4*)o2_slot(o2_slab, lane, 4 * db + q4, o2_lane_order) =
-            make_float4(o[db][4 * q4] * inv, o[db][4 * q4 + 1] * inv, o[db][4 * q4 + 2] * inv,
-                        o[db][4 * q4 + 3] * inv);
-    if (g == 0) A.lse2[ridx] = lam;
+            make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
+      }
+    if (g == 0) A.lse2[ridx] = far ? st.m + __log2f(lf) : -INFINITY;
   } else if constexpr (ROLE == 5) {
-    // disjoint merge: window (base grid) and far (remote grid) are two
-    // halves of one softmax, so both weights are positive
+    // pass 1 merged with the far part: window (base grid) and far (remote
+    // grid) are two halves of one softmax, so both weights are positive
     if (!row_ok) return;
     const float lamf = A.lse2[ridx];
     const float M = fmaxf(lam, lamf);                    // lam is finite: the diagonal is in the window
@@ -1246,50 +1277,6 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
         bf16x4 x;
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = (__bf16)((c1 * o[db][4 * q4 + e] + zf * ofv[e]) * inv);
-        w[hq] = __builtin_bit_cast(u32x2, x);
-      }
-      *(u32x4*)(orow + db * 32 + 16 * (c & 1) + 8 * g) = pair_channels(w[0], w[1]);
-    }
-    if (A.lse != nullptr && g == 0) A.lse[ridx] = (M + __log2f(Z)) * LN2;
-  } else {
-    // ROLE 3, pass 1 done: its accumulator o (scaled by exp2(-st.m)) and lam
-    // stay in registers; passes 2 and 3 come from the pass-2 launch.  With
-    // z_k = exp2(lam_k - M), O = (z1 o1 + [far > 0] (z2 o2 - z3 o3)) / Z,
-    // far = z2 - z3 (the far mass, clamped at zero), Z = z1 + max(far, 0).
-    if (!row_ok) return;
-    float4 v2s[16], v3s[16];
-    pp_load_row(v2s, o2_slab, lane, o2_lane_order);
-    pp_load_row(v3s, A.o3 + slab_off, lane, o2_lane_order);
-    const float lam2 = A.lse2[ridx];
-    const float lam3 = A.lse3[ridx];
-    // lam and lam3 are -inf only when w0 = 0 (no window pair; o = 0, o3 = 0);
-    // a causal row always has a pair, so M is finite
-    const float M = fmaxf(lam, lam2);
-    const float z1 = __builtin_amdgcn_exp2f(lam - M);
-    const float c1 = __builtin_amdgcn_exp2f(st.m - M);   // z1 o1 = c1 o
-    const float z2 = __builtin_amdgcn_exp2f(lam2 - M);
-    const float z3 = __builtin_amdgcn_exp2f(lam3 - M);
-    const float far = z2 - z3;
-    const float Z = z1 + fmaxf(far, 0.f);
-    const float inv = 1.f / Z;
-    const float w2 = far > 0.f ? z2 : 0.f;
-    const float w3 = far > 0.f ? z3 : 0.f;
-    __bf16* orow = A.out + ((s0 + wr.myrow) * A.Hq + h) * D;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int db = c >> 1;
-      u32x2 w[2];
-#pragma unroll
-      for (int hq = 0; hq < 2; ++hq) {
-        const int q4 = 2 * (c & 1) + hq;
-        const float4 v2 = v2s[4 * db + q4];
-        const float4 v3 = v3s[4 * db + q4];
-        const float o2v[4] = {v2.x, v2.y, v2.z, v2.w};
-        const float o3v[4] = {v3.x, v3.y, v3.z, v3.w};
-        bf16x4 x;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          x[e] = (__bf16)((c1 * o[db][4 * q4 + e] + (w2 * o2v[e] - w3 * o3v[e])) * inv);
         w[hq] = __builtin_bit_cast(u32x2, x);
       }
       *(u32x4*)(orow + db * 32 + 16 * (c & 1) + 8 * g) = pair_channels(w[0], w[1]);
@@ -1356,7 +1343,7 @@ hipError_t jl_launch_prefill_bf16(const JlPrefillWs& ws, const void* q, const Jl
   A.o3 = (float*)ws.o3;
   A.lse1 = (float*)ws.lse1;
   A.lse2 = (float*)ws.lse2;
-  A.lse3 = (float*)ws.lse3;
+  A.ml3 = (float2*)ws.ml3;
   A.total = total_tokens;
   A.t_pad = ws.t_pad;
   A.w0 = w0;
@@ -1378,11 +1365,11 @@ hipError_t jl_launch_prefill_bf16(const JlPrefillWs& ws, const void* q, const Jl
   }
   const unsigned nblk = (unsigned)sc.total_units * (unsigned)Hq;   // multiple of 8 when xcd_heads
   const unsigned nfirst = (unsigned)(seqs.nseq * Hq);
-  // rows >= 128 in 256-row tiles (passes 2 and 3 from one walk, then pass 1
-  // and the merge); the first 128 rows of every sequence in the
-  // split-operand kernel, pass by pass
-  // disjoint: 256-row tiles run the far pass, then pass 1 merged with it
-  // (pass 2 only for the G = 1 sequences); the first 128 rows as above
+  // rows >= 128 in 256-row tiles: passes 2 and 3 from one walk, which leaves
+  // the far part (pass 2 minus pass 3), then pass 1 merged with it; the first
+  // 128 rows of every sequence in the split-operand kernel, pass by pass
+  // disjoint: 256-row tiles run the far pass instead (pass 2 only for the
+  // G = 1 sequences), then the same pass-1 launch; the first 128 rows as above
   if (any_p2) {
     if (nblk && (!disjoint || any_only2)) prefill_pp_kernel<0><<<nblk, PP_NT, 0, st>>>(A, hm, seqs, sc);
     prefill_pass_kernel<0, true><<<nfirst, NT, 0, st>>>(A, hm, seqs, sc);
@@ -1392,8 +1379,7 @@ hipError_t jl_launch_prefill_bf16(const JlPrefillWs& ws, const void* q, const Jl
   if (hipEvent_t mid = jl_profile_mid_event()) (void)hipEventRecord(mid, st);
   if (any_p1) {
     if (nblk) {
-      if (disjoint) prefill_pp_kernel<5><<<nblk, PP_NT, 0, st>>>(A, hm, seqs, sc);
-      else prefill_pp_kernel<3><<<nblk, PP_NT, 0, st>>>(A, hm, seqs, sc);
+      prefill_pp_kernel<5><<<nblk, PP_NT, 0, st>>>(A, hm, seqs, sc);
     }
     prefill_pass_kernel<1, true><<<nfirst, NT, 0, st>>>(A, hm, seqs, sc);
   }
