@@ -12,8 +12,10 @@ Prints ONE JSON line:
             F_3pass = 4 d Hq (L(L+1)/2 + 2 W), W = sum_i min(i+1, w0),
             over the whole prefill call (RoPE pre-pass included, inputs
             resident in HBM), timed with HIP events on the stream;
-  roofline  the dominant kernel (the full-causal pass-2 launches): its
-            algorithmic FLOPs 4 d Hq L(L+1)/2 over its own duration, taken
+  roofline  the dominant kernel (the pass-2 launches, which also yield pass 3
+            from the same walk over the remote-grid tiles): the full-causal
+            FLOPs 4 d Hq L(L+1)/2 over its own duration (pass 3's share is
+            reported beside it, not counted), taken
             from events the library records right around it, against the
             MI355X dense bf16 MFMA peak (and against the measured MFMA-only
             ceiling); traffic comes from the committed counter summary when it
@@ -677,9 +679,10 @@ def main():
     roof = {"bound": "mfma", "achieved": round(pass2_tflops, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(pass2_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": read_traffic(PASS2_TRAFFIC),
-            "kernel": "prefill_pp_kernel<0> + prefill_pass_kernel<0, true> (pass 2: remote "
-                      "q/k, full causal; the second kernel takes the first 128 rows)",
-            "flops_per_launch": Fc, "ms_per_launch": round(pass2_ms, 3)}
+            "kernel": "prefill_pp_kernel<0> + prefill_pass_kernel<0, true> (passes 2 and 3: remote "
+                      "q/k, one walk, window tiles first; the second kernel takes the first 128 rows)",
+            "flops_per_launch": Fc, "ms_per_launch": round(pass2_ms, 3),
+            "pass3_flops_shared_not_counted": (F3 - Fc) // 2}
     dec_roof = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
                 "traffic": read_traffic(DECODE_TRAFFIC),

@@ -85,14 +85,19 @@ int64_t jl_group_size(int64_t L, int64_t w_pretrained);
  *   out = (z1 o1 + [far > 0] (z2 o2 - z3 o3)) / (z1 + far),
  *   lse = M + log(z1 + far).
  * In exact arithmetic z2 >= z3 and the clamp changes nothing; it keeps the
- * result finite when rounding makes the difference negative.  Precision: the
- * far mass is formed as the difference of two window-dominated terms, so a
- * row whose far mass is small against its window mass under the remote grid
- * loses relative precision in that term (rounding of passes 2 and 3 times
- * z2 / (z1 + far)).  On inputs with large score spreads (q, k ~ N(0, 9) and
- * more) this can move the output outside the range of V.
- * jl_bifocal_prefill_disjoint computes the same attention with two positive
- * weights and no cancelling term; prefer it for such inputs.
+ * result finite when rounding makes the difference negative.  With JL_BF16,
+ * rows from the 129th of a sequence on take passes 2 and 3 from one walk over
+ * the remote-grid key tiles (the state after the window tiles is pass 3's),
+ * and z2 o2 - z3 o3 and z2 - z3 are formed from the two states' accumulators,
+ * maxima and sums in the frame of pass 2's maximum, which is the same
+ * quantity.  Precision: the far mass is the difference of two
+ * window-dominated terms, so a row whose far mass is small against its
+ * window mass under the remote grid, yet comparable to the base-grid window
+ * mass, loses relative precision in that term (fp32 rounding of the window
+ * terms times their ratio to the far mass).  With q, k ~ N(0, 25) this can
+ * move the output outside the range of V.  jl_bifocal_prefill_disjoint
+ * computes the same attention with two positive weights and no cancelling
+ * term; prefer it for such inputs.
  *
  *   q          [total_tokens, num_q_heads, head_dim]  raw (pre-RoPE), dtype
  *   k, v       [total_tokens, num_kv_heads, head_dim] raw (pre-RoPE), dtype
