@@ -1034,12 +1034,32 @@ __device__ inline void pp_walk_b(const PpTiles& T, const bf16x8* qf, PpState& st
   pp_barrier();
 }
 
+// One group's side of a pass: group A (waves 0-3) or group B.
+template <int KIND, bool GA>
+__device__ inline void pp_walk(const PpTiles& T, const bf16x8* qf, PpState& st, f32x16* o, const WaveRows& wr,
+                               int lane) {
+  if constexpr (GA) pp_walk_a<KIND>(T, qf, st, o, wr, lane);
+  else pp_walk_b<KIND>(T, qf, st, o, wr, lane);
+}
+
 template <int KIND>
 __device__ inline void pp_run(const PpTiles& T, const bf16x8* qf, PpState& st, f32x16* o, const WaveRows& wr,
                               int lane) {
   if (T.wave < 4) pp_walk_a<KIND>(T, qf, st, o, wr, lane);
   else pp_walk_b<KIND>(T, qf, st, o, wr, lane);
 }
+
+// Pass 1's normalised output of a 256-row tile, kept in LDS by ROLE 0 until
+// its merge: 64 bf16 per lane, chunk c (8 values: channels 32 (c / 2) +
+// 8 (c % 2) .. of the lane's slots) of thread t at (c * PP_NT + t) * 16
+// bytes.  o1 enters the merge with a positive weight only (the cancelling
+// pair is passes 2 and 3, kept in fp32), so bf16 holds it within the
+// output's own rounding.  Before pass 1 ends, the same bytes of each thread
+// hold its raw query row for the second rotation.
+constexpr int O1_BYTES = PP_NT * 128;
+// pass 1's log2-LSE of each thread's row, beside o1 (in LDS rather than in a
+// register across the two later walks)
+constexpr int LAM1_BYTES = PP_NT * 4;
 
 // Pass 2's (or the far pass's) fp32 output of rows >= JL_LO_ROWS, as the
 // 256-row kernel writes and reads it.  slab is the wave's first row.  A lane
@@ -1062,6 +1082,67 @@ __device__ inline float* o2_slot(float* slab, int lane, int i, bool lane_order) 
 __device__ inline void pp_load_row(float4* v, const float* slab, int lane, bool lane_order) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) v[i] = *(const float4*)o2_slot((float*)slab, lane, i, lane_order);
+}
+
+// ROLE 0's walks for one wave group (GA: waves 0-3): pass 1 on the base
+// grid (the whole attention when single), its output to LDS, then pass 3 on
+// the remote grid, whose state is stored, then the far tiles, after which the
+// state is pass 2's.  Each group runs its walks in its own branch: joining
+// the groups between walks that carry the state made the register allocator
+// spill it.
+template <bool GA>
+__device__ inline __attribute__((always_inline)) void pp_three_walks(
+    const PrefillArgs& A, const PpTiles& T, bf16x8* qf, PpState& st, f32x16* o, const WaveRows& wr, int lane,
+    bool single, bool live, bool q_valid, int q_row, int G, int64_t krow,
+    __attribute__((address_space(3))) bf16x8* o1s, float* lam1s, int64_t slab_off, int L, int h, int64_t s0,
+    int far_tiles) {
+  const int g = lane >> 5;
+  const int iw = wr.iw;
+  pp_walk<1, GA>(T, qf, st, o, wr, lane);
+  if (single) return;
+  // pass 1 done: its log2-LSE and o1 (normalised, bf16) to LDS, o1 after the
+  // raw query rows come back from there
+  const float l1 = pair_sum(st.l);
+  *lam1s = l1 > 0.f ? st.m + __log2f(l1) : -INFINITY;
+  bf16x8 x[8];
+  if (live) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) x[c] = o1s[c * PP_NT];
+  }
+  {
+    const float inv = l1 > 0.f ? 1.f / l1 : 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      bf16x8 w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e] = (__bf16)(o[c >> 1][8 * (c & 1) + e] * inv);
+      o1s[c * PP_NT] = w;
+    }
+  }
+  if (live) rotate_q<false>(qf, nullptr, x, q_valid, jl_remote_pos(q_row, G), A, g);
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+  st = PpState{-INFINITY, 0.f, f32x16{}};
+  PpTiles T3 = T;
+  T3.rk = __builtin_amdgcn_make_buffer_rsrc((void*)(A.kr + krow), 0, 0x7fffffff, BUF_RSRC_WORD3);
+  pp_walk<1, GA>(T3, qf, st, o, wr, lane);
+  if (live && wr.myrow < L) {
+    // pass 3's state as it stands (a row without window pairs, w0 = 0,
+    // stores m3 = -inf, l3 = 0 and a zero accumulator)
+    const float l3 = pair_sum(st.l);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *(float4*)o2_slot(A.o3 + slab_off, lane, 4 * db + q4, iw + 32 <= L) =
+            make_float4(o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]);
+    // both lanes of the row store the same (m3, l3), so that each reads
+    // back its own store
+    A.ml3[(int64_t)h * A.total + s0 + wr.myrow] = make_float2(st.m, l3);
+  }
+  T3.t0 = 0;
+  T3.n = far_tiles;
+  if (T3.n > 0) pp_walk<2, GA>(T3, qf, st, o, wr, lane);
 }
 
 // ROLE 0: passes 2 and 3 (remote q/k) from one walk over the key tiles.  On a
@@ -1090,8 +1171,8 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
                                                              JlSched sc) {
   static_assert(ROLE == 0 || ROLE == 4 || ROLE == 5, "pass roles of the 256-row kernel");
   constexpr int KIND = ROLE == 0 ? 0 : ROLE == 4 ? 2 : 1;
-  constexpr bool BASE = ROLE == 5;                   // pass 1 runs on the base grid
-  __shared__ __align__(1024) char smem[2 * (KT_BYTES + VT_BYTES)];
+  constexpr bool BASE = ROLE == 0 || ROLE == 5;      // the first walk is pass 1, on the base grid
+  __shared__ __align__(1024) char smem[2 * (KT_BYTES + VT_BYTES) + (ROLE == 0 ? O1_BYTES + LAM1_BYTES : 0)];
   int h, b, u;
   if (!block_item<false>(sc, A.Hq, &h, &b, &u)) return;
   // the work item is uniform over the block; say so, so that pointers built
@@ -1104,7 +1185,7 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
   if (r0 >= L) return;
   const bool only1 = A.w0 >= (int64_t)L;
   const bool only2 = seqs.G[b] == 1 && !only1;
-  if (ROLE == 0 && (only1 || (A.disjoint && !only2))) return;
+  if (ROLE == 0 && A.disjoint && !only2) return;
   if (ROLE == 5 && only2) return;
   if (ROLE == 4 && (only1 || only2)) return;
   const int tid = threadIdx.x;
@@ -1114,7 +1195,8 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
   const int kvh = __builtin_amdgcn_readfirstlane(hm.kv_of[h]);
   const int64_t s0 = uniform_i64(seqs.start[b]);
   // the window of the walk: w0, or L where it covers every causal pair (w0 >= L,
-  // and ROLE 0's walk on a G = 1 sequence, which is then the plain causal pass)
+  // and ROLE 0's first walk on a G = 1 sequence, which is then the whole
+  // attention: the two grids coincide)
   const int w0 = A.w0 > (int64_t)L || (ROLE == 0 && only2) ? L : (int)A.w0;
   const int iw = r0 + wave * 32;
   const WaveRows wr{iw, iw + (lane & 31), w0};
@@ -1138,12 +1220,21 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
   // operands) and its positions on the two grids
   const bool q_valid = wr.myrow < L;
   const int q_row = q_valid ? wr.myrow : L - 1;
-  const int q_rem = jl_remote_pos(q_row, __builtin_amdgcn_readfirstlane(seqs.G[b]));
   const __bf16* q_src = A.q + ((s0 + q_row) * A.Hq + h) * D;
+  // ROLE 0 rotates the same rows again for passes 3 and 2: the raw rows wait
+  // in the LDS area of pass 1's output, which pass 1 does not touch, each
+  // thread's 128 bytes where its own o1 chunks go (so no barrier is needed)
+  __attribute__((address_space(3))) bf16x8* const o1s =
+      (__attribute__((address_space(3))) bf16x8*)(lds + 2 * (KT_BYTES + VT_BYTES)) + tid;
   if (live) {
     bf16x8 x[8];
     load_q_raw(x, q_src, g);
-    rotate_q<false>(qf, nullptr, x, q_valid, BASE ? q_row : q_rem, A, g);
+    if constexpr (ROLE == 0) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) o1s[c * PP_NT] = x[c];
+    }
+    rotate_q<false>(qf, nullptr, x, q_valid,
+                    BASE ? q_row : jl_remote_pos(q_row, __builtin_amdgcn_readfirstlane(seqs.G[b])), A, g);
   } else {
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) qf[kb] = bf16x8{};
@@ -1156,41 +1247,19 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
   // far pairs of the tile's rows end at key r0 + 255 - w0
   const int far_last = r0 + PP_BQ - 1 - w0;
   const int far_tiles = far_last < 0 ? 0 : min(tiles_end, far_last / BK + 1);
+  float* const lam1s = (float*)(smem + 2 * (KT_BYTES + VT_BYTES) + O1_BYTES) + tid;   // ROLE 0
   if constexpr (ROLE == 0) {
-    // pass 3 (the whole causal pass on a G = 1 sequence): the window tiles
-    // under the window mask; then, on a G > 1 sequence, pass 3's output from
-    // the running state and pass 2: the far tiles under the far mask.  Each
-    // group runs both walks in its own branch (joining the groups between
-    // them made the register allocator spill the carried state).
+    // pass 1, then passes 3 and 2 (the whole attention in one walk when
+    // w0 >= L or G = 1)
+    const bool single = only1 || only2;
     T.t0 = tw0;
     T.n = tiles_end - tw0;
-    PpTiles T2 = T;
-    T2.t0 = 0;
-    T2.n = only2 ? 0 : far_tiles;
-    const auto store_pass3 = [&]() {
-      // pass 3's state as it stands (a row without window pairs, w0 = 0,
-      // stores m3 = -inf, l3 = 0 and a zero accumulator)
-      if (only2 || !live || wr.myrow >= L) return;
-      const float l3 = pair_sum(st.l);
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          *(float4*)o2_slot(A.o3 + slab_off, lane, 4 * db + q4, iw + 32 <= L) =
-              make_float4(o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]);
-      // both lanes of the row store the same (m3, l3), so that each reads back
-      // its own store
-      A.ml3[(int64_t)h * A.total + s0 + wr.myrow] = make_float2(st.m, l3);
-    };
-    if (wave < 4) {
-      pp_walk_a<1>(T, qf, st, o, wr, lane);
-      store_pass3();
-      if (T2.n > 0) pp_walk_a<2>(T2, qf, st, o, wr, lane);
-    } else {
-      pp_walk_b<1>(T, qf, st, o, wr, lane);
-      store_pass3();
-      if (T2.n > 0) pp_walk_b<2>(T2, qf, st, o, wr, lane);
-    }
+    if (wave < 4)
+      pp_three_walks<true>(A, T, qf, st, o, wr, lane, single, live, q_valid, q_row, seqs.G[b], krow, o1s, lam1s,
+                           slab_off, L, h, s0, far_tiles);
+    else
+      pp_three_walks<false>(A, T, qf, st, o, wr, lane, single, live, q_valid, q_row, seqs.G[b], krow, o1s, lam1s,
+                            slab_off, L, h, s0, far_tiles);
   } else {
     T.t0 = ROLE == 4 || only1 ? 0 : tw0;
     T.n = (ROLE == 4 ? far_tiles : tiles_end) - T.t0;
@@ -1202,7 +1271,7 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
   const bool row_ok = live && wr.myrow < L;
   float* const o2_slab = A.o2 + slab_off;
   const bool o2_lane_order = iw + 32 <= L;
-  if (ROLE == 0 ? only2 : only1) {
+  if (ROLE == 0 ? only1 || only2 : only1) {
     // the pass is the whole attention of the sequence
     if (!row_ok) return;
     __bf16* orow = A.out + ((s0 + wr.myrow) * A.Hq + h) * D;
@@ -1224,34 +1293,56 @@ __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlH
     if (A.lse != nullptr && g == 0) A.lse[ridx] = lam * LN2;
     return;
   }
-  if constexpr (ROLE == 0 || ROLE == 4) {
-    // the far part: pass 2 minus pass 3 (ROLE 0), or the far pass (ROLE 4);
-    // rows without a far key (i < w0) store o = 0 and lam = -inf
+  if constexpr (ROLE == 0) {
+    // the far part from passes 2 and 3 in pass 2's frame (c = exp2(m3 - m2)
+    // <= 1: F = O2 - c O3, lf = l2 - c l3, the far mass clamped at zero),
+    // merged with pass 1: M = max(lam1, m2), z1 = exp2(lam1 - M),
+    // zf = exp2(m2 - M), O = (z1 o1 + zf F) / (z1 + zf lf)
     if (!row_ok) return;
-    float lf = l;
-    float c = 0.f;
     float4 s3[16];
-    if constexpr (ROLE == 0) {
-      pp_load_row(s3, A.o3 + slab_off, lane, o2_lane_order);
-      const float2 ml3 = A.ml3[ridx];
-      c = ml3.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml3.x - st.m);
-      lf = l - c * ml3.y;
+    pp_load_row(s3, A.o3 + slab_off, lane, o2_lane_order);
+    const float2 ml3 = A.ml3[ridx];
+    const float c = ml3.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml3.x - st.m);
+    const float lf = l - c * ml3.y;
+    const bool far = lf > 0.f;
+    const float lam1 = *lam1s;
+    const float M = fmaxf(lam1, st.m);                   // m2 is finite: pass 2 holds the diagonal
+    const float z1 = __builtin_amdgcn_exp2f(lam1 - M);   // 0 when w0 = 0 (no window pair)
+    const float zf = far ? __builtin_amdgcn_exp2f(st.m - M) : 0.f;
+    const float Z = z1 + (far ? zf * lf : 0.f);
+    const float inv = 1.f / Z;
+    __bf16* orow = A.out + ((s0 + wr.myrow) * A.Hq + h) * D;
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+      const bf16x8 v1 = o1s[cc * PP_NT];
+      const int db = cc >> 1;
+      u32x2 w[2];
+#pragma unroll
+      for (int hq = 0; hq < 2; ++hq) {
+        const int q4 = 2 * (cc & 1) + hq;
+        const float4 v3 = s3[4 * db + q4];
+        const float o3v[4] = {v3.x, v3.y, v3.z, v3.w};
+        bf16x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          x[e] = (__bf16)((z1 * (float)v1[4 * hq + e] + zf * (o[db][4 * q4 + e] - c * o3v[e])) * inv);
+        w[hq] = __builtin_bit_cast(u32x2, x);
+      }
+      *(u32x4*)(orow + db * 32 + 16 * (cc & 1) + 8 * g) = pair_channels(w[0], w[1]);
     }
-    const bool far = lf > 0.f;                           // the far mass, clamped at zero
-    const float inv = far ? 1.f / lf : 0.f;
+    if (A.lse != nullptr && g == 0) A.lse[ridx] = (M + __log2f(Z)) * LN2;
+  } else if constexpr (ROLE == 4) {
+    // the far pass: rows without a far key (i < w0) store o = 0 and lam = -inf
+    if (!row_ok) return;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        float4 v = make_float4(o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]);
-        if constexpr (ROLE == 0) {
-          const float4 w = s3[4 * db + q4];
-          v = make_float4(v.x - c * w.x, v.y - c * w.y, v.z - c * w.z, v.w - c * w.w);
-        }
+      for (int q4 = 0; q4 < 4; ++q4)
         *(float4*)o2_slot(o2_slab, lane, 4 * db + q4, o2_lane_order) =
-            make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
-      }
-    if (g == 0) A.lse2[ridx] = far ? st.m + __log2f(lf) : -INFINITY;
+            make_float4(o[db][4 * q4] * inv, o[db][4 * q4 + 1] * inv, o[db][4 * q4 + 2] * inv,
+                        o[db][4 * q4 + 3] * inv);
+    if (g == 0) A.lse2[ridx] = lam;
   } else if constexpr (ROLE == 5) {
     // pass 1 merged with the far part: window (base grid) and far (remote
     // grid) are two halves of one softmax, so both weights are positive
@@ -1365,22 +1456,19 @@ hipError_t jl_launch_prefill_bf16(const JlPrefillWs& ws, const void* q, const Jl
   }
   const unsigned nblk = (unsigned)sc.total_units * (unsigned)Hq;   // multiple of 8 when xcd_heads
   const unsigned nfirst = (unsigned)(seqs.nseq * Hq);
-  // rows >= 128 in 256-row tiles: passes 2 and 3 from one walk, which leaves
-  // the far part (pass 2 minus pass 3), then pass 1 merged with it; the first
-  // 128 rows of every sequence in the split-operand kernel, pass by pass
-  // disjoint: 256-row tiles run the far pass instead (pass 2 only for the
-  // G = 1 sequences), then the same pass-1 launch; the first 128 rows as above
-  if (any_p2) {
-    if (nblk && (!disjoint || any_only2)) prefill_pp_kernel<0><<<nblk, PP_NT, 0, st>>>(A, hm, seqs, sc);
-    prefill_pass_kernel<0, true><<<nfirst, NT, 0, st>>>(A, hm, seqs, sc);
-  }
+  // rows >= 128 in 256-row tiles: pass 1, then passes 2 and 3 from one walk,
+  // and the merge, all in one workgroup; the first 128 rows of every
+  // sequence in the split-operand kernel, pass by pass
+  // disjoint: 256-row tiles run the far pass (ROLE 0 only for the G = 1
+  // sequences), then pass 1 merged with it; the first 128 rows as above
+  if (nblk && (!disjoint || any_only2)) prefill_pp_kernel<0><<<nblk, PP_NT, 0, st>>>(A, hm, seqs, sc);
+  if (any_p2) prefill_pass_kernel<0, true><<<nfirst, NT, 0, st>>>(A, hm, seqs, sc);
   if (disjoint && any_p3 && nblk) prefill_pp_kernel<4><<<nblk, PP_NT, 0, st>>>(A, hm, seqs, sc);
-  // profiling mark after the dominant launch of either form (pass 2, or the far pass)
+  // profiling mark after the dominant launch of either form (all three passes
+  // of rows >= 128, or the far pass)
   if (hipEvent_t mid = jl_profile_mid_event()) (void)hipEventRecord(mid, st);
   if (any_p1) {
-    if (nblk) {
-      prefill_pp_kernel<5><<<nblk, PP_NT, 0, st>>>(A, hm, seqs, sc);
-    }
+    if (disjoint && nblk) prefill_pp_kernel<5><<<nblk, PP_NT, 0, st>>>(A, hm, seqs, sc);
     prefill_pass_kernel<1, true><<<nfirst, NT, 0, st>>>(A, hm, seqs, sc);
   }
   if (any_p3) prefill_pass_kernel<2, true><<<nfirst, NT, 0, st>>>(A, hm, seqs, sc);
