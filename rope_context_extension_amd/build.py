@@ -12,6 +12,7 @@ from __future__ import annotations
 import concurrent.futures
 import glob
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -45,12 +46,41 @@ EXTRA = {
 }
 
 
+# Every kernel keeps its state in registers and LDS: a kernel that spills
+# VGPRs or puts arrays on the stack (scratch) runs many times slower (a
+# restructured prefill kernel once took 704 bytes of stack per lane and ran
+# at half speed), so the build reads the compiler's resource report and
+# stops on either.
+RESOURCE_REPORT = "-Rpass-analysis=kernel-resource-usage"
+
+
+def _check_resources(src: str, report: str) -> None:
+    kernel, bad = None, []
+    for ln in report.splitlines():
+        if "remark:" not in ln:
+            continue
+        msg = ln.split("remark:", 1)[1].split(" [-R", 1)[0].strip()
+        if msg.startswith("Function Name:"):
+            kernel = msg.split(":", 1)[1].strip()
+        elif msg.startswith("ScratchSize") or msg.startswith("VGPRs Spill") or msg.startswith("SGPRs Spill"):
+            key, val = msg.split(":", 1)
+            n = int(val.split()[0])
+            if n and not key.startswith("SGPRs"):
+                bad.append(f"{kernel}: {key.strip()} {n}")
+    if bad:
+        raise RuntimeError(f"{src}: kernels use stack or spill VGPRs:\n  " + "\n  ".join(bad))
+
+
 def _compile(src: str, obj: str) -> None:
-    cmd = [HIPCC, *COMMON, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(os.path.basename(src), []), RESOURCE_REPORT, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
-    noisy = [ln for ln in r.stderr.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
+    _check_resources(src, r.stderr)
+    # (the report's remarks quote their source lines: "  42 | code" and "     | ^")
+    noisy = [ln for ln in r.stderr.splitlines()
+             if "packed-fp32-ops" not in ln and "remark:" not in ln and ln.strip()
+             and not re.match(r"\s*\d*\s*\|", ln)]
     if noisy:
         sys.stderr.write("\n".join(noisy) + "\n")
 

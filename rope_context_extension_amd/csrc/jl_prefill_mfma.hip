@@ -8,12 +8,12 @@
 //     lse_k = m_k + log l_k,  M = max(lse_1, lse_2),  z_k = exp(lse_k - M),
 //     out = (z1 o1 + z2 o2 - z3 o3) / (z1 + z2 - z3).
 //
-// Rows from 128 on (prefill_pp_kernel, 256 rows and 8 waves per workgroup,
-// two launches): passes 2 and 3 come from one walk over the remote-grid key
-// tiles, window tiles first; the walk's state after the window tiles is
-// pass 3's, its end state pass 2's, and the far part z2 o2 - z3 o3 is formed
-// from the two states before it leaves the launch.  The second launch runs
-// pass 1 and adds the far part.
+// Rows from 128 on (prefill_pp_kernel, 256 rows and 8 waves per workgroup):
+// one workgroup runs all three passes of its tile.  Pass 1 first; then
+// passes 2 and 3 come from one walk over the remote-grid key tiles, window
+// tiles first: the walk's state after the window tiles is pass 3's, its end
+// state pass 2's, and the far part z2 o2 - z3 o3 is formed from the two
+// states and added to pass 1's share in the same workgroup.
 //
 // A sequence's first 128 rows (prefill_pass_kernel, one workgroup = 4 waves
 // = 128 query rows of one head): the three passes run one after another over
@@ -1145,27 +1145,30 @@ __device__ inline __attribute__((always_inline)) void pp_three_walks(
   if (T3.n > 0) pp_walk<2, GA>(T3, qf, st, o, wr, lane);
 }
 
-// ROLE 0: passes 2 and 3 (remote q/k) from one walk over the key tiles.  On a
-// sequence with G > 1 the walk takes the window tiles first under the window
-// mask (0 <= i - j < w0), which is exactly pass 3, stores that running state
-// (accumulator, stabiliser m3 and sum l3), and goes on over the far tiles
-// under the far mask (i - j >= w0); the end state has seen every causal pair
-// once, which is pass 2.  Pass 3 thus shares pass 2's K/V tiles, scores and
-// probabilities (only the few tiles that hold the window's lower edge are
-// walked twice, once per mask).  The inclusion-exclusion step then takes
-// pass 3 from pass 2 in the frame of pass 2's stabiliser m2: with
-// c = exp2(m3 - m2) (m only rises along the walk, so c <= 1), the far part
-// is O_far = O2 - c O3 and l_far = l2 - c l3, which is z2 o2 - z3 o3 and
-// z2 - z3 through the two passes' LogSumExp statistics (lam = m + log2 l),
-// formed without the exp2 of large lam values.  Its far mass is clamped at
-// zero, and (o_far = O_far / l_far, lam_far) goes where pass 2's output
-// would.  On a G = 1 sequence ROLE 0 is the plain causal pass.
-// ROLE 4 (the disjoint variant) is the far pass alone: remote q/k, pairs
-// with i - j >= w0 only, written to the same place; ROLE 0 then serves only
-// the G = 1 sequences.
-// ROLE 5: pass 1 (window, base q/k) merged with the far part,
-// O = (z1 o1 + zf of) / (z1 + zf); sequences with w0 >= L run pass 1 over the
-// whole causal range and write O directly.
+// ROLE 0: all three passes of a 256-row tile and their merge.  Pass 1 (base
+// q/k, window tiles) first, its normalised output kept in LDS.  Then passes
+// 2 and 3 (remote q/k) from one walk over the key tiles: the walk takes the
+// window tiles first under the window mask (0 <= i - j < w0), which is
+// exactly pass 3, stores that running state (accumulator, stabiliser m3 and
+// sum l3), and goes on over the far tiles under the far mask (i - j >= w0);
+// the end state has seen every causal pair once, which is pass 2.  Pass 3
+// thus shares pass 2's K/V tiles, scores and probabilities (only the few
+// tiles that hold the window's lower edge are walked twice, once per mask).
+// The inclusion-exclusion step then takes pass 3 from pass 2 in the frame of
+// pass 2's stabiliser m2: with c = exp2(m3 - m2) (m only rises along the
+// walk, so c <= 1), the far part is F = O2 - c O3 and l_far = l2 - c l3,
+// which is z2 o2 - z3 o3 and z2 - z3 through the two passes' LogSumExp
+// statistics (lam = m + log2 l), formed without the exp2 of large lam
+// values.  The far mass is clamped at zero, and the merge with pass 1 is
+// O = (z1 o1 + zf F) / (z1 + zf l_far), z1 = exp2(lam1 - M),
+// zf = exp2(m2 - M), M = max(lam1, m2).  On a G = 1 sequence, or with
+// w0 >= L, ROLE 0's first walk with the window set to L is the whole
+// attention.
+// The disjoint variant: ROLE 4 is the far pass alone (remote q/k, pairs with
+// i - j >= w0 only, written to o2), and ROLE 5 is pass 1 merged with it,
+// O = (z1 o1 + zf of) / (z1 + zf), two positive weights; sequences with
+// w0 >= L run pass 1 over the whole causal range and write O directly; ROLE
+// 0 then serves only the G = 1 sequences.
 template <int ROLE>
 __global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillArgs A, JlHeadMap hm, JlSeqs seqs,
                                                              JlSched sc) {
