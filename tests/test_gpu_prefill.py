@@ -192,10 +192,11 @@ def test_bf16_large_sigma_robustness(sigma):
     """q, k, v ~ N(0, sigma^2), L = 2048, G = 4, w0 = 256.  With sigma = 3
     the scores spread over about +-100 (log units), so the window terms of
     passes 1 and 3 dwarf the far mass of most rows and the three-pass merge
-    subtracts nearly equal numbers.  Reported, not gated on accuracy: the
-    errors of both merges against the oracle are printed.  The gate is that
-    neither merge emits a non-finite output or LSE (the window weight z1 is
-    positive and the far weight z2 - z3 is clamped at zero, so Z > 0)."""
+    subtracts nearly equal numbers.  Not gated at the bf16 bar: the errors of
+    both merges against the oracle are printed.  The gates are that neither
+    merge emits a non-finite output or LSE (the window weight z1 is positive
+    and the far weight z2 - z3 is clamped at zero, so Z > 0), and at sigma = 3
+    that the three-pass error stays within twice the disjoint merge's."""
     jl, torch = gpu_or_skip()
     L, Hq, Hkv, d, w0, wpt = 2048, 2, 1, 128, 256, 512
     g = torch.Generator("cpu").manual_seed(31)
@@ -205,12 +206,20 @@ def test_bf16_large_sigma_robustness(sigma):
     kw = dict(w0=w0, w_pretrained=wpt, rope_base=1e6)
     oo, ll = oracle.prefill(_np(q), _np(k), _np(v), **kw)
     report = []
+    errs = {}
     for dj in (False, True):
         o, lse = _run(jl, torch, q, k, v, disjoint=dj, **kw)
         assert np.isfinite(o).all() and np.isfinite(lse).all(), (sigma, dj)
-        report.append(f"{'disjoint' if dj else 'three-pass'} max|do|={max_abs(o, oo):.3e} "
-                      f"lse rel={lse_rel_err(lse, ll):.3e}")
+        errs[dj] = (max_abs(o, oo), lse_rel_err(lse, ll))
+        report.append(f"{'disjoint' if dj else 'three-pass'} max|do|={errs[dj][0]:.3e} "
+                      f"lse rel={errs[dj][1]:.3e}")
     _say(f"[prefill] sigma={sigma}: " + "; ".join(report))
+    if sigma == 3.0:
+        # passes 2 and 3 share their window products (one walk) and their
+        # difference is taken on the accumulators, so at sigma = 3 the
+        # three-pass merge is as accurate as the disjoint one (measured 0.31
+        # against 0.33 max-abs; with separate passes it was 73)
+        assert errs[False][0] <= 2 * errs[True][0] and errs[False][1] <= 2 * errs[True][1], errs
 
 
 def test_bf16_empty_is_noop():
