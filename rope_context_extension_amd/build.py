@@ -36,9 +36,10 @@ COMMON = [
 # dwords on gfx950): a decode step's first loads then wait for no load of a
 # kernel argument.  The prefill kernels are scheduled with the compiler's
 # ILP strategy, which orders the softmax phase's instructions (the matrix
-# phases are pinned by scheduling barriers): the causal pass keeps 217
-# registers and no spills, results are bitwise the same, and a prefill call
-# was about 0.4% faster on two boxes.  On the decode kernels it was slower
+# phases are pinned by scheduling barriers): results are bitwise the same,
+# and a prefill call was about 0.4% faster on two boxes with the earlier
+# two-launch kernels and 0.7% faster with the three-pass kernel (same-box
+# A/B, 116.1 against 117.0 ms).  On the decode kernels it was slower
 # at 128K keys, so they keep the default.
 EXTRA = {
     "jl_decode.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"],
