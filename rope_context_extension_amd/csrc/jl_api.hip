@@ -209,16 +209,18 @@ static int prefill_impl(const void* q, const void* k, const void* v, void* o, fl
   const size_t lrows = (size_t)num_seqs * JL_LO_ROWS;
   const size_t nklo = (size_t)num_kv_heads * lrows * head_dim * el;
   pl.off_lo = off; if (dtype == JL_BF16) off += 2 * align256(nklo);
-  // rows >= JL_LO_ROWS: the pass-2 launch keeps pass 3's state (accumulator,
-  // stabiliser and sum) until it has formed the far part, which it hands
-  // (o, lse) to the pass-1 launch; the first JL_LO_ROWS rows hand pass 1's
-  // and pass 2's outputs to the launch that runs pass 3 and merges
+  // rows >= JL_LO_ROWS: the three-pass kernel keeps pass 3's state
+  // (accumulator, stabiliser and sum) until it has formed the far part; the
+  // accumulator takes those rows of the o2 array, which only the disjoint
+  // variant's far pass uses otherwise (one or the other per call), and a
+  // sequence's first JL_LO_ROWS rows of o2 hold pass 2's output for the
+  // launch that runs pass 3 and merges them
   const bool merge = dtype == JL_BF16 && pl.seqs.any_remote;
   const size_t no = align256((size_t)num_q_heads * total_tokens * head_dim * 4);
   const size_t nl = align256((size_t)num_q_heads * total_tokens * 4);
   const size_t no1 = align256((size_t)num_q_heads * lrows * head_dim * 4);
   const size_t nl1 = align256((size_t)num_q_heads * lrows * 4);
-  pl.off_o = off; if (merge) off += no1 + 2 * no;
+  pl.off_o = off; if (merge) off += no1 + no;
   pl.off_lse = off; if (merge) off += nl1 + 3 * nl;
   pl.total = total_tokens == 0 ? 0 : off;
 
@@ -251,11 +253,10 @@ static int prefill_impl(const void* q, const void* k, const void* v, void* o, fl
     const size_t lrows = (size_t)num_seqs * JL_LO_ROWS;
     const size_t no1 = align256((size_t)num_q_heads * lrows * head_dim * 4);
     const size_t nl1 = align256((size_t)num_q_heads * lrows * 4);
-    const size_t no = align256((size_t)num_q_heads * total_tokens * head_dim * 4);
     const size_t nl = align256((size_t)num_q_heads * total_tokens * 4);
     ws.o1 = wsb + pl.off_o;
     ws.o2 = wsb + pl.off_o + no1;
-    ws.o3 = wsb + pl.off_o + no1 + no;
+    ws.o3 = ws.o2;   // rows >= JL_LO_ROWS only (see the layout above)
     ws.lse1 = wsb + pl.off_lse;
     ws.lse2 = wsb + pl.off_lse + nl1;
     ws.ml3 = wsb + pl.off_lse + nl1 + nl;

@@ -75,7 +75,8 @@ struct JlPrefillWs {
   void* o2;      // [Hq][T][d] fp32: normalised pass-2 output; the 256-row kernels keep each
                  // full 32-row group of a wave in that wave's lane order
   void* o3;      // [Hq][T][d] fp32: pass 3's accumulator of rows >= JL_LO_ROWS (scaled by
-                 // exp2(-m3)), written and read back by the pass-2 launch (same layout as o2)
+                 // exp2(-m3)), written and read back by the three-pass kernel; it is the o2
+                 // array, whose rows >= JL_LO_ROWS only the disjoint variant uses otherwise
   void* lse1;    // [Hq][nseq * JL_LO_ROWS] fp32: pass-1 LogSumExp of the first rows, log2 units
   void* lse2;    // [Hq][T] fp32: pass-2 LogSumExp, log2 units
   void* ml3;     // [Hq][T] float2: pass 3's stabiliser m3 (log2 units) and sum l3, rows >= JL_LO_ROWS
